@@ -1,0 +1,221 @@
+"""Seeded synthetic inputs for the SemKV hot path.
+
+This module only draws random numbers and builds the importance score that
+stands in for the model's indicator; it holds none of the ranking,
+quantization, packing or attention arithmetic of the method.  Both the HIP
+path's tests/benchmark and the CPU oracle receive the very same arrays from
+here.
+
+The pages evaluate on LongBench / MT-Eval with Llama-3.1-8B and
+Mistral-7B (SemKV Table 2); those datasets and weights are not available, so
+seeded synthetic K/V of the backbones' KV shape (32 layers, 8 KV heads,
+head_dim 128, 32 query heads) stand in for them.
+
+Draw order per workload: K, V, outlier channels, scores, queries.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+HEAD_DIM = 128
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    layers: int
+    kv_heads: int
+    q_heads: int
+    n: int                 # prompt tokens per sequence
+    r: float
+    L_high: int
+    L_low: int
+    decode_steps: int
+    gen_tokens: int = 0    # generated tokens per sequence (block-exact path)
+    block: int = 128
+    v_dist: str = "normal"     # "normal" | "student_t4"
+    score: str = "uniform"     # "uniform" | "attn_mass"
+    outliers: int = 4          # K channels per layer scaled x10
+    sm_scale: float = 1.0      # q is drawn pre-scaled by 1/sqrt(128)
+
+
+WORKLOADS = {
+    # tiny single layer, full parity
+    "tiny": Workload("tiny", 1, 1, 8, 32, 512, 0.25, 6, 5, 1),
+    # Llama-3.1-8B-shaped cache, 32k context, r = 0.5
+    "llama8b_32k": Workload("llama8b_32k", 1, 32, 8, 32, 32768, 0.5, 6, 5, 256,
+                            score="attn_mass"),
+    # generation: 16 x 8192 prompts + 1024 generated tokens in 128-token blocks
+    "gen_16x8k": Workload("gen_16x8k", 16, 32, 8, 32, 8192, 0.25, 6, 5, 1024,
+                          gen_tokens=1024, score="attn_mass"),
+    # Mistral-7B-shaped 128k context, heavy-tailed V
+    "mistral7b_128k": Workload("mistral7b_128k", 1, 32, 8, 32, 131072, 0.5, 6, 5, 128,
+                               v_dist="student_t4", score="attn_mass"),
+    # cliff-grid sweep base shape (levels and r vary per setting)
+    "cliff_4x32k": Workload("cliff_4x32k", 4, 32, 8, 32, 32768, 0.25, 6, 5, 64,
+                            score="attn_mass"),
+}
+
+CLIFF_UNIFORM = (4, 5, 6, 8, 16)
+CLIFF_PAIRS = ((5, 4), (6, 5), (8, 6))
+CLIFF_RS = (0.1, 0.25, 0.5, 0.75, 0.9)
+
+
+def scaled(w: Workload, **kw) -> Workload:
+    """Same distributions, other sizes (used for small parity cases)."""
+    d = dict(w.__dict__)
+    d.update(kw)
+    return Workload(**d)
+
+
+# ---------------------------------------------------------------- numpy (CPU)
+
+def make_inputs_np(w: Workload, seed: int = 0):
+    """All inputs of a workload drawn on the CPU with numpy (small sizes).
+
+    Returns dict with K, V fp16 [B][layers][kv][n][128], scores fp32 [B][n],
+    q fp16 [steps][B][layers][Hq][128], outlier channel table int [layers][4].
+    """
+    rng = np.random.default_rng(seed)
+    shape = (w.batch, w.layers, w.kv_heads, w.n, HEAD_DIM)
+    K = rng.standard_normal(shape, dtype=np.float32)
+    if w.v_dist == "normal":
+        V = rng.standard_normal(shape, dtype=np.float32)
+    else:
+        z = rng.standard_normal(shape, dtype=np.float32)
+        chi = rng.standard_normal(shape + (4,), dtype=np.float32)
+        V = z / np.sqrt((chi * chi).sum(-1) / 4.0)
+    chans = np.stack([rng.choice(HEAD_DIM, size=w.outliers, replace=False)
+                      for _ in range(w.layers)]) if w.outliers else np.zeros((w.layers, 0), int)
+    for layer in range(w.layers):
+        K[:, layer, :, :, chans[layer]] *= 10.0
+    K16 = K.astype(np.float16)
+    V16 = V.astype(np.float16)
+    if w.score == "uniform":
+        scores = rng.random((w.batch, w.n), dtype=np.float32)
+    else:
+        scores = attention_mass_np(K16, rng, w)
+    steps = max(w.decode_steps, 1)
+    q = (rng.standard_normal((steps, w.batch, w.layers, w.q_heads, HEAD_DIM), dtype=np.float32)
+         / math.sqrt(HEAD_DIM)).astype(np.float16)
+    return {"K": K16, "V": V16, "scores": scores.astype(np.float32), "q": q,
+            "outlier_channels": chans}
+
+
+def attention_mass_np(K16, rng, w: Workload, nq: int = 32):
+    """Stand-in importance score: attention mass that 32 synthetic queries per
+    query head put on each token, summed over heads and layers (fp32, no
+    causal mask).  Harness-side score generator, not part of the hot path."""
+    B, layers, kv, n, d = K16.shape
+    group = w.q_heads // kv
+    qs = (rng.standard_normal((layers, w.q_heads, nq, d), dtype=np.float32)
+          / math.sqrt(d)).astype(np.float16).astype(np.float32)
+    score = np.zeros((B, n), np.float32)
+    for b in range(B):
+        for layer in range(layers):
+            keys = K16[b, layer].astype(np.float32)                  # [kv][n][d]
+            for h in range(w.q_heads):
+                z = qs[layer, h] @ keys[h // group].T                # [nq][n]
+                z = z - z.max(axis=1, keepdims=True)
+                p = np.exp(z)
+                p /= p.sum(axis=1, keepdims=True)
+                score[b] += p.sum(axis=0)
+    return score
+
+
+def make_gen_tokens_np(w: Workload, steps: int, seed: int = 1):
+    """Generated-token K/V [steps][B][layers][kv][128] fp16 and scores U(0,1)."""
+    rng = np.random.default_rng(seed)
+    shape = (steps, w.batch, w.layers, w.kv_heads, HEAD_DIM)
+    K = rng.standard_normal(shape, dtype=np.float32)
+    V = rng.standard_normal(shape, dtype=np.float32)
+    s = rng.random((steps, w.batch), dtype=np.float32)
+    q = (rng.standard_normal((steps, w.batch, w.layers, w.q_heads, HEAD_DIM), dtype=np.float32)
+         / math.sqrt(HEAD_DIM)).astype(np.float16)
+    return K.astype(np.float16), V.astype(np.float16), s, q
+
+
+# ---------------------------------------------------------------- torch (GPU)
+
+def make_kv_torch(w: Workload, device, seed: int = 0):
+    """K, V fp16 [B][layers][kv][n][128] drawn on `device` (large workloads).
+
+    Same recipe as make_inputs_np (N(0,1) K with 4 per-layer channels x10;
+    V N(0,1) or Student-t nu=4), drawn with a seeded torch generator on the
+    device, so the bytes differ from the numpy draw of the same seed.
+    """
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shape = (w.batch, w.layers, w.kv_heads, w.n, HEAD_DIM)
+    K = torch.empty(shape, dtype=torch.float16, device=device)
+    V = torch.empty(shape, dtype=torch.float16, device=device)
+    for layer in range(w.layers):        # per layer keeps the fp32 temporaries small
+        kl = torch.randn((w.batch, w.kv_heads, w.n, HEAD_DIM), generator=g, device=device)
+        K[:, layer] = kl.half()
+    for layer in range(w.layers):
+        if w.v_dist == "normal":
+            vl = torch.randn((w.batch, w.kv_heads, w.n, HEAD_DIM), generator=g, device=device)
+        else:
+            z = torch.randn((w.batch, w.kv_heads, w.n, HEAD_DIM), generator=g, device=device)
+            chi = torch.zeros_like(z)
+            for _ in range(4):
+                e = torch.randn(z.shape, generator=g, device=device)
+                chi += e * e
+            vl = z / torch.sqrt(chi / 4.0)
+        V[:, layer] = vl.half()
+    gc = torch.Generator()
+    gc.manual_seed(seed + 7)
+    chans = torch.stack([torch.randperm(HEAD_DIM, generator=gc)[:w.outliers]
+                         for _ in range(w.layers)])
+    for layer in range(w.layers):
+        idx = chans[layer].to(device)
+        sub = K[:, layer].index_select(-1, idx).float() * 10.0
+        K[:, layer].index_copy_(-1, idx, sub.half())
+    return K, V, chans
+
+
+def attention_mass_torch(K, w: Workload, device, seed: int = 0, nq: int = 32):
+    """Device version of attention_mass_np (fp32), for the large workloads."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 11)
+    B, layers, kv, n, d = K.shape
+    group = w.q_heads // kv
+    score = torch.zeros((B, n), dtype=torch.float32, device=device)
+    for layer in range(layers):
+        qs = (torch.randn((w.q_heads, nq, d), generator=g, device=device)
+              / math.sqrt(d)).half().float()
+        for b in range(B):
+            keys = K[b, layer].float()                               # [kv][n][d]
+            for gi in range(kv):
+                qg = qs[gi * group:(gi + 1) * group].reshape(group * nq, d).contiguous()
+                z = qg @ keys[gi].t().contiguous()                   # [group*nq][n]
+                score[b] += torch.softmax(z, dim=1).sum(dim=0)
+    return score
+
+
+def make_q_torch(w: Workload, steps: int, device, seed: int = 0):
+    """Decode queries fp16 [steps][B][layers][Hq][128], N(0,1)/sqrt(128)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 13)
+    q = torch.randn((steps, w.batch, w.layers, w.q_heads, HEAD_DIM), generator=g,
+                    device=device) / math.sqrt(HEAD_DIM)
+    return q.half()
+
+
+def make_gen_tokens_torch(w: Workload, steps: int, device, seed: int = 1):
+    """Generated-token K/V [steps][B][layers][kv][128] fp16 and U(0,1) scores."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    shape = (steps, w.batch, w.layers, w.kv_heads, HEAD_DIM)
+    K = torch.randn(shape, generator=g, device=device).half()
+    V = torch.randn(shape, generator=g, device=device).half()
+    s = torch.rand((steps, w.batch), generator=g, device=device)
+    return K, V, s
