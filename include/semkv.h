@@ -1,0 +1,195 @@
+/*
+ * semkv.h -- C ABI of the SemKV mixed-precision KV-cache hot path (gfx950).
+ *
+ * The operations follow the problem statement of the page "SemKV: Semantic
+ * Mixed-Precision KV Cache Quantization Guided by the Quality Cliff for
+ * Long-Context LLM Inference" (abbreviated SemKV): a full-precision KV cache
+ * and a per-token importance score go in; the tokens are ranked, the top-r
+ * set gets the higher of two level counts, every K and V row is quantized and
+ * packed, and decoding reads the packed cache (SemKV Fig. 1, Figs. 4-5);
+ * newly generated tokens are quantized block-exactly (SemKV Fig. 6).
+ *
+ * Conventions for every entry point
+ *  - Data pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or retains device memory and keeps no global state
+ *    besides its loaded code objects.  `stream` is a hipStream_t passed as
+ *    void* (NULL = the null stream).  Calls enqueue work on `stream` and
+ *    return without synchronising, except semkv_sync_check.
+ *  - fp16 data is passed as uint16_t bit patterns so this header does not
+ *    depend on HIP.
+ *  - Arguments are validated on the host before anything is launched; an
+ *    invalid call returns a negative status and enqueues nothing.  No
+ *    exception crosses the ABI.  Asynchronous device errors surface at the
+ *    next semkv_sync_check.
+ *  - Calls that mutate one semkv_cache (quantize_pack, append_block) must not
+ *    overlap; different caches may be used concurrently on different streams.
+ *  - head_dim is 128; level counts L satisfy 3 <= L <= 65536.
+ *
+ * Packed row format (ours; SemKV Table 6 fixes only the code-bit rates):
+ *  a row is the 128 values of one (sequence, token, layer, KV head, K-or-V).
+ *  m = min, M = max, scale = smallest fp16 >= (M - m)/(L - 1) (0 when M == m),
+ *  code_i = round-half-even((x_i - m)/scale) in [0, L-1]; meta = {scale, m}
+ *  as two fp16 (scale first; a zero minimum is stored as +0).  g codes form
+ *  one b-bit field sum_i code[g*j+i] * L^i, fields are laid LSB-first into a
+ *  little-endian bit stream; (g, b) = (5,8) for L=3, (4,8) L=4, (3,7) L=5,
+ *  (3,8) L=6, (1,3) L=8, (2,8) L=16, (1,16) L=65536, else (1, ceil(log2 L)).
+ *  semkv_row_bytes(L) = ceil(ceil(128/g) * b / 8): 43 B for L=6, 38 B for L=5.
+ */
+#ifndef SEMKV_H
+#define SEMKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t semkv_status;
+enum {
+  SEMKV_OK = 0,
+  SEMKV_EINVAL = -1,       /* null/misaligned pointer, size or range error */
+  SEMKV_EUNSUPPORTED = -2, /* valid but not supported (head_dim, L, ragged) */
+  SEMKV_ECAPACITY = -3,    /* a pool has no room for the rows to be written */
+  SEMKV_EWORKSPACE = -4,   /* workspace missing or smaller than required    */
+  SEMKV_EHIP = -5          /* the HIP runtime reported an error             */
+};
+
+/* Geometry of one cache.  One precision per token for all layers, KV heads,
+ * K and V (SemKV Fig. 5).  Query head h reads KV head h / (q_heads/kv_heads)
+ * (grouped-query attention of the backbones in SemKV Table 2). */
+typedef struct {
+  int32_t batch, layers, kv_heads, q_heads, head_dim; /* head_dim must be 128 */
+  int32_t L_high, L_low;   /* 3 <= L_low <= L_high <= 65536                  */
+  int32_t block;           /* generation block (SemKV Fig. 6), 1..1024       */
+  int64_t cap_high, cap_low; /* rows per (b, layer, kv head, K|V); multiple of 16 */
+} semkv_geom;
+
+/* A mixed-precision cache.  All buffers are caller-owned device memory whose
+ * sizes semkv_cache_sizes reports; every base pointer is 256-byte aligned.
+ *  codes_*  uint8  [B][layers][kv][2][cap][row_bytes(L)]  rows back to back
+ *  meta_*   fp16   [B][layers][kv][2][cap][2]              {scale, min}
+ *  tok_*    int32  [B][cap]      slot -> token index (written with the rows)
+ *  tail_kv  fp16   [B][layers][kv][2][block][128]  newest tokens, unquantized
+ *  tail_score fp32 [B][block]    their importance scores
+ *  index 2 of the [..][2] axes: 0 = K, 1 = V.
+ *  The counters are HOST-side and shared by every sequence of the batch:
+ *  rows [0, n_high) / [0, n_low) of each pool are valid, tail rows
+ *  [0, n_tail) are valid, and n_high + n_low + n_tail == n_tokens. */
+typedef struct {
+  semkv_geom g;
+  uint8_t* codes_high;
+  uint8_t* codes_low;
+  uint16_t* meta_high;
+  uint16_t* meta_low;
+  int32_t* tok_high;
+  int32_t* tok_low;
+  uint16_t* tail_kv;
+  float* tail_score;
+  int64_t n_high, n_low, n_tail, n_tokens;
+} semkv_cache;
+
+/* Packed bytes of one 128-value row at L levels; < 0 if L is unsupported. */
+int64_t semkv_row_bytes(int32_t L);
+
+/* Top-r count k = floor(r*n + 1/2) computed in double (SemKV Fig. 4: the
+ * allocation is the top-r ranking; the integer rounding is our reading).
+ * Returns < 0 if n < 0 or r is outside [0, 1]. */
+int64_t semkv_topr_count(int64_t n, double r);
+
+/* Bytes of each cache buffer for geometry *g, in this order:
+ * codes_high, codes_low, meta_high, meta_low, tok_high, tok_low, tail_kv,
+ * tail_score.  Validates *g. */
+semkv_status semkv_cache_sizes(const semkv_geom* g, int64_t bytes_out[8]);
+
+/* Workspace bytes needed by semkv_decode_* for `nlayers` layers and up to
+ * `max_tokens` cached tokens per sequence, and by semkv_append_block.
+ * Returns < 0 if *g is invalid. */
+int64_t semkv_workspace_bytes(const semkv_geom* g, int32_t nlayers, int64_t max_tokens);
+
+/* Rank (SemKV Figs. 2 and 4: rank within each prompt, no threshold; top-r
+ * forms the high-precision set H).
+ *  scores  fp32 [batch][ld_scores], the first n entries of each row are used
+ *  k       0 <= k <= n, the size of H for every sequence
+ *  perm    int32 [batch][n] out: H in ascending token order, then the other
+ *          tokens ascending (so slot j of the high pool holds perm[j])
+ *  mask    uint32 [batch][ceil(n/32)] out, nullable: bit t%32 of word t/32 is
+ *          set iff token t is in H
+ * Order: score descending, ties to the lower index, -0 == +0, NaN below
+ * every number.  Errors: EINVAL (null scores/perm, n < 1, k outside [0, n],
+ * ld_scores < n, batch < 1, n > 2^31 - 1). */
+semkv_status semkv_rank_topr(const float* scores, int32_t batch, int64_t n, int64_t ld_scores,
+                             int64_t k, int32_t* perm, uint32_t* mask, void* stream);
+
+/* Quantize and pack a prompt (SemKV Fig. 5 and Table 6).
+ *  k, v     fp16 rows; element (b, layer, head, token, d) is at
+ *           base + b*strides[0] + layer*strides[1] + head*strides[2]
+ *                + token*strides[3] + d        (strides in elements, d contiguous)
+ *  n        tokens per sequence; perm int32 [batch][n] as from semkv_rank_topr
+ *  k_high   |H|: tokens perm[b][0..k_high) go to the high pool at L_high, the
+ *           rest to the low pool at L_low
+ * Rows are written at slots n_high.. and n_low.. of each pool (K and V of
+ * every layer and KV head); tok_* records n_tokens + token.  On success the
+ * host counters advance: n_high += k_high, n_low += n - k_high,
+ * n_tokens += n.  Requires an empty tail (n_tail == 0).
+ * Errors: EINVAL (null/misaligned pointers, n < 1, k_high outside [0, n],
+ * n_tail != 0), ECAPACITY (a pool would overflow), EUNSUPPORTED (geometry). */
+semkv_status semkv_quantize_pack(semkv_cache* c, const uint16_t* k, const uint16_t* v,
+                                 const int64_t strides[4], int64_t n, const int32_t* perm,
+                                 int64_t k_high, void* stream);
+
+/* Generation-time block-exact quantization (SemKV Fig. 6).
+ *  k_new, v_new  fp16, t_new tokens per sequence, strides as in
+ *                semkv_quantize_pack; score_new fp32 [batch][t_new]
+ * The tokens are appended to the fp16 tail.  Each time the tail holds
+ * `block` tokens, the block is ranked on its own scores with
+ * k_b = semkv_topr_count(block, r), quantized, packed and appended to the
+ * pools (ascending token order within each pool), and the tail empties.
+ * With flush != 0 the residual tail is then processed the same way with
+ * k = semkv_topr_count(n_tail, r) (end of a generation turn).  Host counters
+ * are updated.  workspace: device memory of at least
+ * semkv_workspace_bytes(g, 0, 0) bytes.
+ * Errors: EINVAL, ECAPACITY, EWORKSPACE. */
+semkv_status semkv_append_block(semkv_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                                const int64_t strides[4], const float* score_new, int32_t t_new,
+                                double r, int32_t flush, void* workspace, int64_t ws_bytes,
+                                void* stream);
+
+/* Decode attention over the packed mixed-precision cache (SemKV Figs. 1 and
+ * 5: the quantized cache is what decoding reads).  For each sequence b,
+ * layer layer0 + i (0 <= i < nlayers) and query head h:
+ *   out[b][i][h] = sum_t softmax_t(sm_scale * q[b][i][h] . k_t) v_t
+ * over every cached token t -- high pool rows, low pool rows and the fp16
+ * tail rows -- of KV head h / (q_heads/kv_heads); packed rows are
+ * dequantized on the fly (x = min + code * scale).
+ *  q    fp16 [batch][nlayers][q_heads][128]
+ *  out  fp32 [batch][nlayers][q_heads][128]
+ *  workspace  >= semkv_workspace_bytes(g, nlayers, n_tokens) bytes
+ * Errors: EINVAL (pointers, layer range, empty cache), EWORKSPACE. */
+semkv_status semkv_decode_attn(const semkv_cache* c, const uint16_t* q, int32_t layer0,
+                               int32_t nlayers, float sm_scale, float* out, void* workspace,
+                               int64_t ws_bytes, void* stream);
+
+/* The two halves of semkv_decode_attn, for callers that combine partial
+ * results themselves (e.g. a context split across devices):
+ * semkv_decode_partials writes per-chunk (max logit, sum of exponentials,
+ * unnormalised output) into the workspace; semkv_decode_merge combines them
+ * with a log-sum-exp merge into `out`.  Same arguments and errors as
+ * semkv_decode_attn; the merge must use the same cache counters, layer range
+ * and workspace as the partials call before it. */
+semkv_status semkv_decode_partials(const semkv_cache* c, const uint16_t* q, int32_t layer0,
+                                   int32_t nlayers, float sm_scale, void* workspace,
+                                   int64_t ws_bytes, void* stream);
+semkv_status semkv_decode_merge(const semkv_cache* c, int32_t nlayers, float* out,
+                                void* workspace, int64_t ws_bytes, void* stream);
+
+/* Synchronise `stream` and map a sticky HIP error to SEMKV_EHIP. */
+semkv_status semkv_sync_check(void* stream);
+
+/* Static string for a status code. */
+const char* semkv_status_str(semkv_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEMKV_H */

@@ -1,0 +1,270 @@
+// Decode attention over the packed mixed-precision cache (SemKV page, Figs.
+// 1 and 5: decoding reads the quantized cache; grouped-query attention of the
+// backbones in Table 2).
+//
+// Split-K over tokens: the work of one (sequence, layer, KV head) is cut into
+// chunks of `chunk` rows of one segment (high pool, low pool, fp16 tail).
+// One workgroup per chunk computes, for every query head of the group,
+//   m = max_t z_t,  l = sum_t exp(z_t - m),  o = sum_t exp(z_t - m) v_t
+// with z_t = sm_scale * q . k_t, in two passes (keys, then values) so no
+// running rescale is needed.  A merge kernel combines the chunks with a
+// log-sum-exp reduction.  Packed rows are staged through LDS and dequantized
+// on the fly (x = min + code * scale).
+//
+// This is the generic kernel: any level count, any group size <= 8, VALU
+// arithmetic.
+#include "semkv_internal.h"
+
+namespace semkv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;
+constexpr int kChunkMax = 1024;
+constexpr int kStageBytes = kTile * 256 + 16;
+constexpr int kPartialStride = 2 + kHeadDim;   // m, l, o[128]
+
+__device__ __forceinline__ float block_reduce(float v, float* buf, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float t = __shfl_xor(v, o, 64);
+    v = is_max ? fmaxf(v, t) : v + t;
+  }
+  __syncthreads();
+  if (lane == 0) buf[wave] = v;
+  __syncthreads();
+  float r = buf[0];
+  for (int w = 1; w < kThreads / 64; ++w) r = is_max ? fmaxf(r, buf[w]) : r + buf[w];
+  return r;
+}
+
+// code d of a packed row at p (LDS), generic (g, b, L)
+__device__ __forceinline__ uint32_t unpack_code(const uint8_t* p, int d, const RowFmt& f,
+                                                const uint32_t* pw) {
+  const int fi = d / f.g;
+  const int i = d - fi * f.g;
+  const int bo = fi * f.b;
+  const int by = bo >> 3;
+  uint32_t v = (uint32_t)p[by] | ((uint32_t)p[by + 1] << 8) | ((uint32_t)p[by + 2] << 16);
+  v = (v >> (bo & 7)) & ((1u << f.b) - 1u);
+  return (v / pw[i]) % (uint32_t)f.L;
+}
+
+struct Seg {
+  int seg;       // 0 high, 1 low, 2 tail
+  int64_t t0, t1;
+};
+
+__device__ __forceinline__ Seg find_seg(const DecodeArgs& a, int x) {
+  Seg s;
+  int ch;
+  if (x < a.nch[0]) {
+    s.seg = 0; ch = x;
+  } else if (x < a.nch[0] + a.nch[1]) {
+    s.seg = 1; ch = x - a.nch[0];
+  } else {
+    s.seg = 2; ch = x - a.nch[0] - a.nch[1];
+  }
+  const int64_t n = s.seg == 0 ? a.rows[0] : (s.seg == 1 ? a.rows[1] : a.n_tail);
+  s.t0 = (int64_t)ch * a.chunk;
+  s.t1 = min(s.t0 + (int64_t)a.chunk, n);
+  return s;
+}
+
+// Stage rows [t, t + nt) of one plane (K or V) into LDS.
+__device__ void stage_tile(const DecodeArgs& a, const Seg& sg, int b, int layer, int g,
+                           int kvsel, int64_t t, int nt, uint8_t* lds, uint32_t* meta_lds) {
+  const int tid = threadIdx.x;
+  if (sg.seg < 2) {
+    const RowFmt f = a.fmt[sg.seg];
+    const int64_t plane = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2 + kvsel;
+    const uint8_t* base = a.codes[sg.seg] + plane * a.cap[sg.seg] * f.R + t * f.R;
+    const int nd = (nt * f.R + 3) >> 2;   // t * R is a multiple of 4 (t % 64 == 0)
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(base);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(lds);
+    for (int i = tid; i < nd; i += kThreads) dst[i] = src[i];
+    const uint32_t* msrc = a.meta[sg.seg] + plane * a.cap[sg.seg] + t;
+    for (int i = tid; i < nt; i += kThreads) meta_lds[i] = msrc[i];
+  } else {
+    const int64_t plane = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2 + kvsel;
+    const uint16_t* base = a.tail_kv + (plane * a.block + t) * kHeadDim;
+    const uint4* src = reinterpret_cast<const uint4*>(base);
+    uint4* dst = reinterpret_cast<uint4*>(lds);
+    for (int i = tid; i < nt * 16; i += kThreads) dst[i] = src[i];
+  }
+}
+
+__device__ __forceinline__ float row_value(const Seg& sg, const RowFmt& f, const uint8_t* lds,
+                                           const uint32_t* meta_lds, int r, int d,
+                                           const uint32_t* pw) {
+  if (sg.seg == 2) {
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(lds) + r * kHeadDim;
+    return h2f(row[d]);
+  }
+  const uint32_t m = meta_lds[r];
+  const float s = h2f((uint16_t)(m & 0xFFFFu));
+  const float mn = h2f((uint16_t)(m >> 16));
+  const uint32_t c = unpack_code(lds + r * f.R, d, f, pw);
+  return fmaf((float)c, s, mn);
+}
+
+__global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a) {
+  __shared__ float qs[kMaxGroup][kHeadDim];
+  __shared__ float sc[kMaxGroup][kChunkMax];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[kStageBytes];
+  __shared__ uint32_t meta_lds[kTile];
+  __shared__ float red[kThreads / 64];
+  __shared__ float hmax[kMaxGroup], hsum[kMaxGroup];
+
+  const int tid = threadIdx.x;
+  const Seg sg = find_seg(a, blockIdx.x);
+  const int li = blockIdx.y / a.kv_heads;
+  const int g = blockIdx.y % a.kv_heads;
+  const int b = blockIdx.z;
+  const int layer = a.layer0 + li;
+  const int G = a.group;
+  const int nt_chunk = (int)(sg.t1 - sg.t0);
+  const RowFmt f = sg.seg < 2 ? a.fmt[sg.seg] : row_fmt(65536);
+  uint32_t pw[6];
+  pw[0] = 1;
+  for (int i = 1; i < 6; ++i) pw[i] = pw[i - 1] * (uint32_t)f.L;
+
+  for (int i = tid; i < G * kHeadDim; i += kThreads) {
+    const int h = i / kHeadDim, d = i - h * kHeadDim;
+    qs[h][d] = h2f(a.q[(((int64_t)b * a.nl + li) * a.q_heads + g * G + h) * kHeadDim + d]);
+  }
+
+  // ---- pass 1: logits
+  const int r = tid >> 2, qq = tid & 3;
+  for (int64_t t = sg.t0; t < sg.t1; t += kTile) {
+    const int nt = (int)min((int64_t)kTile, sg.t1 - t);
+    __syncthreads();
+    stage_tile(a, sg, b, layer, g, 0, t, nt, stage, meta_lds);
+    __syncthreads();
+    float dot[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) dot[h] = 0.f;
+    if (r < nt) {
+      for (int d = 32 * qq; d < 32 * qq + 32; ++d) {
+        const float x = row_value(sg, f, stage, meta_lds, r, d, pw);
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h)
+          if (h < G) dot[h] = fmaf(qs[h][d], x, dot[h]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      dot[h] += __shfl_xor(dot[h], 1, 64);
+      dot[h] += __shfl_xor(dot[h], 2, 64);
+    }
+    if (r < nt && qq == 0) {
+      const int j = (int)(t - sg.t0) + r;
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h)
+        if (h < G) sc[h][j] = a.sm_scale * dot[h];
+    }
+  }
+  __syncthreads();
+
+  // ---- softmax statistics per head
+  for (int h = 0; h < G; ++h) {
+    float mx = -INFINITY;
+    for (int j = tid; j < nt_chunk; j += kThreads) mx = fmaxf(mx, sc[h][j]);
+    mx = block_reduce(mx, red, true);
+    float sum = 0.f;
+    for (int j = tid; j < nt_chunk; j += kThreads) {
+      const float p = __expf(sc[h][j] - mx);
+      sc[h][j] = p;
+      sum += p;
+    }
+    sum = block_reduce(sum, red, false);
+    if (tid == 0) {
+      hmax[h] = mx;
+      hsum[h] = sum;
+    }
+  }
+
+  // ---- pass 2: values
+  const int d = tid & (kHeadDim - 1);
+  const int hh = tid >> 7;   // heads hh, hh + 2, ...
+  float acc[kMaxGroup / 2];
+#pragma unroll
+  for (int k = 0; k < kMaxGroup / 2; ++k) acc[k] = 0.f;
+  for (int64_t t = sg.t0; t < sg.t1; t += kTile) {
+    const int nt = (int)min((int64_t)kTile, sg.t1 - t);
+    __syncthreads();
+    stage_tile(a, sg, b, layer, g, 1, t, nt, stage, meta_lds);
+    __syncthreads();
+    const int j0 = (int)(t - sg.t0);
+    for (int rr = 0; rr < nt; ++rr) {
+      const float x = row_value(sg, f, stage, meta_lds, rr, d, pw);
+#pragma unroll
+      for (int k = 0; k < kMaxGroup / 2; ++k) {
+        const int h = hh + 2 * k;
+        if (h < G) acc[k] = fmaf(sc[h][j0 + rr], x, acc[k]);
+      }
+    }
+  }
+  __syncthreads();
+
+  const int64_t u = ((((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + blockIdx.x);
+  float* wsu = a.ws + u * G * kPartialStride;
+#pragma unroll
+  for (int k = 0; k < kMaxGroup / 2; ++k) {
+    const int h = hh + 2 * k;
+    if (h < G) wsu[h * kPartialStride + 2 + d] = acc[k];
+  }
+  if (tid < G) {
+    wsu[tid * kPartialStride + 0] = hmax[tid];
+    wsu[tid * kPartialStride + 1] = hsum[tid];
+  }
+}
+
+__global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
+  const int h = blockIdx.x, li = blockIdx.y, b = blockIdx.z;
+  const int G = a.group;
+  const int g = h / G, hl = h - g * G;
+  const int d = threadIdx.x;
+  const int64_t u0 = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks;
+  const float* ws = a.ws;
+  float M = -INFINITY;
+  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, ws[((u0 + c) * G + hl) * kPartialStride]);
+  float num = 0.f, den = 0.f;
+  for (int c = 0; c < a.nchunks; ++c) {
+    const float* p = ws + ((u0 + c) * G + hl) * kPartialStride;
+    const float w = __expf(p[0] - M);
+    den = fmaf(w, p[1], den);
+    num = fmaf(w, p[2 + d], num);
+  }
+  a.out[(((int64_t)b * a.nl + li) * a.q_heads + h) * kHeadDim + d] = num / den;
+}
+
+}  // namespace
+
+int decode_chunk_tokens(int64_t tokens_per_unit, int64_t units) {
+  const int64_t target_wg = 4096;
+  int64_t desired = (target_wg + units - 1) / (units > 0 ? units : 1);
+  if (desired < 1) desired = 1;
+  int64_t c = (tokens_per_unit + desired - 1) / desired;
+  c = (c + kTile - 1) / kTile * kTile;
+  if (c < kTile) c = kTile;
+  if (c > kChunkMax) c = kChunkMax;
+  return (int)c;
+}
+
+int64_t decode_partial_floats_per_chunk(int group) { return (int64_t)group * kPartialStride; }
+
+hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.nchunks, a.nl * a.kv_heads, a.batch);
+  hipLaunchKernelGGL(decode_partials_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
+  dim3 grid(a.q_heads, a.nl, a.batch);
+  hipLaunchKernelGGL(decode_merge_kernel, grid, dim3(kHeadDim), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace semkv

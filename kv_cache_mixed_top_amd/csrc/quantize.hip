@@ -1,0 +1,200 @@
+// Quantize and pack K/V rows into the two precision pools (SemKV page,
+// Fig. 5: one precision per token, applied to K and V of every layer and KV
+// head; Table 6: affine integer-level quantizer with two fp16 scalars per
+// 128-value row).
+//
+// Workgroup = 256 threads = 64 rows x 4 lanes; one workgroup writes 64
+// consecutive slots of one pool plane (sequence, layer, KV head, K|V).  Lane
+// q of a row loads the 16-byte pieces at byte offsets 16q + 64i (i = 0..3),
+// so each load instruction of a quad covers 64 contiguous bytes.
+//
+// Codes: c = round-half-even((x - m) / s).  The fast path evaluates
+// y = fl(fl(x - m) * fl(1/s)) in fp32, whose relative error is < 2^-21; when
+// y lies within (L-1)*2^-20 of a half-integer the code is settled exactly in
+// double with the exact residuals x - m - (c0 +/- 1/2) s.
+//
+// Packing: codes go to LDS; each output byte of the tile's contiguous byte
+// stream is assembled from the fields that overlap it.  Bytes of a dword
+// that is shared with a neighbouring tile are stored one by one.
+#include "semkv_internal.h"
+
+namespace semkv {
+namespace {
+
+constexpr int kRows = 64;
+constexpr int kThreads = 256;
+constexpr int kCodeStride = kHeadDim + 2;   // u16 codes per LDS row (pad)
+
+// Exact round-half-even of (x - m)/s given a candidate c0 within 1 of it.
+__device__ __noinline__ float exact_code(float x, float m, float s, float c0) {
+  const double d = (double)x - (double)m;           // exact: fp16 operands
+  const double sd = (double)s;
+  const double c = (double)c0;
+  const double e_hi = d - (c + 0.5) * sd;           // exact (<= 45 significant bits)
+  const double e_lo = d - (c - 0.5) * sd;
+  const bool odd = (((int)c0) & 1) != 0;
+  if (e_hi > 0.0) return c0 + 1.0f;
+  if (e_hi == 0.0) return odd ? c0 + 1.0f : c0;
+  if (e_lo < 0.0) return c0 - 1.0f;
+  if (e_lo == 0.0) return odd ? c0 - 1.0f : c0;
+  return c0;
+}
+
+__global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, int tiles_high) {
+  __shared__ uint16_t codes[kRows * kCodeStride];
+
+  const int tile = blockIdx.x;
+  const int pool = tile < tiles_high ? 0 : 1;
+  const int tile_in_pool = pool == 0 ? tile : tile - tiles_high;
+  const int count = pool == 0 ? a.k_high : a.n - a.k_high;
+  const int perm_off = pool == 0 ? 0 : a.k_high;
+  const int y = blockIdx.y;
+  const int kvsel = y & 1;
+  const int head = (y >> 1) % a.kv_heads;
+  const int layer = (y >> 1) / a.kv_heads;
+  const int b = blockIdx.z;
+  const int row0 = tile_in_pool * kRows;
+  const int nrows = min(kRows, count - row0);
+  const RowFmt f = a.fmt[pool];
+
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, q = tid & 3;
+  const bool valid = r < nrows;
+  const int64_t plane = (((int64_t)b * a.layers + layer) * a.kv_heads + head) * 2 + kvsel;
+  const int64_t slot0 = a.start[pool] + row0;
+
+  // ---- load 32 values of this row (d = 8q + 32i + e)
+  int token = 0;
+  float v[32];
+  if (valid) {
+    token = a.perm[(int64_t)b * a.n + perm_off + row0 + r];
+    const uint16_t* src = a.src[kvsel] + (int64_t)b * a.sb + (int64_t)layer * a.sl +
+                          (int64_t)head * a.sh + (int64_t)token * a.st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * q + 32 * i);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * i + 2 * e] = h2f((uint16_t)(ws[e] & 0xFFFFu));
+        v[8 * i + 2 * e + 1] = h2f((uint16_t)(ws[e] >> 16));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.f;
+  }
+
+  // ---- row min / max over the quad
+  float lo = v[0], hi = v[0];
+#pragma unroll
+  for (int i = 1; i < 32; ++i) {
+    lo = fminf(lo, v[i]);
+    hi = fmaxf(hi, v[i]);
+  }
+  lo = fminf(lo, __shfl_xor(lo, 1, 64));
+  lo = fminf(lo, __shfl_xor(lo, 2, 64));
+  hi = fmaxf(hi, __shfl_xor(hi, 1, 64));
+  hi = fmaxf(hi, __shfl_xor(hi, 2, 64));
+  lo = lo + 0.0f;   // a zero minimum is stored as +0
+
+  const uint16_t sbits = scale_ceil_bits(lo, hi, f.L);
+  const float s = h2f(sbits);
+  const float lmax = (float)(f.L - 1);
+
+  // ---- codes
+  uint16_t* crow = codes + r * kCodeStride;
+  if (s > 0.0f) {
+    const float rs = 1.0f / s;
+    const float eps = lmax * 0x1p-20f + 0x1p-22f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = v[8 * i + e];
+        const float yv = (x - lo) * rs;
+        float c = rintf(yv);
+        if (fabsf(fabsf(yv - c) - 0.5f) <= eps) c = exact_code(x, lo, s, c);
+        c = fminf(fmaxf(c, 0.0f), lmax);
+        crow[8 * q + 32 * i + e] = (uint16_t)(int)c;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) crow[8 * q + 32 * i + e] = 0;
+  }
+
+  if (valid && q == 0) {
+    const int64_t slot = slot0 + r;
+    a.meta[pool][plane * a.cap[pool] + slot] = (uint32_t)sbits | ((uint32_t)f2h(lo) << 16);
+    if (layer == 0 && head == 0 && kvsel == 0)
+      a.tok[pool][(int64_t)b * a.cap[pool] + slot] = (int32_t)(a.token_base + token);
+  }
+  __syncthreads();
+
+  // ---- pack this tile's rows into the plane's byte stream
+  uint8_t* base = a.codes[pool] + plane * a.cap[pool] * f.R;
+  const int64_t B0 = slot0 * f.R;
+  const int64_t B1 = B0 + (int64_t)nrows * f.R;
+  const int64_t w0 = B0 >> 2, w1 = (B1 + 3) >> 2;
+  const int nfields = (kHeadDim + f.g - 1) / f.g;
+  uint32_t pw[6];
+  pw[0] = 1;
+  for (int i = 1; i < 6; ++i) pw[i] = pw[i - 1] * (uint32_t)f.L;
+  const uint32_t fmask = (f.b >= 32) ? 0xFFFFFFFFu : ((1u << f.b) - 1u);
+
+  for (int64_t w = w0 + tid; w < w1; w += kThreads) {
+    uint32_t val = 0;
+    bool full = true;
+    uint32_t inmask = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t pbyte = 4 * w + e;
+      if (pbyte < B0 || pbyte >= B1) { full = false; continue; }
+      inmask |= 1u << e;
+      const int local = (int)(pbyte - B0);
+      const int row = local / f.R;
+      const int jb = local - row * f.R;
+      const int bit0 = 8 * jb;
+      const int fl = bit0 / f.b;
+      const int fh = min((bit0 + 7) / f.b, nfields - 1);
+      uint32_t byte = 0;
+      for (int fi = fl; fi <= fh; ++fi) {
+        uint32_t fv = 0;
+        for (int i = 0; i < f.g; ++i) {
+          const int pos = f.g * fi + i;
+          if (pos < kHeadDim) fv += (uint32_t)codes[row * kCodeStride + pos] * pw[i];
+        }
+        fv &= fmask;
+        const int shift = f.b * fi - bit0;
+        const uint32_t part = shift >= 0 ? (fv << shift) : (fv >> (-shift));
+        byte |= part;
+      }
+      val |= (byte & 0xFFu) << (8 * e);
+    }
+    if (full) {
+      reinterpret_cast<uint32_t*>(base)[w] = val;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (inmask & (1u << e)) base[4 * w + e] = (uint8_t)(val >> (8 * e));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream) {
+  const int count_low = a.n - a.k_high;
+  const int tiles_high = (a.k_high + kRows - 1) / kRows;
+  const int tiles_low = (count_low + kRows - 1) / kRows;
+  const int tiles = tiles_high + tiles_low;
+  if (tiles == 0) return hipSuccess;
+  dim3 grid(tiles, a.layers * a.kv_heads * 2, a.batch);
+  hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(kThreads), 0, stream, a, tiles_high);
+  return hipGetLastError();
+}
+
+}  // namespace semkv

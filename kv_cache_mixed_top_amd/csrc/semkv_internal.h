@@ -1,0 +1,68 @@
+// Launch interfaces between the C ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include "semkv_common.h"
+
+namespace semkv {
+
+// ---------------------------------------------------------------- rank
+// perm/mask of `batch` sequences of n scores each (row stride ld).
+hipError_t launch_rank(const float* scores, int batch, int n, int64_t ld, int k,
+                       int32_t* perm, uint32_t* mask, hipStream_t stream);
+
+// ---------------------------------------------------------------- quantize
+struct QuantArgs {
+  const uint16_t* src[2];   // K rows, V rows
+  int64_t sb, sl, sh, st;   // element strides: batch, layer, head, token
+  const int32_t* perm;      // [batch][n]
+  int32_t n, k_high;
+  int32_t batch, layers, kv_heads;
+  uint8_t* codes[2];        // [0] high pool, [1] low pool
+  uint32_t* meta[2];        // {scale, min} fp16 pair as one word per row
+  int32_t* tok[2];
+  int64_t cap[2];
+  int64_t start[2];         // first destination slot (n_high, n_low)
+  RowFmt fmt[2];
+  int64_t token_base;       // tok_* = token_base + token
+};
+hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- append
+struct AppendArgs {
+  const uint16_t* src[2];
+  int64_t sb, sl, sh, st;
+  const float* score_new;   // [batch][t_total]
+  int32_t t_total, t_off, t_cnt;   // copy new tokens [t_off, t_off + t_cnt)
+  int32_t batch, layers, kv_heads, block;
+  int32_t pos;              // first tail row written
+  uint16_t* tail_kv;
+  float* tail_score;
+};
+hipError_t launch_append_tail(const AppendArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode
+struct DecodeArgs {
+  const uint8_t* codes[2];
+  const uint32_t* meta[2];
+  int64_t cap[2];
+  int64_t rows[2];          // valid rows per pool
+  RowFmt fmt[2];
+  const uint16_t* tail_kv;
+  int64_t n_tail;
+  int32_t block;
+  const uint16_t* q;        // [batch][nl][Hq][128]
+  float* out;               // [batch][nl][Hq][128]
+  int32_t batch, layers, kv_heads, q_heads, group, layer0, nl;
+  float sm_scale;
+  int32_t chunk;            // tokens per chunk (multiple of 64)
+  int32_t nch[3];           // chunks of high pool, low pool, tail
+  int32_t nchunks;
+  float* ws;                // partials
+};
+// Chunking rule shared by the launchers and the workspace query.
+int decode_chunk_tokens(int64_t tokens_per_unit, int64_t units);
+int64_t decode_partial_floats_per_chunk(int group);
+hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace semkv

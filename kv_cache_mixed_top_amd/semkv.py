@@ -1,0 +1,286 @@
+"""Thin Python binding of libsemkv.so (include/semkv.h).
+
+Argument marshalling only: every function forwards device pointers of torch
+tensors and the current (or given) HIP stream to the C entry point of the
+same name and raises SemKVError on a non-zero status.  No arithmetic of the
+method happens here; there is no CPU fallback -- importing this module fails
+if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsemkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m kv_cache_mixed_top_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+c_i32, c_i64, c_p, c_f32, c_f64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_float, ctypes.c_double)
+
+SEMKV_OK, SEMKV_EINVAL, SEMKV_EUNSUPPORTED, SEMKV_ECAPACITY, SEMKV_EWORKSPACE, SEMKV_EHIP = \
+    0, -1, -2, -3, -4, -5
+
+
+class semkv_geom(ctypes.Structure):
+    _fields_ = [("batch", c_i32), ("layers", c_i32), ("kv_heads", c_i32), ("q_heads", c_i32),
+                ("head_dim", c_i32), ("L_high", c_i32), ("L_low", c_i32), ("block", c_i32),
+                ("cap_high", c_i64), ("cap_low", c_i64)]
+
+
+class semkv_cache(ctypes.Structure):
+    _fields_ = [("g", semkv_geom),
+                ("codes_high", c_p), ("codes_low", c_p), ("meta_high", c_p), ("meta_low", c_p),
+                ("tok_high", c_p), ("tok_low", c_p), ("tail_kv", c_p), ("tail_score", c_p),
+                ("n_high", c_i64), ("n_low", c_i64), ("n_tail", c_i64), ("n_tokens", c_i64)]
+
+
+_SIGS = {
+    "semkv_row_bytes": (c_i64, [c_i32]),
+    "semkv_topr_count": (c_i64, [c_i64, c_f64]),
+    "semkv_cache_sizes": (c_i32, [ctypes.POINTER(semkv_geom), ctypes.POINTER(c_i64)]),
+    "semkv_workspace_bytes": (c_i64, [ctypes.POINTER(semkv_geom), c_i32, c_i64]),
+    "semkv_rank_topr": (c_i32, [c_p, c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p]),
+    "semkv_quantize_pack": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_p,
+                                    ctypes.POINTER(c_i64), c_i64, c_p, c_i64, c_p]),
+    "semkv_append_block": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_p, ctypes.POINTER(c_i64),
+                                   c_p, c_i32, c_f64, c_i32, c_p, c_i64, c_p]),
+    "semkv_decode_attn": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_i32, c_i32, c_f32, c_p,
+                                  c_p, c_i64, c_p]),
+    "semkv_decode_partials": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_i32, c_i32, c_f32,
+                                      c_p, c_i64, c_p]),
+    "semkv_decode_merge": (c_i32, [ctypes.POINTER(semkv_cache), c_i32, c_p, c_p, c_i64, c_p]),
+    "semkv_sync_check": (c_i32, [c_p]),
+    "semkv_status_str": (ctypes.c_char_p, [c_i32]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class SemKVError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn}: {_lib.semkv_status_str(status).decode()} ({status})")
+
+
+def _check(fn, status):
+    if status != SEMKV_OK:
+        raise SemKVError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _strides(t):
+    """Element strides (batch, layer, head, token) of a [B][layers][kv][n][128] view."""
+    if t.dim() != 5 or t.shape[-1] != 128 or t.stride(-1) != 1:
+        raise ValueError("K/V must be [batch][layers][kv_heads][tokens][128] with unit-stride d")
+    return (c_i64 * 4)(*[t.stride(i) for i in range(4)])
+
+
+# ------------------------------------------------------------------ host-only
+
+def semkv_row_bytes(L: int) -> int:
+    return _lib.semkv_row_bytes(L)
+
+
+def semkv_topr_count(n: int, r: float) -> int:
+    return _lib.semkv_topr_count(n, r)
+
+
+def semkv_cache_sizes(geom: semkv_geom):
+    out = (c_i64 * 8)()
+    _check("semkv_cache_sizes", _lib.semkv_cache_sizes(ctypes.byref(geom), out))
+    return list(out)
+
+
+def semkv_workspace_bytes(geom: semkv_geom, nlayers: int, max_tokens: int) -> int:
+    v = _lib.semkv_workspace_bytes(ctypes.byref(geom), nlayers, max_tokens)
+    if v < 0:
+        raise SemKVError("semkv_workspace_bytes", SEMKV_EINVAL)
+    return v
+
+
+# ------------------------------------------------------------------ device calls
+
+def semkv_rank_topr(scores, k, perm, mask=None, n=None, stream=None):
+    """scores fp32 [B][ld]; perm int32 [B][n] out; mask uint32-as-int32 [B][ceil(n/32)] out."""
+    batch = scores.shape[0]
+    n = scores.shape[1] if n is None else n
+    _check("semkv_rank_topr", _lib.semkv_rank_topr(_ptr(scores), batch, n, scores.stride(0), k,
+                                                   _ptr(perm), _ptr(mask), _stream(stream)))
+
+
+def semkv_quantize_pack(cache: "SemKVCache", K, V, perm, k_high, stream=None):
+    n = K.shape[3]
+    if V.shape != K.shape or tuple(V.stride()) != tuple(K.stride()):
+        raise ValueError("K and V must share shape and strides")
+    _check("semkv_quantize_pack",
+           _lib.semkv_quantize_pack(ctypes.byref(cache.c), _ptr(K), _ptr(V), _strides(K), n,
+                                    _ptr(perm), k_high, _stream(stream)))
+
+
+def semkv_append_block(cache: "SemKVCache", K_new, V_new, score_new, r, flush=False,
+                       workspace=None, stream=None):
+    """K_new/V_new fp16 [B][layers][kv][t_new][128] (or None with flush); score_new [B][t_new]."""
+    ws = cache.workspace if workspace is None else workspace
+    if K_new is None:
+        _check("semkv_append_block",
+               _lib.semkv_append_block(ctypes.byref(cache.c), None, None, None, None, 0, r,
+                                       int(bool(flush)), _ptr(ws), ws.numel(), _stream(stream)))
+        return
+    t_new = K_new.shape[3]
+    if V_new.shape != K_new.shape or tuple(V_new.stride()) != tuple(K_new.stride()):
+        raise ValueError("K_new and V_new must share shape and strides")
+    _check("semkv_append_block",
+           _lib.semkv_append_block(ctypes.byref(cache.c), _ptr(K_new), _ptr(V_new),
+                                   _strides(K_new), _ptr(score_new), t_new, r, int(bool(flush)),
+                                   _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def semkv_decode_attn(cache: "SemKVCache", q, out, layer0=0, sm_scale=1.0, workspace=None,
+                      stream=None):
+    """q fp16 [B][nl][Hq][128]; out fp32 [B][nl][Hq][128]."""
+    ws = cache.workspace if workspace is None else workspace
+    _check("semkv_decode_attn",
+           _lib.semkv_decode_attn(ctypes.byref(cache.c), _ptr(q), layer0, q.shape[1], sm_scale,
+                                  _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def semkv_decode_partials(cache: "SemKVCache", q, layer0=0, sm_scale=1.0, workspace=None,
+                          stream=None):
+    ws = cache.workspace if workspace is None else workspace
+    _check("semkv_decode_partials",
+           _lib.semkv_decode_partials(ctypes.byref(cache.c), _ptr(q), layer0, q.shape[1],
+                                      sm_scale, _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def semkv_decode_merge(cache: "SemKVCache", out, workspace=None, stream=None):
+    ws = cache.workspace if workspace is None else workspace
+    _check("semkv_decode_merge",
+           _lib.semkv_decode_merge(ctypes.byref(cache.c), out.shape[1], _ptr(out), _ptr(ws),
+                                   ws.numel(), _stream(stream)))
+
+
+def semkv_sync_check(stream=None):
+    _check("semkv_sync_check", _lib.semkv_sync_check(_stream(stream)))
+
+
+def semkv_status_str(status: int) -> str:
+    return _lib.semkv_status_str(status).decode()
+
+
+# ------------------------------------------------------------------ cache holder
+
+class SemKVCache:
+    """Device buffers of one cache, allocated with torch, and its C struct.
+
+    The buffers are plain tensors (views of the C layout in include/semkv.h);
+    the host counters live in the struct and are advanced by the C calls.
+    """
+
+    def __init__(self, batch, layers, kv_heads, q_heads, L_high, L_low, cap_high, cap_low,
+                 block=128, device="cuda", max_decode_layers=None, max_tokens=None):
+        g = semkv_geom(batch=batch, layers=layers, kv_heads=kv_heads, q_heads=q_heads,
+                       head_dim=128, L_high=L_high, L_low=L_low, block=block,
+                       cap_high=cap_high, cap_low=cap_low)
+        sizes = semkv_cache_sizes(g)
+        self.geom = g
+        dev = torch.device(device)
+        self.codes_high = torch.zeros(sizes[0], dtype=torch.uint8, device=dev)
+        self.codes_low = torch.zeros(sizes[1], dtype=torch.uint8, device=dev)
+        self.meta_high = torch.zeros(sizes[2] // 2, dtype=torch.int16, device=dev)
+        self.meta_low = torch.zeros(sizes[3] // 2, dtype=torch.int16, device=dev)
+        self.tok_high = torch.full((sizes[4] // 4,), -1, dtype=torch.int32, device=dev)
+        self.tok_low = torch.full((sizes[5] // 4,), -1, dtype=torch.int32, device=dev)
+        self.tail_kv = torch.zeros(sizes[6] // 2, dtype=torch.float16, device=dev)
+        self.tail_score = torch.zeros(sizes[7] // 4, dtype=torch.float32, device=dev)
+        nl = layers if max_decode_layers is None else max_decode_layers
+        mt = cap_high + cap_low + block if max_tokens is None else max_tokens
+        self.workspace = torch.empty(semkv_workspace_bytes(g, nl, mt), dtype=torch.uint8,
+                                     device=dev)
+        self.c = semkv_cache(g=g,
+                             codes_high=self.codes_high.data_ptr() or None,
+                             codes_low=self.codes_low.data_ptr() or None,
+                             meta_high=self.meta_high.data_ptr() or None,
+                             meta_low=self.meta_low.data_ptr() or None,
+                             tok_high=self.tok_high.data_ptr() or None,
+                             tok_low=self.tok_low.data_ptr() or None,
+                             tail_kv=self.tail_kv.data_ptr(),
+                             tail_score=self.tail_score.data_ptr(),
+                             n_high=0, n_low=0, n_tail=0, n_tokens=0)
+
+    # counters
+    @property
+    def n_high(self):
+        return self.c.n_high
+
+    @property
+    def n_low(self):
+        return self.c.n_low
+
+    @property
+    def n_tail(self):
+        return self.c.n_tail
+
+    @property
+    def n_tokens(self):
+        return self.c.n_tokens
+
+    def reset(self):
+        self.c.n_high = self.c.n_low = self.c.n_tail = self.c.n_tokens = 0
+
+    # shaped views of the C layout (for tests and checkpointing)
+    def codes_view(self, high: bool):
+        g = self.geom
+        L = g.L_high if high else g.L_low
+        cap = g.cap_high if high else g.cap_low
+        t = self.codes_high if high else self.codes_low
+        return t.view(g.batch, g.layers, g.kv_heads, 2, cap, semkv_row_bytes(L))
+
+    def meta_view(self, high: bool):
+        g = self.geom
+        cap = g.cap_high if high else g.cap_low
+        t = self.meta_high if high else self.meta_low
+        return t.view(g.batch, g.layers, g.kv_heads, 2, cap, 2)
+
+    def tok_view(self, high: bool):
+        g = self.geom
+        cap = g.cap_high if high else g.cap_low
+        return (self.tok_high if high else self.tok_low).view(g.batch, cap)
+
+    def tail_view(self):
+        g = self.geom
+        return self.tail_kv.view(g.batch, g.layers, g.kv_heads, 2, g.block, 128)
+
+    def state_dict(self):
+        """Buffers and counters; load_state_dict restores an identical cache."""
+        d = {k: getattr(self, k).clone() for k in ("codes_high", "codes_low", "meta_high",
+                                                   "meta_low", "tok_high", "tok_low",
+                                                   "tail_kv", "tail_score")}
+        d["counters"] = (self.c.n_high, self.c.n_low, self.c.n_tail, self.c.n_tokens)
+        return d
+
+    def load_state_dict(self, d):
+        for k in ("codes_high", "codes_low", "meta_high", "meta_low", "tok_high", "tok_low",
+                  "tail_kv", "tail_score"):
+            getattr(self, k).copy_(d[k])
+        self.c.n_high, self.c.n_low, self.c.n_tail, self.c.n_tokens = d["counters"]

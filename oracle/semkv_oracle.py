@@ -138,7 +138,9 @@ def quantize_rows(x: np.ndarray, L: int):
 
     Returns (codes int64[..., 128], scale fp16[...], minimum fp16[...]).
     codes_i = clamp(round_half_even((x_i - min) / scale), 0, L - 1); a row
-    whose max equals its min gets scale 0 and all codes 0 (reading R9).
+    whose max equals its min gets scale 0 and all codes 0 (reading R9).  A
+    minimum of -0 is stored as +0 (same arithmetic, one canonical meta byte
+    pattern; reading R6).
     """
     if not (3 <= L <= 65536):
         raise ValueError("L must be in [3, 65536]")
@@ -146,7 +148,7 @@ def quantize_rows(x: np.ndarray, L: int):
     if xh.shape[-1] != HEAD_DIM:
         raise ValueError("rows must hold 128 values")
     x64 = xh.astype(np.float64)
-    lo = x64.min(axis=-1)
+    lo = x64.min(axis=-1) + 0.0                           # a zero minimum is stored as +0
     hi = x64.max(axis=-1)
     s16 = scale_fp16_ceil(lo, hi, L)
     s64 = s16.astype(np.float64)

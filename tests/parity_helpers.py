@@ -1,0 +1,48 @@
+"""Helpers shared by the GPU parity tests (marshalling and comparison only)."""
+import numpy as np
+import torch
+
+import oracle as O
+
+TOL = 2e-3   # decode attention: |gpu - oracle| <= TOL * max(1, |oracle|)
+
+
+def cap16(x):
+    return max(16, (int(x) + 15) // 16 * 16)
+
+
+def assert_attention_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= TOL, f"{what}: max abs/rel error {worst:.3e} > {TOL}"
+    return worst
+
+
+def gpu_pools(cache, sk):
+    """Valid rows of the device pools as numpy arrays in the oracle's layout."""
+    nh, nl = cache.n_high, cache.n_low
+    out = {}
+    for name, high, n in (("high", True, nh), ("low", False, nl)):
+        out["codes_" + name] = cache.codes_view(high)[..., :n, :].cpu().numpy()
+        out["meta_" + name] = cache.meta_view(high)[..., :n, :].cpu().numpy().view(np.uint16)
+        out["tok_" + name] = cache.tok_view(high)[:, :n].cpu().numpy()
+    return out
+
+
+def assert_pools_equal(gp, op: "O.Pools", what=""):
+    for name in ("codes_high", "codes_low", "meta_high", "meta_low", "tok_high", "tok_low"):
+        a = gp[name]
+        b = getattr(op, name)
+        assert a.shape == b.shape, f"{what} {name}: shape {a.shape} != {b.shape}"
+        if not np.array_equal(a, b):
+            bad = np.argwhere(a != b)
+            raise AssertionError(f"{what} {name}: {len(bad)} mismatches, first at {bad[:5].tolist()}")
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()

@@ -219,6 +219,15 @@ def test_constant_row_exact():
         assert np.all(O.dequantize_rows(c, s, m) == -1.5)
 
 
+def test_signed_zero_minimum_stored_as_plus_zero():
+    row = np.full((1, 128), 1.0, np.float16)
+    row[0, 3] = -0.0
+    row[0, 4] = 0.0
+    c, s, m = O.quantize_rows(row, 6)
+    assert O.fp16_bits(m)[0] == 0x0000
+    assert c[0, 3] == 0 and c[0, 4] == 0
+
+
 def test_L65536_round_trip_bounds():
     """Reading R18: at 65536 levels the affine step can be coarser than the
     fp16 spacing near 0, so the round trip is a bound, not bit equality."""
