@@ -66,7 +66,11 @@ typedef struct {
 
 /* A mixed-precision cache.  All buffers are caller-owned device memory whose
  * sizes semkv_cache_sizes reports; every base pointer is 256-byte aligned.
- *  codes_*  uint8  [B][layers][kv][2][cap][row_bytes(L)]  rows back to back
+ *  codes_*  uint8  [B][layers][kv][2][cap * row_bytes(L)]  one plane per
+ *           (b, layer, kv head, K|V).  K planes hold rows back to back (row r
+ *           at r*R).  V planes are byte-planar in 16-row tiles: byte j of row
+ *           r is at (r/16)*16*R + 16*j + r%16, so one code byte of 16
+ *           consecutive tokens is contiguous.  R = semkv_row_bytes(L).
  *  meta_*   fp16   [B][layers][kv][2][cap][2]              {scale, min}
  *  tok_*    int32  [B][cap]      slot -> token index (written with the rows)
  *  tail_kv  fp16   [B][layers][kv][2][block][128]  newest tokens, unquantized

@@ -139,6 +139,7 @@ semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0
   a->nch[1] = (int32_t)((c->n_low + chunk - 1) / chunk);
   a->nch[2] = (int32_t)((c->n_tail + chunk - 1) / chunk);
   a->nchunks = a->nch[0] + a->nch[1] + a->nch[2];
+  a->x0 = 0;
   a->ws = reinterpret_cast<float*>(ws);
   const int64_t need = units * a->nchunks * decode_partial_floats_per_chunk(a->group) * 4;
   if (!ws || !aligned(ws, 256) || ws_bytes < need) return SEMKV_EWORKSPACE;

@@ -13,6 +13,8 @@
 //
 // This is the generic kernel: any level count, any group size <= 8, VALU
 // arithmetic.
+#include <cstdlib>
+
 #include "semkv_internal.h"
 
 namespace semkv {
@@ -21,7 +23,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 64;
 constexpr int kChunkMax = 1024;
-constexpr int kStageBytes = kTile * 256 + 16;
+constexpr int kStageBytes = kTile * 256 + 64;
 constexpr int kPartialStride = 2 + kHeadDim;   // m, l, o[128]
 
 __device__ __forceinline__ float block_reduce(float v, float* buf, bool is_max) {
@@ -39,14 +41,16 @@ __device__ __forceinline__ float block_reduce(float v, float* buf, bool is_max) 
   return r;
 }
 
-// code d of a packed row at p (LDS), generic (g, b, L)
-__device__ __forceinline__ uint32_t unpack_code(const uint8_t* p, int d, const RowFmt& f,
-                                                const uint32_t* pw) {
+// code d of a packed row whose byte j is at p[j * stride] (LDS): stride 1
+// for row-major K planes, 16 for byte-planar V planes
+__device__ __forceinline__ uint32_t unpack_code(const uint8_t* p, int stride, int d,
+                                                const RowFmt& f, const uint32_t* pw) {
   const int fi = d / f.g;
   const int i = d - fi * f.g;
   const int bo = fi * f.b;
   const int by = bo >> 3;
-  uint32_t v = (uint32_t)p[by] | ((uint32_t)p[by + 1] << 8) | ((uint32_t)p[by + 2] << 16);
+  uint32_t v = (uint32_t)p[by * stride] | ((uint32_t)p[(by + 1) * stride] << 8) |
+               ((uint32_t)p[(by + 2) * stride] << 16);
   v = (v >> (bo & 7)) & ((1u << f.b) - 1u);
   return (v / pw[i]) % (uint32_t)f.L;
 }
@@ -80,7 +84,9 @@ __device__ void stage_tile(const DecodeArgs& a, const Seg& sg, int b, int layer,
     const RowFmt f = a.fmt[sg.seg];
     const int64_t plane = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2 + kvsel;
     const uint8_t* base = a.codes[sg.seg] + plane * a.cap[sg.seg] * f.R + t * f.R;
-    const int nd = (nt * f.R + 3) >> 2;   // t * R is a multiple of 4 (t % 64 == 0)
+    // t * R is a multiple of 4 (t % 64 == 0); V planes are byte-planar in
+    // 16-row tiles, so whole tiles are staged
+    const int nd = kvsel == 0 ? (nt * f.R + 3) >> 2 : ((nt + 15) >> 4) * 4 * f.R;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(base);
     uint32_t* dst = reinterpret_cast<uint32_t*>(lds);
     for (int i = tid; i < nd; i += kThreads) dst[i] = src[i];
@@ -96,7 +102,7 @@ __device__ void stage_tile(const DecodeArgs& a, const Seg& sg, int b, int layer,
 }
 
 __device__ __forceinline__ float row_value(const Seg& sg, const RowFmt& f, const uint8_t* lds,
-                                           const uint32_t* meta_lds, int r, int d,
+                                           const uint32_t* meta_lds, int kvsel, int r, int d,
                                            const uint32_t* pw) {
   if (sg.seg == 2) {
     const uint16_t* row = reinterpret_cast<const uint16_t*>(lds) + r * kHeadDim;
@@ -105,7 +111,9 @@ __device__ __forceinline__ float row_value(const Seg& sg, const RowFmt& f, const
   const uint32_t m = meta_lds[r];
   const float s = h2f((uint16_t)(m & 0xFFFFu));
   const float mn = h2f((uint16_t)(m >> 16));
-  const uint32_t c = unpack_code(lds + r * f.R, d, f, pw);
+  const uint32_t c = kvsel == 0
+                         ? unpack_code(lds + r * f.R, 1, d, f, pw)
+                         : unpack_code(lds + (r >> 4) * 16 * f.R + (r & 15), 16, d, f, pw);
   return fmaf((float)c, s, mn);
 }
 
@@ -118,7 +126,8 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
   __shared__ float hmax[kMaxGroup], hsum[kMaxGroup];
 
   const int tid = threadIdx.x;
-  const Seg sg = find_seg(a, blockIdx.x);
+  const int x = a.x0 + blockIdx.x;
+  const Seg sg = find_seg(a, x);
   const int li = blockIdx.y / a.kv_heads;
   const int g = blockIdx.y % a.kv_heads;
   const int b = blockIdx.z;
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
     for (int h = 0; h < kMaxGroup; ++h) dot[h] = 0.f;
     if (r < nt) {
       for (int d = 32 * qq; d < 32 * qq + 32; ++d) {
-        const float x = row_value(sg, f, stage, meta_lds, r, d, pw);
+        const float x = row_value(sg, f, stage, meta_lds, 0, r, d, pw);
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h)
           if (h < G) dot[h] = fmaf(qs[h][d], x, dot[h]);
@@ -198,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
     __syncthreads();
     const int j0 = (int)(t - sg.t0);
     for (int rr = 0; rr < nt; ++rr) {
-      const float x = row_value(sg, f, stage, meta_lds, rr, d, pw);
+      const float x = row_value(sg, f, stage, meta_lds, 1, rr, d, pw);
 #pragma unroll
       for (int k = 0; k < kMaxGroup / 2; ++k) {
         const int h = hh + 2 * k;
@@ -208,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
   }
   __syncthreads();
 
-  const int64_t u = ((((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + blockIdx.x);
+  const int64_t u = ((((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x);
   float* wsu = a.ws + u * G * kPartialStride;
 #pragma unroll
   for (int k = 0; k < kMaxGroup / 2; ++k) {
@@ -255,10 +264,30 @@ int decode_chunk_tokens(int64_t tokens_per_unit, int64_t units) {
 
 int64_t decode_partial_floats_per_chunk(int group) { return (int64_t)group * kPartialStride; }
 
-hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.nchunks, a.nl * a.kv_heads, a.batch);
+hipError_t launch_decode_generic(const DecodeArgs& a, int count, hipStream_t stream) {
+  if (count <= 0) return hipSuccess;
+  dim3 grid(count, a.nl * a.kv_heads, a.batch);
   hipLaunchKernelGGL(decode_partials_kernel, grid, dim3(kThreads), 0, stream, a);
   return hipGetLastError();
+}
+
+// SEMKV_DECODE=generic forces the generic kernel (diagnostics and tests that
+// compare the two kernels on identical inputs); read at every launch.
+static bool force_generic() {
+  const char* e = getenv("SEMKV_DECODE");
+  return e && e[0] == 'g';
+}
+
+hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
+  DecodeArgs g = a;
+  if (!force_generic() && decode_mfma_supported(a)) {
+    hipError_t e = launch_decode_mfma(a, stream);
+    if (e != hipSuccess) return e;
+    g.x0 = a.nch[0] + a.nch[1];          // the fp16 tail chunks
+    return launch_decode_generic(g, a.nch[2], stream);
+  }
+  g.x0 = 0;
+  return launch_decode_generic(g, a.nchunks, stream);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {

@@ -1,0 +1,482 @@
+// Matrix-core decode attention over pools of 6-level and 5-level rows (the
+// SemKV page's operating pair b_high/b_low = log2 6 / log2 5, Fig. 1 and
+// Table 2).  Same split-K contract as the generic kernel in decode.hip: one
+// workgroup (one wave64) per chunk of one pool plane pair (K and V of one
+// sequence, layer and KV head), writing (m, l, o[4][128]) partials.
+//
+// Per 64-row tile:
+//  * QK^T on the 4x4x4 (16-block) f16 MFMA.  Lane t owns token row t of the
+//    row-major K plane; its base-L digits are computed with packed 16-bit
+//    integer arithmetic.  A 16-bit integer c read as fp16 is the subnormal
+//    c * 2^-24; one packed fp16 multiply by 2^14 makes it the normal value
+//    c * 2^-10 exactly.  (Measured on gfx950: a chain of these MFMAs with
+//    subnormal operands loses ~1e-6 of sum|terms|, 100x more than with
+//    normal operands, which outlier K rows with large scales turn into
+//    visible logit error.)  The 4 query heads of the KV head are the
+//    A operand; cbsz = 4 broadcasts block `abid`'s A to all 16 blocks, so the
+//    q fragments of 16 consecutive instructions share one VGPR pair.  Lane t
+//    ends with the 4 heads' logits of its own token.
+//  * logit z = sm_scale * (scale_K * (q . c) + min_K * sum(q)); softmax
+//    weights are taken against a running per-head maximum (rescaling the
+//    accumulators only when a tile raises it, so every weight is <= 1).
+//  * PV on the 16x16x32 f16 MFMA with K = 32 tokens.  V planes are stored
+//    byte-planar in 16-row tiles (byte j of 16 consecutive rows is
+//    contiguous), so one 8-byte LDS read gives one code byte of 8 tokens.
+//    The A operand is w = p * scale_V * 2^E (E per chunk keeps w below 2^14)
+//    split into two fp16 terms w_hi + w_lo issued as two MFMAs into the same
+//    accumulator, so the weights keep ~22 bits: with heavy-tailed V the
+//    min_V and scale_V * code terms nearly cancel and a single fp16 weight
+//    (11 bits) is not enough.  The B operand holds the linear features of
+//    each packed field f:
+//    f, floor(f/L), floor(f/L^2), again made normal fp16 (* 2^-10).  Digits are linear
+//    in these features (c0 = f - L*f1, c1 = f1 - L*f2, c2 = f2), so the
+//    exact digit sums are recovered from the fp32 accumulators at the end.
+//    sum_t p_t * min_V(t) is accumulated on the VALU.
+#include <utility>
+
+#include "semkv_internal.h"
+
+namespace semkv {
+namespace {
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTile = 64;
+constexpr int kBuf = 2880;          // >= 64 * 43 + 48 bytes of read slack
+constexpr int kPartialStride = 2 + kHeadDim;
+constexpr int kQkInstr = 33;        // 4x4x4 MFMAs per row (132 digit slots)
+
+__device__ __forceinline__ uint32_t u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ u16x2 v2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+__device__ __forceinline__ h4 as_h4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(h4, make_uint2(lo, hi));
+}
+__device__ __forceinline__ h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(h8, make_uint4(a, b, c, d));
+}
+
+// Per 16-bit slot: x < 216 (3 base-6 digits) or x < 128 (3 base-5 digits).
+template <int L>
+__device__ __forceinline__ void digits(uint32_t x, uint32_t& c0, uint32_t& c1, uint32_t& c2) {
+  const u16x2 v = v2(x);
+  u16x2 f1, f2;
+  if (L == 6) {
+    f1 = (v * (u16x2){171, 171}) >> (u16x2){10, 10};   // floor(v / 6), v < 216
+    f2 = (v * (u16x2){57, 57}) >> (u16x2){11, 11};     // floor(v / 36)
+  } else {
+    f1 = (v * (u16x2){205, 205}) >> (u16x2){10, 10};   // floor(v / 5), v < 128
+    f2 = (v * (u16x2){41, 41}) >> (u16x2){10, 10};     // floor(v / 25)
+  }
+  c2 = u32(f2);
+  c1 = u32(f1 - f2 * (u16x2){(unsigned short)L, (unsigned short)L});
+  c0 = u32(v - f1 * (u16x2){(unsigned short)L, (unsigned short)L});
+}
+
+template <int L>
+__device__ __forceinline__ void features(uint32_t x, uint32_t& f1o, uint32_t& f2o) {
+  const u16x2 v = v2(x);
+  if (L == 6) {
+    f1o = u32((v * (u16x2){171, 171}) >> (u16x2){10, 10});
+    f2o = u32((v * (u16x2){57, 57}) >> (u16x2){11, 11});
+  } else {
+    f1o = u32((v * (u16x2){205, 205}) >> (u16x2){10, 10});
+    f2o = u32((v * (u16x2){41, 41}) >> (u16x2){10, 10});
+  }
+}
+
+// Two 16-bit integers (< 2048) -> the normal fp16 values c * 2^-10, exactly.
+__device__ __forceinline__ uint32_t int_to_f16x2(uint32_t x) {
+  const h2 v = __builtin_bit_cast(h2, x) * (h2){(_Float16)16384.0f, (_Float16)16384.0f};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+template <int S>
+__device__ __forceinline__ f4 qk_mfma(const h4 (&qf)[3], uint32_t lo, uint32_t hi, f4 acc) {
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(qf[S / 16], as_h4(int_to_f16x2(lo), int_to_f16x2(hi)),
+                                            acc, 4, S % 16, 0);
+}
+
+// ---- 6 levels: one K row = 43 bytes = 11 dwords (the 44th byte masked)
+template <int W>
+__device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const h4 (&qf)[3],
+                                          f4 (&acc)[3]) {
+  const uint32_t X = d[W];
+  const uint32_t xe = X & 0x00FF00FFu;            // bytes 4W, 4W+2 -> 16-bit slots
+  const uint32_t xo = (X >> 8) & 0x00FF00FFu;     // bytes 4W+1, 4W+3
+  uint32_t e0, e1, e2, o0, o1, o2;
+  digits<6>(xe, e0, e1, e2);
+  digits<6>(xo, o0, o1, o2);
+  acc[0] = qk_mfma<3 * W + 0>(qf, e0, o0, acc[0]);
+  acc[1] = qk_mfma<3 * W + 1>(qf, e1, o1, acc[1]);
+  acc[2] = qk_mfma<3 * W + 2>(qf, e2, o2, acc[2]);
+}
+template <int... Ws>
+__device__ __forceinline__ void qk6(const uint32_t (&d)[12], const h4 (&qf)[3], f4 (&acc)[3],
+                                    std::integer_sequence<int, Ws...>) {
+  (qk6_dword<Ws>(d, qf, acc), ...);
+}
+
+// ---- 5 levels: one K row = 38 bytes; 7-byte units hold 8 fields of 7 bits.
+// From a word W with fields at bits 0, 7, 14, 21: slots (F0, F2) and (F1, F3).
+__device__ __forceinline__ void field_pairs(uint32_t W, uint32_t& pa, uint32_t& pb) {
+  pa = (W & 0x7Fu) | ((W << 2) & 0x7F0000u);
+  const uint32_t Wp = W >> 7;
+  pb = (Wp & 0x7Fu) | ((Wp << 2) & 0x7F0000u);
+}
+template <int Q>   // Q = 2u + quad
+__device__ __forceinline__ void qk5_quad(uint32_t W, const h4 (&qf)[3], f4 (&acc)[3]) {
+  uint32_t pa, pb, a0, a1, a2, b0, b1, b2;
+  field_pairs(W, pa, pb);
+  digits<5>(pa, a0, a1, a2);
+  digits<5>(pb, b0, b1, b2);
+  acc[0] = qk_mfma<3 * Q + 0>(qf, a0, b0, acc[0]);
+  acc[1] = qk_mfma<3 * Q + 1>(qf, a1, b1, acc[1]);
+  acc[2] = qk_mfma<3 * Q + 2>(qf, a2, b2, acc[2]);
+}
+template <int U>
+__device__ __forceinline__ void qk5_unit(const uint32_t (&d)[12], const h4 (&qf)[3],
+                                         f4 (&acc)[3]) {
+  constexpr int b0 = 7 * U;
+  const uint32_t lo = __builtin_amdgcn_alignbyte(d[b0 / 4 + 1], d[b0 / 4], b0 % 4);
+  if (U < 5) {
+    constexpr int b1 = 7 * U + 4;
+    const uint32_t hi = __builtin_amdgcn_alignbyte(d[b1 / 4 + 1], d[b1 / 4], b1 % 4);
+    const uint32_t m = __builtin_amdgcn_alignbit(hi, lo, 28);
+    qk5_quad<2 * U>(lo, qf, acc);
+    qk5_quad<2 * U + 1>(m, qf, acc);
+  } else {
+    qk5_quad<2 * U>(lo, qf, acc);   // fields 40..42 and one zero pad field
+  }
+}
+template <int... Us>
+__device__ __forceinline__ void qk5(const uint32_t (&d)[12], const h4 (&qf)[3], f4 (&acc)[3],
+                                    std::integer_sequence<int, Us...>) {
+  (qk5_unit<Us>(d, qf, acc), ...);
+}
+
+// d index of slot `i` (0..3) of QK instruction s, or -1 for a zero slot.
+template <int L>
+__device__ __forceinline__ int qk_slot_dim(int s, int i) {
+  const int order[4] = {0, 2, 1, 3};
+  if (L == 6) {
+    const int w = s / 3, k = s % 3;
+    const int byte = 4 * w + order[i];
+    const int d = 3 * byte + k;
+    return (byte < 43 && d < kHeadDim) ? d : -1;
+  } else {
+    const int q = s / 3, k = s % 3;           // q = 2u + quad
+    const int f = 4 * q + order[i];           // fields 8u + 4quad + {0,2,1,3}
+    const int d = 3 * f + k;
+    return (f < 43 && d < kHeadDim) ? d : -1;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+template <int L>
+__device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r1, int b,
+                             int li, int g, int64_t u, uint8_t* kbuf, uint8_t* vbuf,
+                             uint32_t* kmeta, uint32_t* vmeta, _Float16* wbuf) {
+  constexpr int R = (L == 6) ? 43 : 38;
+  const int lane = threadIdx.x;
+  const int layer = a.layer0 + li;
+  const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
+  const int64_t cap = a.cap[seg];
+  const uint8_t* kcodes = a.codes[seg] + plane_k * cap * R;
+  const uint8_t* vcodes = kcodes + cap * R;
+  const uint32_t* kmg = a.meta[seg] + plane_k * cap;
+  const uint32_t* vmg = kmg + cap;
+  const float sm = a.sm_scale;
+
+  // ---- queries: ABID-packed 4x4x4 A fragments and per-head sums
+  const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
+                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
+  h4 qf[3];
+  {
+    const int head = lane & 3, blk = lane >> 2;
+#pragma unroll
+    for (int P = 0; P < 3; ++P) {
+      const int s = 16 * P + blk;
+      h4 v = {0, 0, 0, 0};
+      if (s < kQkInstr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = qk_slot_dim<L>(s, i);
+          v[i] = d >= 0 ? qg[head * kHeadDim + d] : (_Float16)0.0f;
+        }
+      }
+      qf[P] = v;
+    }
+  }
+  float sumq[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
+
+  // ---- per-chunk exponent E: w = p * scale_V * 2^E stays below 2^14
+  uint32_t smax = 0;
+  for (int64_t r = r0 + lane; r < r1; r += 64) smax = max(smax, vmg[r] & 0xFFFFu);
+  smax = wave_max_u32(smax);
+  int E = 0;
+  if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
+  const float two_e = ldexpf(1.0f, E);
+
+  float mref[4], lsum[4], msum[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    mref[h] = -INFINITY;
+    lsum[h] = 0.f;
+    msum[h] = 0.f;
+  }
+  f4 acc[3][3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int k = 0; k < 3; ++k) acc[s][k] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t t0 = r0; t0 < r1; t0 += kTile) {
+    const int nt = (int)min((int64_t)kTile, r1 - t0);
+    __syncthreads();
+    {   // stage K rows (row-major) and V tiles (byte-planar by 16 rows)
+      const uint4* ks = reinterpret_cast<const uint4*>(kcodes + t0 * R);
+      uint4* kd = reinterpret_cast<uint4*>(kbuf);
+      const int nk = (nt * R + 15) >> 4;
+      for (int i = lane; i < nk; i += 64) kd[i] = ks[i];
+      const uint4* vs = reinterpret_cast<const uint4*>(vcodes + t0 * R);
+      uint4* vd = reinterpret_cast<uint4*>(vbuf);
+      const int nv = ((nt + 15) >> 4) * R;
+      for (int i = lane; i < nv; i += 64) vd[i] = vs[i];
+      kmeta[lane] = lane < nt ? kmg[t0 + lane] : 0u;
+      vmeta[lane] = lane < nt ? vmg[t0 + lane] : 0u;
+    }
+    __syncthreads();
+
+    // ---- QK^T: lane = token
+    f4 sacc[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) sacc[k] = (f4){0.f, 0.f, 0.f, 0.f};
+    {
+      const int off = lane * R;
+      const uint32_t* kb32 = reinterpret_cast<const uint32_t*>(kbuf + (off & ~3));
+      const int sh = off & 3;
+      uint32_t raw[12];
+#pragma unroll
+      for (int i = 0; i < 12; ++i) raw[i] = kb32[i];
+      uint32_t d[12];
+#pragma unroll
+      for (int i = 0; i < 11; ++i) d[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
+      d[11] = 0;
+      if (L == 6) {
+        d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
+        qk6(d, qf, sacc, std::make_integer_sequence<int, 11>{});
+      } else {
+        d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
+        d[10] = 0;
+        qk5(d, qf, sacc, std::make_integer_sequence<int, 6>{});
+      }
+    }
+    const uint32_t km = kmeta[lane];
+    const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu)) * 1024.0f;   // digits enter as c * 2^-10
+    const float kbias = sm * h2f((uint16_t)(km >> 16));
+    float z[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float s = sacc[0][h] + sacc[1][h] + sacc[2][h];
+      z[h] = lane < nt ? fmaf(kfac, s, kbias * sumq[h]) : -INFINITY;
+    }
+
+    // ---- running maximum (all weights <= 1)
+    const bool up = z[0] > mref[0] || z[1] > mref[1] || z[2] > mref[2] || z[3] > mref[3];
+    if (__ballot(up) != 0ull) {
+      float fac[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float nm = fmaxf(mref[h], wave_max(z[h]));
+        fac[h] = __expf(mref[h] - nm);              // exp(-inf) = 0 on the first tile
+        mref[h] = nm;
+        lsum[h] *= fac[h];
+        msum[h] *= fac[h];
+      }
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[s][k][r] *= fac[r];
+    }
+    const uint32_t vm = vmeta[lane];
+    const float vs = h2f((uint16_t)(vm & 0xFFFFu)) * two_e;
+    const float vmin = h2f((uint16_t)(vm >> 16));
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float p = __expf(z[h] - mref[h]);
+      lsum[h] += p;
+      msum[h] = fmaf(p, vmin, msum[h]);
+      const float w = p * vs;
+      const _Float16 whi = (_Float16)w;
+      wbuf[h * kTile + lane] = whi;
+      wbuf[4 * kTile + h * kTile + lane] = (_Float16)(w - (float)whi);
+    }
+    __syncthreads();
+
+    // ---- PV: 32 tokens per MFMA
+    const int col = lane & 15;
+    const int quad = lane >> 4;
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      if (32 * G >= nt) break;
+      h8 aw = {0, 0, 0, 0, 0, 0, 0, 0}, awl = aw;
+      if (col < 4) {
+        aw = *reinterpret_cast<const h8*>(wbuf + col * kTile + 32 * G + 8 * quad);
+        awl = *reinterpret_cast<const h8*>(wbuf + 4 * kTile + col * kTile + 32 * G + 8 * quad);
+      }
+      const int tok0 = 32 * G + 8 * quad;                 // first of this lane's 8 tokens
+      const uint8_t* vt = vbuf + (tok0 >> 4) * (16 * R) + (tok0 & 15);
+#pragma unroll
+      for (int set = 0; set < 3; ++set) {
+        const int j = 16 * set + col;                     // byte (L=6) or field (L=5)
+        uint32_t p0 = 0, p1 = 0, p2 = 0, p3 = 0;
+        if (L == 6) {
+          if (j < R) {
+            const uint2 w8 = *reinterpret_cast<const uint2*>(vt + j * 16);
+            p0 = perm(0u, w8.x, 0x0C010C00u);
+            p1 = perm(0u, w8.x, 0x0C030C02u);
+            p2 = perm(0u, w8.y, 0x0C010C00u);
+            p3 = perm(0u, w8.y, 0x0C030C02u);
+          }
+        } else {
+          if (j < 43) {
+            const int bit = 7 * j;
+            const int j0 = bit >> 3;
+            const uint2 b0 = *reinterpret_cast<const uint2*>(vt + j0 * 16);
+            const uint2 b1 = *reinterpret_cast<const uint2*>(vt + (j0 + 1) * 16);
+            const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
+            const u16x2 m7 = {0x7F, 0x7F};
+            p0 = u32((v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & m7);
+            p1 = u32((v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & m7);
+            p2 = u32((v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & m7);
+            p3 = u32((v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & m7);
+          }
+        }
+        uint32_t f10, f20, f11, f21, f12, f22, f13, f23;
+        features<L>(p0, f10, f20);
+        features<L>(p1, f11, f21);
+        features<L>(p2, f12, f22);
+        features<L>(p3, f13, f23);
+        const h8 B0 = as_h8(int_to_f16x2(p0), int_to_f16x2(p1), int_to_f16x2(p2),
+                            int_to_f16x2(p3));
+        const h8 B1 = as_h8(int_to_f16x2(f10), int_to_f16x2(f11), int_to_f16x2(f12),
+                            int_to_f16x2(f13));
+        const h8 B2 = as_h8(int_to_f16x2(f20), int_to_f16x2(f21), int_to_f16x2(f22),
+                            int_to_f16x2(f23));
+        acc[set][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B0, acc[set][0], 0, 0, 0);
+        acc[set][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B1, acc[set][1], 0, 0, 0);
+        acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B2, acc[set][2], 0, 0, 0);
+        acc[set][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(awl, B0, acc[set][0], 0, 0, 0);
+        acc[set][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(awl, B1, acc[set][1], 0, 0, 0);
+        acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(awl, B2, acc[set][2], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- epilogue: per-head sums, digits from features, partial record
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    lsum[h] = wave_sum(lsum[h]);
+    msum[h] = wave_sum(msum[h]);
+  }
+  float* wsu = a.ws + u * 4 * kPartialStride;
+  const float back = ldexpf(1.0f, 10 - E);   // features enter as f * 2^-10
+  if (lane < 16) {
+#pragma unroll
+    for (int set = 0; set < 3; ++set) {
+      const int j = 16 * set + lane;
+      if (j < 43) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float F0 = acc[set][0][r] * back;
+          const float F1 = acc[set][1][r] * back;
+          const float F2 = acc[set][2][r] * back;
+          float* o = wsu + r * kPartialStride + 2;
+          const int d = 3 * j;
+          o[d] = msum[r] + fmaf(-(float)L, F1, F0);
+          o[d + 1] = msum[r] + fmaf(-(float)L, F2, F1);
+          if (d + 2 < kHeadDim) o[d + 2] = msum[r] + F2;
+        }
+      }
+    }
+  }
+  if (lane < 4) {
+    float mv = mref[0], lv = lsum[0];
+#pragma unroll
+    for (int h = 1; h < 4; ++h)
+      if (lane == h) {
+        mv = mref[h];
+        lv = lsum[h];
+      }
+    wsu[lane * kPartialStride + 0] = mv;
+    wsu[lane * kPartialStride + 1] = lv;
+  }
+}
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
+void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[kBuf];
+  __shared__ uint32_t kmeta[kTile], vmeta[kTile];
+  __shared__ __attribute__((aligned(16))) _Float16 wbuf[2 * 4 * kTile];   // hi, lo
+
+  const int x = blockIdx.x;
+  const int seg = x < a.nch[0] ? 0 : 1;
+  const int ch = seg == 0 ? x : x - a.nch[0];
+  const int64_t r0 = (int64_t)ch * a.chunk;
+  const int64_t r1 = min(r0 + (int64_t)a.chunk, a.rows[seg]);
+  const int li = blockIdx.y / a.kv_heads;
+  const int g = blockIdx.y % a.kv_heads;
+  const int b = blockIdx.z;
+  const int64_t u = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x;
+  if (a.fmt[seg].L == 6)
+    decode_chunk<6>(a, seg, r0, r1, b, li, g, u, kbuf, vbuf, kmeta, vmeta, wbuf);
+  else
+    decode_chunk<5>(a, seg, r0, r1, b, li, g, u, kbuf, vbuf, kmeta, vmeta, wbuf);
+}
+
+}  // namespace
+
+bool decode_mfma_supported(const DecodeArgs& a) {
+  if (a.group != 4) return false;
+  for (int s = 0; s < 2; ++s)
+    if (a.rows[s] > 0 && a.fmt[s].L != 5 && a.fmt[s].L != 6) return false;
+  return true;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+  const int pool_chunks = a.nch[0] + a.nch[1];
+  if (pool_chunks == 0) return hipSuccess;
+  dim3 grid(pool_chunks, a.nl * a.kv_heads, a.batch);
+  hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace semkv

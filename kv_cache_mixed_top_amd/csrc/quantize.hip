@@ -13,9 +13,11 @@
 // y lies within (L-1)*2^-20 of a half-integer the code is settled exactly in
 // double with the exact residuals x - m - (c0 +/- 1/2) s.
 //
-// Packing: codes go to LDS; each output byte of the tile's contiguous byte
-// stream is assembled from the fields that overlap it.  Bytes of a dword
-// that is shared with a neighbouring tile are stored one by one.
+// Packing: codes go to LDS; each output byte is assembled from the fields
+// that overlap it.  K planes hold rows back to back; V planes are byte-planar
+// in 16-row tiles (the layout the decode kernel reads 8 tokens' byte from).
+// Bytes of a dword shared with rows of another workgroup are stored one by
+// one.
 #include "semkv_internal.h"
 
 namespace semkv {
@@ -40,12 +42,12 @@ __device__ __noinline__ float exact_code(float x, float m, float s, float c0) {
   return c0;
 }
 
-__global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, int tiles_high) {
-  __shared__ uint16_t codes[kRows * kCodeStride];
-
-  const int tile = blockIdx.x;
-  const int pool = tile < tiles_high ? 0 : 1;
-  const int tile_in_pool = pool == 0 ? tile : tile - tiles_high;
+// One 64-slot tile of one pool plane.  LF = level count known at compile
+// time (6 or 5), or 0 for the runtime format of the pool.
+template <int LF>
+__device__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
+                              uint16_t* codes) {
+  const RowFmt f = LF ? row_fmt(LF) : a.fmt[pool];
   const int count = pool == 0 ? a.k_high : a.n - a.k_high;
   const int perm_off = pool == 0 ? 0 : a.k_high;
   const int y = blockIdx.y;
@@ -55,7 +57,6 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, in
   const int b = blockIdx.z;
   const int row0 = tile_in_pool * kRows;
   const int nrows = min(kRows, count - row0);
-  const RowFmt f = a.fmt[pool];
 
   const int tid = threadIdx.x;
   const int r = tid >> 2, q = tid & 3;
@@ -134,29 +135,49 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, in
   }
   __syncthreads();
 
-  // ---- pack this tile's rows into the plane's byte stream
-  uint8_t* base = a.codes[pool] + plane * a.cap[pool] * f.R;
-  const int64_t B0 = slot0 * f.R;
-  const int64_t B1 = B0 + (int64_t)nrows * f.R;
+  // ---- pack.  K planes: rows back to back.  V planes: byte-planar in
+  // 16-row tiles (byte j of row r at (r/16)*16R + 16j + r%16).  Each output
+  // byte is assembled from the fields overlapping it; bytes of rows outside
+  // this workgroup's slots are left untouched.
+  const int R = f.R;
+  uint8_t* base = a.codes[pool] + plane * a.cap[pool] * R;
+  const int64_t s_lo = slot0, s_hi = slot0 + nrows;
+  int64_t B0, B1;
+  if (kvsel == 0) {
+    B0 = s_lo * R;
+    B1 = s_hi * R;
+  } else {
+    B0 = (s_lo >> 4) * 16 * R;
+    B1 = ((s_hi + 15) >> 4) * 16 * R;
+  }
   const int64_t w0 = B0 >> 2, w1 = (B1 + 3) >> 2;
   const int nfields = (kHeadDim + f.g - 1) / f.g;
   uint32_t pw[6];
   pw[0] = 1;
+#pragma unroll
   for (int i = 1; i < 6; ++i) pw[i] = pw[i - 1] * (uint32_t)f.L;
-  const uint32_t fmask = (f.b >= 32) ? 0xFFFFFFFFu : ((1u << f.b) - 1u);
+  const uint32_t fmask = (1u << f.b) - 1u;
 
   for (int64_t w = w0 + tid; w < w1; w += kThreads) {
-    uint32_t val = 0;
-    bool full = true;
-    uint32_t inmask = 0;
+    uint32_t val = 0, inmask = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int64_t pbyte = 4 * w + e;
-      if (pbyte < B0 || pbyte >= B1) { full = false; continue; }
+      if (pbyte < B0 || pbyte >= B1) continue;
+      int64_t row_abs;
+      int jb;
+      if (kvsel == 0) {
+        row_abs = pbyte / R;
+        jb = (int)(pbyte - row_abs * R);
+      } else {
+        const int64_t tile = pbyte / (16 * R);
+        const int rem = (int)(pbyte - tile * 16 * R);
+        jb = rem >> 4;
+        row_abs = tile * 16 + (rem & 15);
+      }
+      const int64_t row = row_abs - s_lo;
+      if (row < 0 || row >= nrows) continue;
       inmask |= 1u << e;
-      const int local = (int)(pbyte - B0);
-      const int row = local / f.R;
-      const int jb = local - row * f.R;
       const int bit0 = 8 * jb;
       const int fl = bit0 / f.b;
       const int fh = min((bit0 + 7) / f.b, nfields - 1);
@@ -169,12 +190,11 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, in
         }
         fv &= fmask;
         const int shift = f.b * fi - bit0;
-        const uint32_t part = shift >= 0 ? (fv << shift) : (fv >> (-shift));
-        byte |= part;
+        byte |= shift >= 0 ? (fv << shift) : (fv >> (-shift));
       }
       val |= (byte & 0xFFu) << (8 * e);
     }
-    if (full) {
+    if (inmask == 0xFu) {
       reinterpret_cast<uint32_t*>(base)[w] = val;
     } else {
 #pragma unroll
@@ -182,6 +202,14 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, in
         if (inmask & (1u << e)) base[4 * w + e] = (uint8_t)(val >> (8 * e));
     }
   }
+}
+
+template <int LH, int LL>
+__global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, int tiles_high) {
+  __shared__ uint16_t codes[kRows * kCodeStride];
+  const int tile = blockIdx.x;
+  if (tile < tiles_high) quantize_tile<LH>(a, 0, tile, codes);
+  else quantize_tile<LL>(a, 1, tile - tiles_high, codes);
 }
 
 }  // namespace
@@ -193,7 +221,12 @@ hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream) {
   const int tiles = tiles_high + tiles_low;
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, a.layers * a.kv_heads * 2, a.batch);
-  hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(kThreads), 0, stream, a, tiles_high);
+  if (a.fmt[0].L == 6 && a.fmt[1].L == 5)
+    hipLaunchKernelGGL((quantize_pack_kernel<6, 5>), grid, dim3(kThreads), 0, stream, a,
+                       tiles_high);
+  else
+    hipLaunchKernelGGL((quantize_pack_kernel<0, 0>), grid, dim3(kThreads), 0, stream, a,
+                       tiles_high);
   return hipGetLastError();
 }
 

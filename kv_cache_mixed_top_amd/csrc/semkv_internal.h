@@ -57,12 +57,19 @@ struct DecodeArgs {
   int32_t chunk;            // tokens per chunk (multiple of 64)
   int32_t nch[3];           // chunks of high pool, low pool, tail
   int32_t nchunks;
+  int32_t x0;               // first chunk index handled by a launch
   float* ws;                // partials
 };
 // Chunking rule shared by the launchers and the workspace query.
 int decode_chunk_tokens(int64_t tokens_per_unit, int64_t units);
 int64_t decode_partial_floats_per_chunk(int group);
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream);
+// Generic kernel over chunks [a.x0, a.x0 + count).
+hipError_t launch_decode_generic(const DecodeArgs& a, int count, hipStream_t stream);
+// Matrix-core kernel for the pool chunks [0, nch[0] + nch[1]) when both pool
+// formats are 6- or 5-level and the query group is 4.
+bool decode_mfma_supported(const DecodeArgs& a);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace semkv

@@ -20,12 +20,30 @@ def assert_attention_close(got, ref, what=""):
     return worst
 
 
+def planar_rows(plane, R, n):
+    """Rows 0..n-1 of a byte-planar plane (byte j of row r at
+    (r // 16) * 16 * R + 16 * j + r % 16) as [..., n, R]."""
+    r = np.arange(n)[:, None]
+    j = np.arange(R)[None, :]
+    return plane[..., (r // 16) * 16 * R + 16 * j + (r % 16)]
+
+
 def gpu_pools(cache, sk):
-    """Valid rows of the device pools as numpy arrays in the oracle's layout."""
-    nh, nl = cache.n_high, cache.n_low
+    """Valid rows of the device pools as numpy arrays in the oracle's layout.
+
+    K planes hold rows back to back; V planes are byte-planar in 16-row
+    tiles (include/semkv.h)."""
+    g = cache.geom
     out = {}
-    for name, high, n in (("high", True, nh), ("low", False, nl)):
-        out["codes_" + name] = cache.codes_view(high)[..., :n, :].cpu().numpy()
+    for name, high, n in (("high", True, cache.n_high), ("low", False, cache.n_low)):
+        L = g.L_high if high else g.L_low
+        cap = g.cap_high if high else g.cap_low
+        R = sk.semkv_row_bytes(L)
+        raw = (cache.codes_high if high else cache.codes_low).view(
+            g.batch, g.layers, g.kv_heads, 2, cap * R).cpu().numpy()
+        k_rows = raw[..., 0, :n * R].reshape(g.batch, g.layers, g.kv_heads, n, R)
+        v_rows = planar_rows(raw[..., 1, :], R, n)
+        out["codes_" + name] = np.stack([k_rows, v_rows], axis=3)
         out["meta_" + name] = cache.meta_view(high)[..., :n, :].cpu().numpy().view(np.uint16)
         out["tok_" + name] = cache.tok_view(high)[:, :n].cpu().numpy()
     return out

@@ -321,3 +321,69 @@ def test_checkpoint_roundtrip():
     sk.semkv_decode_attn(other, q, b)
     sk.semkv_sync_check()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ matrix-core decode path
+# (6,5) and uniform 6- or 5-level pools with 4 query heads per KV head take
+# the MFMA kernel; these cases cover several 64-row tiles per chunk, ragged
+# last tiles, empty pools, constant / tiny / wide rows and heavy-tailed V.
+
+@pytest.mark.parametrize("n,r,kind", [
+    (1, 0.5, "normal"), (63, 0.5, "normal"), (64, 0.25, "normal"), (65, 0.75, "normal"),
+    (130, 0.5, "mixed"), (1000, 0.1, "normal"), (3000, 0.5, "mixed"), (5000, 0.9, "normal"),
+    (700, 0.0, "normal"), (700, 1.0, "normal"), (2049, 0.5, "studentt"),
+])
+def test_decode_mfma_shapes(n, r, kind):
+    _print("decode mfma", n, r, kind)
+    rng = np.random.default_rng(n * 3 + int(r * 10))
+    B, layers, kv, Hq = 2, 2, 2, 8
+    if kind == "studentt":
+        K, _ = _kv(rng, B, layers, kv, n)
+        z = rng.standard_normal((B, layers, kv, n, 128))
+        chi = (rng.standard_normal((B, layers, kv, n, 128, 4)) ** 2).sum(-1)
+        V = (z / np.sqrt(chi / 4)).astype(np.float16)
+    else:
+        K, V = _kv(rng, B, layers, kv, n, kind)
+    s = rng.random((B, n)).astype(np.float32)
+    Lh, Ll = (6, 6) if r == 1.0 else (6, 5)
+    cache, op = _quantize_case(K, V, s, r, Lh, Ll, f"mfma n={n}")
+    for sm in (1.0, 1 / math.sqrt(128)):
+        q = (rng.standard_normal((B, layers, Hq, 128)) / math.sqrt(128)).astype(np.float16)
+        out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
+        sk.semkv_decode_attn(cache, to_dev(q), out, sm_scale=sm)
+        sk.semkv_sync_check()
+        assert_attention_close(out.cpu().numpy(), O.decode_attention(q, op, sm),
+                               f"mfma n={n} r={r} {kind} sm={sm}")
+
+
+@pytest.mark.parametrize("L", [5, 6])
+def test_decode_mfma_uniform_levels(L):
+    _print("decode mfma uniform", L)
+    rng = np.random.default_rng(L)
+    B, layers, kv, Hq, n = 1, 2, 2, 8, 777
+    K, V = _kv(rng, B, layers, kv, n)
+    s = rng.random((B, n)).astype(np.float32)
+    cache, op = _quantize_case(K, V, s, 0.0, L, L, f"uniform L={L}")
+    q = (rng.standard_normal((B, layers, Hq, 128)) / math.sqrt(128)).astype(np.float16)
+    out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
+    sk.semkv_decode_attn(cache, to_dev(q), out)
+    sk.semkv_sync_check()
+    assert_attention_close(out.cpu().numpy(), O.decode_attention(q, op, 1.0), f"uniform {L}")
+
+
+def test_decode_mfma_large_logits():
+    """Peaked softmax: a few tokens dominate, the running maximum moves
+    between tiles, and exp() must not overflow."""
+    _print("decode mfma peaked")
+    rng = np.random.default_rng(99)
+    B, layers, kv, Hq, n = 1, 1, 2, 8, 4000
+    K, V = _kv(rng, B, layers, kv, n)
+    K[:, :, :, 3000:3010] *= 4.0            # late tokens with large keys
+    K = K.astype(np.float16)
+    s = rng.random((B, n)).astype(np.float32)
+    cache, op = _quantize_case(K, V, s, 0.5, 6, 5, "peaked")
+    q = rng.standard_normal((B, layers, Hq, 128)).astype(np.float16)      # not pre-scaled
+    out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
+    sk.semkv_decode_attn(cache, to_dev(q), out, sm_scale=0.5)
+    sk.semkv_sync_check()
+    assert_attention_close(out.cpu().numpy(), O.decode_attention(q, op, 0.5), "peaked")
