@@ -230,22 +230,53 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
   }
 }
 
+// Log-sum-exp merge of the chunk partials of one (sequence, layer, query
+// head): the chunk maxima and sums are read in parallel, the weights
+// exp(m_c - M) go to LDS, then each thread combines one output dimension
+// with an unrolled loop over the chunks.
 __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
+  extern __shared__ float wch[];           // nchunks weights
+  __shared__ float red[2];
   const int h = blockIdx.x, li = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
   const int g = h / G, hl = h - g * G;
   const int d = threadIdx.x;
   const int64_t u0 = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks;
   const float* ws = a.ws;
+  const int nc = a.nchunks;
   float M = -INFINITY;
-  for (int c = 0; c < a.nchunks; ++c) M = fmaxf(M, ws[((u0 + c) * G + hl) * kPartialStride]);
-  float num = 0.f, den = 0.f;
-  for (int c = 0; c < a.nchunks; ++c) {
+  for (int c = d; c < nc; c += kHeadDim) M = fmaxf(M, ws[((u0 + c) * G + hl) * kPartialStride]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if ((d & 63) == 0) red[d >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float den = 0.f;
+  for (int c = d; c < nc; c += kHeadDim) {
     const float* p = ws + ((u0 + c) * G + hl) * kPartialStride;
     const float w = __expf(p[0] - M);
+    wch[c] = w;
     den = fmaf(w, p[1], den);
-    num = fmaf(w, p[2 + d], num);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+  __syncthreads();
+  if ((d & 63) == 0) red[d >> 6] = den;
+  __syncthreads();
+  den = red[0] + red[1];
+  float num = 0.f;
+  const float* pd = ws + (u0 * G + hl) * kPartialStride + 2 + d;
+  const int64_t step = (int64_t)G * kPartialStride;
+  int c = 0;
+  for (; c + 4 <= nc; c += 4) {
+    const float v0 = pd[(c + 0) * step], v1 = pd[(c + 1) * step];
+    const float v2 = pd[(c + 2) * step], v3 = pd[(c + 3) * step];
+    num = fmaf(wch[c], v0, num);
+    num = fmaf(wch[c + 1], v1, num);
+    num = fmaf(wch[c + 2], v2, num);
+    num = fmaf(wch[c + 3], v3, num);
+  }
+  for (; c < nc; ++c) num = fmaf(wch[c], pd[c * step], num);
   a.out[(((int64_t)b * a.nl + li) * a.q_heads + h) * kHeadDim + d] = num / den;
 }
 
@@ -278,9 +309,11 @@ static bool force_generic() {
   return e && e[0] == 'g';
 }
 
+bool decode_use_mfma(const DecodeArgs& a) { return !force_generic() && decode_mfma_supported(a); }
+
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
   DecodeArgs g = a;
-  if (!force_generic() && decode_mfma_supported(a)) {
+  if (decode_use_mfma(a)) {
     hipError_t e = launch_decode_mfma(a, stream);
     if (e != hipSuccess) return e;
     g.x0 = a.nch[0] + a.nch[1];          // the fp16 tail chunks
@@ -292,8 +325,23 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.q_heads, a.nl, a.batch);
-  hipLaunchKernelGGL(decode_merge_kernel, grid, dim3(kHeadDim), 0, stream, a);
+  hipLaunchKernelGGL(decode_merge_kernel, grid, dim3(kHeadDim), a.nchunks * sizeof(float),
+                     stream, a);
   return hipGetLastError();
+}
+
+int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units) {
+  const int64_t slots = decode_mfma_resident_waves();
+  int64_t per_unit = slots / (units > 0 ? units : 1);
+  if (per_unit < 2) per_unit = 2;
+  // smallest tile multiple whose high-pool plus low-pool chunk count fits the
+  // resident slots of one unit
+  auto count = [&](int64_t c) { return (n_high + c - 1) / c + (n_low + c - 1) / c; };
+  int64_t c = (n_high + n_low + per_unit - 1) / per_unit;
+  c = (c + kTile - 1) / kTile * kTile;
+  if (c < kTile) c = kTile;
+  while (count(c) > per_unit) c += kTile;
+  return (int)c;
 }
 
 }  // namespace semkv

@@ -23,8 +23,8 @@
 //    byte-planar in 16-row tiles (byte j of 16 consecutive rows is
 //    contiguous), so one 8-byte LDS read gives one code byte of 8 tokens.
 //    The A operand is w = p * scale_V * 2^E (E per chunk keeps w below 2^14)
-//    split into two fp16 terms w_hi + w_lo issued as two MFMAs into the same
-//    accumulator, so the weights keep ~22 bits: with heavy-tailed V the
+//    split into two fp16 terms w_hi (A rows 0-3) + w_lo (rows 4-7), summed
+//    once at the end, so the weights keep ~22 bits: with heavy-tailed V the
 //    min_V and scale_V * code terms nearly cancel and a single fp16 weight
 //    (11 bits) is not enough.  The B operand holds the linear features of
 //    each packed field f:
@@ -46,7 +46,7 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 64;
-constexpr int kBuf = 2880;          // >= 64 * 43 + 48 bytes of read slack
+constexpr int kBuf = 3072;          // 3 x 1 KB load blocks (>= 64 * 43 + 48 read slack)
 constexpr int kPartialStride = 2 + kHeadDim;
 constexpr int kQkInstr = 33;        // 4x4x4 MFMAs per row (132 digit slots)
 
@@ -109,7 +109,7 @@ __device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const h4 (&qf
                                           f4 (&acc)[3]) {
   const uint32_t X = d[W];
   const uint32_t xe = X & 0x00FF00FFu;            // bytes 4W, 4W+2 -> 16-bit slots
-  const uint32_t xo = (X >> 8) & 0x00FF00FFu;     // bytes 4W+1, 4W+3
+  const uint32_t xo = perm(0u, X, 0x0C030C01u);   // bytes 4W+1, 4W+3
   uint32_t e0, e1, e2, o0, o1, o2;
   digits<6>(xe, e0, e1, e2);
   digits<6>(xo, o0, o1, o2);
@@ -194,12 +194,23 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS of one wave (a workgroup is one wave): two staging buffers of K rows
+// and V tiles filled by direct global->LDS loads, plus the softmax weights.
+// 13312 bytes, so that twelve workgroups fit in the 160 KB of one CU.
+struct Stage {
+  uint8_t k[2][kBuf];
+  uint8_t v[2][kBuf];
+  _Float16 w[2 * 4 * kTile];   // hi, lo
+};
+
 template <int L>
-__device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r1, int b,
-                             int li, int g, int64_t u, uint8_t* kbuf, uint8_t* vbuf,
-                             uint32_t* kmeta, uint32_t* vmeta, _Float16* wbuf) {
+__device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r1,
+                                             int b, int li, int g, int64_t u, Stage& st) {
   constexpr int R = (L == 6) ? 43 : 38;
   const int lane = threadIdx.x;
+  _Float16* wbuf = st.w;
   const int layer = a.layer0 + li;
   const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
   const int64_t cap = a.cap[seg];
@@ -255,22 +266,72 @@ __device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r
 #pragma unroll
     for (int k = 0; k < 3; ++k) acc[s][k] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t t0 = r0; t0 < r1; t0 += kTile) {
+  // Direct global->LDS loads of rows [t0, t0 + nt) into buffer `buf`: each
+  // instruction moves 16 bytes per lane (1 KB); chunks past the valid range
+  // re-read the last valid chunk so that no load leaves the plane.  The
+  // lane's own K and V meta words go to registers.
+  uint32_t km_next = 0, vm_next = 0;
+  auto issue = [&](int buf, int64_t t0, int nt) {
+    const int nk = (nt * R + 15) >> 4;
+    const uint8_t* ks = kcodes + t0 * R;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (64 * i < nk)
+        __builtin_amdgcn_global_load_lds(ks + 16 * min(64 * i + lane, nk - 1),
+                                         (lds_void*)(st.k[buf] + 1024 * i), 16, 0, 0);
+    const int nv = ((nt + 15) >> 4) * R;          // whole 16-row byte-planar tiles
+    const uint8_t* vs = vcodes + t0 * R;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (64 * i < nv)
+        __builtin_amdgcn_global_load_lds(vs + 16 * min(64 * i + lane, nv - 1),
+                                         (lds_void*)(st.v[buf] + 1024 * i), 16, 0, 0);
+    const int mi = min(lane, nt - 1);
+    km_next = kmg[t0 + mi];
+    vm_next = vmg[t0 + mi];
+  };
+
+  // The tile loop keeps one tile's loads in flight while computing the
+  // previous one.  Only the loop head waits for outstanding loads; inside a
+  // tile, LDS hand-offs between lanes of the (single) wave only wait for the
+  // LDS queue (a workgroup barrier would also wait for the prefetch).
+  int buf = 0;
+  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
+  for (int64_t t0 = r0; t0 < r1; t0 += kTile, buf ^= 1) {
     const int nt = (int)min((int64_t)kTile, r1 - t0);
-    __syncthreads();
-    {   // stage K rows (row-major) and V tiles (byte-planar by 16 rows)
-      const uint4* ks = reinterpret_cast<const uint4*>(kcodes + t0 * R);
-      uint4* kd = reinterpret_cast<uint4*>(kbuf);
-      const int nk = (nt * R + 15) >> 4;
-      for (int i = lane; i < nk; i += 64) kd[i] = ks[i];
-      const uint4* vs = reinterpret_cast<const uint4*>(vcodes + t0 * R);
-      uint4* vd = reinterpret_cast<uint4*>(vbuf);
-      const int nv = ((nt + 15) >> 4) * R;
-      for (int i = lane; i < nv; i += 64) vd[i] = vs[i];
-      kmeta[lane] = lane < nt ? kmg[t0 + lane] : 0u;
-      vmeta[lane] = lane < nt ? vmg[t0 + lane] : 0u;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile's loads have landed
+    __syncthreads();                                     // every lane is past tile - 1
+    const uint8_t* kbuf = st.k[buf];
+    const uint8_t* vbuf = st.v[buf];
+    const int col = lane & 15;
+    const int quad = lane >> 4;
+
+    // This lane's V code bytes of the tile (8 tokens x one byte per group and
+    // set; two bytes for 5 levels) are read into registers before the next
+    // tile's loads are issued: LDS reads that follow an in-flight
+    // global->LDS load of the same array would wait for it.
+    uint2 vr[2][3][L == 6 ? 1 : 2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      const int tok0 = 32 * G + 8 * quad;
+      const uint8_t* vt = vbuf + (tok0 >> 4) * (16 * R) + (tok0 & 15);
+#pragma unroll
+      for (int set = 0; set < 3; ++set) {
+        const int j = 16 * set + col;
+        if (L == 6) {
+          vr[G][set][0] = (32 * G < nt && j < R) ? *reinterpret_cast<const uint2*>(vt + j * 16)
+                                                : make_uint2(0u, 0u);
+        } else {
+          const int j0 = (7 * j) >> 3;
+          const bool ok = 32 * G < nt && j < 43;
+          vr[G][set][0] = ok ? *reinterpret_cast<const uint2*>(vt + j0 * 16) : make_uint2(0u, 0u);
+          vr[G][set][L == 6 ? 0 : 1] =
+              ok ? *reinterpret_cast<const uint2*>(vt + (j0 + 1) * 16) : make_uint2(0u, 0u);
+        }
+      }
     }
-    __syncthreads();
+    const uint32_t km = km_next;
+    const uint32_t vm = vm_next;
 
     // ---- QK^T: lane = token
     f4 sacc[3];
@@ -283,6 +344,8 @@ __device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r
       uint32_t raw[12];
 #pragma unroll
       for (int i = 0; i < 12; ++i) raw[i] = kb32[i];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // staging reads done
+      if (t0 + kTile < r1) issue(buf ^ 1, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
       uint32_t d[12];
 #pragma unroll
       for (int i = 0; i < 11; ++i) d[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
@@ -296,7 +359,6 @@ __device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r
         qk5(d, qf, sacc, std::make_integer_sequence<int, 6>{});
       }
     }
-    const uint32_t km = kmeta[lane];
     const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu)) * 1024.0f;   // digits enter as c * 2^-10
     const float kbias = sm * h2f((uint16_t)(km >> 16));
     float z[4];
@@ -325,7 +387,6 @@ __device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[s][k][r] *= fac[r];
     }
-    const uint32_t vm = vmeta[lane];
     const float vs = h2f((uint16_t)(vm & 0xFFFFu)) * two_e;
     const float vmin = h2f((uint16_t)(vm >> 16));
 #pragma unroll
@@ -338,46 +399,35 @@ __device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r
       wbuf[h * kTile + lane] = whi;
       wbuf[4 * kTile + h * kTile + lane] = (_Float16)(w - (float)whi);
     }
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // weights visible to the wave
 
     // ---- PV: 32 tokens per MFMA
-    const int col = lane & 15;
-    const int quad = lane >> 4;
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       if (32 * G >= nt) break;
-      h8 aw = {0, 0, 0, 0, 0, 0, 0, 0}, awl = aw;
-      if (col < 4) {
-        aw = *reinterpret_cast<const h8*>(wbuf + col * kTile + 32 * G + 8 * quad);
-        awl = *reinterpret_cast<const h8*>(wbuf + 4 * kTile + col * kTile + 32 * G + 8 * quad);
-      }
-      const int tok0 = 32 * G + 8 * quad;                 // first of this lane's 8 tokens
-      const uint8_t* vt = vbuf + (tok0 >> 4) * (16 * R) + (tok0 & 15);
+      // A rows 0-3: w_hi of the 4 heads, rows 4-7: w_lo; rows 8-15 repeat
+      // them and only feed C rows 8-15, which are never read.
+      const h8 aw = *reinterpret_cast<const h8*>(wbuf + (col & 7) * kTile + 32 * G + 8 * quad);
 #pragma unroll
       for (int set = 0; set < 3; ++set) {
         const int j = 16 * set + col;                     // byte (L=6) or field (L=5)
-        uint32_t p0 = 0, p1 = 0, p2 = 0, p3 = 0;
+        uint32_t p0, p1, p2, p3;
         if (L == 6) {
-          if (j < R) {
-            const uint2 w8 = *reinterpret_cast<const uint2*>(vt + j * 16);
-            p0 = perm(0u, w8.x, 0x0C010C00u);
-            p1 = perm(0u, w8.x, 0x0C030C02u);
-            p2 = perm(0u, w8.y, 0x0C010C00u);
-            p3 = perm(0u, w8.y, 0x0C030C02u);
-          }
+          const uint2 w8 = vr[G][set][0];
+          p0 = perm(0u, w8.x, 0x0C010C00u);
+          p1 = perm(0u, w8.x, 0x0C030C02u);
+          p2 = perm(0u, w8.y, 0x0C010C00u);
+          p3 = perm(0u, w8.y, 0x0C030C02u);
         } else {
-          if (j < 43) {
-            const int bit = 7 * j;
-            const int j0 = bit >> 3;
-            const uint2 b0 = *reinterpret_cast<const uint2*>(vt + j0 * 16);
-            const uint2 b1 = *reinterpret_cast<const uint2*>(vt + (j0 + 1) * 16);
-            const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
-            const u16x2 m7 = {0x7F, 0x7F};
-            p0 = u32((v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & m7);
-            p1 = u32((v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & m7);
-            p2 = u32((v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & m7);
-            p3 = u32((v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & m7);
-          }
+          const int bit = 7 * j;
+          const uint2 b0 = vr[G][set][0];
+          const uint2 b1 = vr[G][set][L == 6 ? 0 : 1];
+          const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
+          const u16x2 m7 = {0x7F, 0x7F};
+          p0 = u32((v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & m7);
+          p1 = u32((v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & m7);
+          p2 = u32((v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & m7);
+          p3 = u32((v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & m7);
         }
         uint32_t f10, f20, f11, f21, f12, f22, f13, f23;
         features<L>(p0, f10, f20);
@@ -393,9 +443,6 @@ __device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r
         acc[set][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B0, acc[set][0], 0, 0, 0);
         acc[set][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B1, acc[set][1], 0, 0, 0);
         acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B2, acc[set][2], 0, 0, 0);
-        acc[set][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(awl, B0, acc[set][0], 0, 0, 0);
-        acc[set][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(awl, B1, acc[set][1], 0, 0, 0);
-        acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(awl, B2, acc[set][2], 0, 0, 0);
       }
     }
   }
@@ -406,6 +453,13 @@ __device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r
     lsum[h] = wave_sum(lsum[h]);
     msum[h] = wave_sum(msum[h]);
   }
+  // C rows 4-7 (lanes 16-31) hold the w_lo products of the heads in rows 0-3
+#pragma unroll
+  for (int set = 0; set < 3; ++set)
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[set][k][r] += __shfl_xor(acc[set][k][r], 16, 64);
   float* wsu = a.ws + u * 4 * kPartialStride;
   const float back = ldexpf(1.0f, 10 - E);   // features enter as f * 2^-10
   if (lane < 16) {
@@ -442,10 +496,7 @@ __device__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r
 
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
 void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[kBuf];
-  __shared__ __attribute__((aligned(16))) uint8_t vbuf[kBuf];
-  __shared__ uint32_t kmeta[kTile], vmeta[kTile];
-  __shared__ __attribute__((aligned(16))) _Float16 wbuf[2 * 4 * kTile];   // hi, lo
+  __shared__ __attribute__((aligned(16))) Stage st;
 
   const int x = blockIdx.x;
   const int seg = x < a.nch[0] ? 0 : 1;
@@ -457,12 +508,29 @@ void decode_mfma_kernel(DecodeArgs a) {
   const int b = blockIdx.z;
   const int64_t u = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x;
   if (a.fmt[seg].L == 6)
-    decode_chunk<6>(a, seg, r0, r1, b, li, g, u, kbuf, vbuf, kmeta, vmeta, wbuf);
+    decode_chunk<6>(a, seg, r0, r1, b, li, g, u, st);
   else
-    decode_chunk<5>(a, seg, r0, r1, b, li, g, u, kbuf, vbuf, kmeta, vmeta, wbuf);
+    decode_chunk<5>(a, seg, r0, r1, b, li, g, u, st);
 }
 
 }  // namespace
+
+// Workgroups of the matrix-core kernel resident on the device at once
+// (registers and LDS both limit it); the pool chunking fills them once.
+int64_t decode_mfma_resident_waves() {
+  static int64_t slots = 0;
+  if (slots <= 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel, 64, 0) !=
+            hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return 2816;
+    slots = (int64_t)cus * per_cu;
+  }
+  return slots;
+}
 
 bool decode_mfma_supported(const DecodeArgs& a) {
   if (a.group != 4) return false;

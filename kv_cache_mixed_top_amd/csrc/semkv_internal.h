@@ -69,6 +69,13 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int count, hipStream_t str
 // Matrix-core kernel for the pool chunks [0, nch[0] + nch[1]) when both pool
 // formats are 6- or 5-level and the query group is 4.
 bool decode_mfma_supported(const DecodeArgs& a);
+// The matrix-core kernel will run for these arguments (supported and not
+// disabled with SEMKV_DECODE=generic).
+bool decode_use_mfma(const DecodeArgs& a);
+// Pool chunk rows for the matrix-core kernel: enough chunks per (sequence,
+// layer, KV head) to fill the device's resident wave slots once.
+int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units);
+int64_t decode_mfma_resident_waves();
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
 
