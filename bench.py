@@ -68,6 +68,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=16,
                     help="layers of the bounded oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a streaming copy of MIB MiB (read + write) three times, "
+                         "the reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -78,6 +81,19 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n_el = args.calibrate_copy * (1 << 20) // 4
+        src = torch.arange(n_el, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)            # one 4-byte read + one 4-byte write per element
+        torch.cuda.synchronize()
+        assert int(dst[-1]) == -(n_el - 1)
+        print(json.dumps({"copy_bytes_read": n_el * 4, "copy_bytes_written": n_el * 4,
+                          "launches": 3}), flush=True)
+        return
+
     import workloads as W
     from kv_cache_mixed_top_amd import semkv as sk
 
@@ -169,7 +185,9 @@ def main():
     quant_gbs = quant_bytes / (ms_quant * 1e-3) / 1e9
     dec_gbs = decode_bytes / (ms_dec * 1e-3) / 1e9 if D else 0.0
     part_gbs = partial_bytes / (ms_part * 1e-3) / 1e9 if D else 0.0
-    kernel_src = ["kv_cache_mixed_top_amd/csrc/decode.hip"]
+    kernel_src = ["kv_cache_mixed_top_amd/csrc/decode_mfma.hip",
+                  "kv_cache_mixed_top_amd/csrc/semkv_internal.h",
+                  "kv_cache_mixed_top_amd/csrc/semkv_common.h"]
     traffic = traffic_for(kernel_src)
 
     result = {
@@ -183,7 +201,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "layers": layers, "kv_heads": kv,
                    "q_heads": Hq, "head_dim": 128, "tokens": n, "r": w.r,

@@ -13,18 +13,18 @@ Source pages (cited by title and figure/table; the text is not quoted):
   figure/table captions (Figs. 1-6, Tables 2, 6, 7) and its abstract.
 
 The pages give captions and an abstract only; where they leave a step open,
-the reading used here is the plainest one that the rest supports.  Every such
-reading is listed in DESIGN.md ("Readings of the pages").  In short:
+the reading used here is the plainest one that the rest supports, marked
+"(open on the pages)" below.  In short:
 
-  * k = floor(r*n + 1/2)                                 (reading R1)
+  * k = floor(r*n + 1/2)                                 (open on the pages)
   * ties in score go to the lower token index; -0 == +0; NaN ranks below
-    every number                                         (reading R2)
+    every number                                         (open on the pages)
   * one top-r set per sequence, shared by every layer, KV head, K and V
                                                          (SemKV Fig. 5)
   * a quantization row is the 128 values of one (token, layer, KV head,
     K-or-V); two fp16 scalars per row: scale then min   (SemKV Table 6)
   * scale = smallest fp16 >= (max-min)/(L-1); codes = round-half-even of
-    (x-min)/scale, clamped to [0, L-1]                   (readings R7, R8)
+    (x-min)/scale, clamped to [0, L-1]                   (open on the pages)
   * packing: g codes of base L per b-bit field, first code in the least
     significant digit, fields LSB-first in a little-endian bit stream
     (our layout; the pages fix only the rates of SemKV Table 6)
@@ -52,7 +52,8 @@ HEAD_DIM = 128
 def topr_count(n: int, r: float) -> int:
     """Number of high-precision tokens for a fraction r of n tokens.
 
-    Reading R1: round r*n to the nearest integer, halves up, in float64.
+    Open on the pages; our reading: round r*n to the nearest integer, halves
+    up, in float64.
     """
     if n < 0 or not (0.0 <= r <= 1.0):
         raise ValueError("need n >= 0 and 0 <= r <= 1")
@@ -63,7 +64,7 @@ def rank_order(scores: np.ndarray) -> np.ndarray:
     """Token indices ordered best-first: score descending, index ascending.
 
     Scores compare as IEEE numbers (so -0 equals +0); every NaN ranks below
-    every number and NaNs tie among themselves (reading R2).
+    every number and NaNs tie among themselves (open on the pages).
     """
     s = np.asarray(scores, dtype=np.float64).ravel()
     n = s.shape[0]
@@ -114,7 +115,8 @@ def rank_topr_batch(scores: np.ndarray, k: int):
 
 
 def scale_fp16_ceil(lo: np.ndarray, hi: np.ndarray, L: int) -> np.ndarray:
-    """Smallest fp16 value >= (hi - lo) / (L - 1), elementwise (reading R7).
+    """Smallest fp16 value >= (hi - lo) / (L - 1), elementwise (open on the
+    pages: a ceiling, so that no code is clipped).
 
     hi - lo is exact in float64 (fp16 operands); the correctly rounded float64
     quotient has the same fp16 ceiling as the exact quotient because a
@@ -138,9 +140,9 @@ def quantize_rows(x: np.ndarray, L: int):
 
     Returns (codes int64[..., 128], scale fp16[...], minimum fp16[...]).
     codes_i = clamp(round_half_even((x_i - min) / scale), 0, L - 1); a row
-    whose max equals its min gets scale 0 and all codes 0 (reading R9).  A
+    whose max equals its min gets scale 0 and all codes 0 (open on the pages).  A
     minimum of -0 is stored as +0 (same arithmetic, one canonical meta byte
-    pattern; reading R6).
+    pattern; open on the pages).
     """
     if not (3 <= L <= 65536):
         raise ValueError("L must be in [3, 65536]")

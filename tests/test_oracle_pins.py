@@ -22,7 +22,7 @@ from conftest import read_table
 
 def ranks_before(s, i, j):
     """Token i precedes token j: higher score, equal scores by lower index,
-    NaN below every number (reading R2)."""
+    NaN below every number (open on the pages; our reading)."""
     a, b = float(s[i]), float(s[j])
     if math.isnan(a) and math.isnan(b):
         return i < j
@@ -100,7 +100,7 @@ def test_rank_special_cases():
 
 
 def test_topr_count():
-    # reading R1: nearest integer, halves up
+    # open on the pages; our reading: nearest integer, halves up
     assert O.topr_count(512, 0.25) == 128
     assert O.topr_count(32768, 0.5) == 16384
     assert O.topr_count(32768, 0.1) == 3277
@@ -229,7 +229,7 @@ def test_signed_zero_minimum_stored_as_plus_zero():
 
 
 def test_L65536_round_trip_bounds():
-    """Reading R18: at 65536 levels the affine step can be coarser than the
+    """At 65536 levels (our reading of a round trip) the affine step can be coarser than the
     fp16 spacing near 0, so the round trip is a bound, not bit equality."""
     rng = np.random.default_rng(3)
     rows = _rows(rng, 300, "normal")
