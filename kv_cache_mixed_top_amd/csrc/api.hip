@@ -140,19 +140,25 @@ semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0
   a->nch[2] = (int32_t)((c->n_tail + chunk - 1) / chunk);
   a->nchunks = a->nch[0] + a->nch[1] + a->nch[2];
   a->x0 = 0;
-  if (decode_use_mfma(*a)) {
-    // pool chunks sized to fill the resident wave slots once; the fp16 tail
-    // (< block <= 1024 rows) stays one generic chunk of the same size
-    const int c2 = decode_mfma_chunk_rows(c->n_high, c->n_low, units);
-    const int cm = c2 > chunk ? c2 : chunk;
+  const int64_t per_chunk_bytes = decode_partial_floats_per_chunk(a->group) * 4;
+  auto set_chunk = [&](int cm) {
     a->chunk = cm;
     a->nch[0] = (int32_t)((c->n_high + cm - 1) / cm);
     a->nch[1] = (int32_t)((c->n_low + cm - 1) / cm);
     a->nch[2] = (int32_t)((c->n_tail + cm - 1) / cm);
     a->nchunks = a->nch[0] + a->nch[1] + a->nch[2];
+  };
+  if (decode_use_mfma(*a)) {
+    // pool chunks fill whole rounds of the resident workgroup slots (the fp16
+    // tail, < block <= 1024 rows, stays one generic chunk of the same size);
+    // if the caller's workspace cannot hold that many partials, chunks no
+    // finer than the generic ones, which semkv_workspace_bytes covers
+    const int c2 = decode_mfma_chunk_rows(c->n_high, c->n_low, units);
+    set_chunk(c2);
+    if (units * a->nchunks * per_chunk_bytes > ws_bytes && c2 < chunk) set_chunk(chunk);
   }
   a->ws = reinterpret_cast<float*>(ws);
-  const int64_t need = units * a->nchunks * decode_partial_floats_per_chunk(a->group) * 4;
+  const int64_t need = units * a->nchunks * per_chunk_bytes;
   if (!ws || !aligned(ws, 256) || ws_bytes < need) return SEMKV_EWORKSPACE;
   return SEMKV_OK;
 }

@@ -331,16 +331,23 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
 }
 
 int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units) {
+  // Chunks fill whole rounds of the resident workgroup slots; a chunk holds
+  // at most kMfmaChunkMax rows, which bounds the length of the matrix-core
+  // accumulations (longer contexts take more rounds instead).
+  constexpr int64_t kMfmaChunkMax = 4096;
   const int64_t slots = decode_mfma_resident_waves();
-  int64_t per_unit = slots / (units > 0 ? units : 1);
-  if (per_unit < 2) per_unit = 2;
-  // smallest tile multiple whose high-pool plus low-pool chunk count fits the
-  // resident slots of one unit
+  int64_t per_round = slots / (units > 0 ? units : 1);
+  if (per_round < 2) per_round = 2;
   auto count = [&](int64_t c) { return (n_high + c - 1) / c + (n_low + c - 1) / c; };
-  int64_t c = (n_high + n_low + per_unit - 1) / per_unit;
-  c = (c + kTile - 1) / kTile * kTile;
-  if (c < kTile) c = kTile;
-  while (count(c) > per_unit) c += kTile;
+  auto fit = [&](int64_t target) {
+    int64_t c = (n_high + n_low + target - 1) / target;
+    c = (c + kTile - 1) / kTile * kTile;
+    if (c < kTile) c = kTile;
+    while (count(c) > target) c += kTile;   // smallest tile multiple that fits
+    return c;
+  };
+  int64_t c = fit(per_round);
+  if (c > kMfmaChunkMax) c = fit(per_round * ((c + kMfmaChunkMax - 1) / kMfmaChunkMax));
   return (int)c;
 }
 

@@ -27,10 +27,14 @@
 //    once at the end, so the weights keep ~22 bits: with heavy-tailed V the
 //    min_V and scale_V * code terms nearly cancel and a single fp16 weight
 //    (11 bits) is not enough.  The B operand holds the linear features of
-//    each packed field f:
-//    f, floor(f/L), floor(f/L^2), again made normal fp16 (* 2^-10).  Digits are linear
-//    in these features (c0 = f - L*f1, c1 = f1 - L*f2, c2 = f2), so the
-//    exact digit sums are recovered from the fp32 accumulators at the end.
+//    each packed field f: f, floor(f/L), floor(f/L^2).  Digits are linear in
+//    them (c0 = f - L*f1, c1 = f1 - L*f2, c2 = f2), so the digit sums are
+//    recovered from the fp32 accumulators at the end.  The features enter
+//    centred on the middle of their range (and scaled by 2^-10, exact normal
+//    fp16): the weights are all positive, so uncentred sums would grow with
+//    the chunk length and the recovery c0 = F0 - L*F1 would amplify their
+//    rounding ~40x; centred sums stay small.  The centring adds m*sum(w) to
+//    every digit sum (m = (L-1)/2), read from a column that holds no field.
 //    sum_t p_t * min_V(t) is accumulated on the VALU.
 #include <utility>
 
@@ -94,6 +98,25 @@ __device__ __forceinline__ void features(uint32_t x, uint32_t& f1o, uint32_t& f2
 // Two 16-bit integers (< 2048) -> the normal fp16 values c * 2^-10, exactly.
 __device__ __forceinline__ uint32_t int_to_f16x2(uint32_t x) {
   const h2 v = __builtin_bit_cast(h2, x) * (h2){(_Float16)16384.0f, (_Float16)16384.0f};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Centre of PV feature k (0: f, 1: floor(f/L), 2: floor(f/L^2)) of a field of
+// three base-L digits: m * (L^(3-k) - 1) / (L - 1) with m = (L - 1) / 2, the
+// middle of its range.
+template <int L, int K>
+constexpr float feature_centre() {
+  return 0.5f * (float)((K == 0 ? L * L * L : K == 1 ? L * L : L) - 1);
+}
+
+// Two 16-bit feature values x -> (x - centre) * 2^-10 as fp16, exactly: one
+// packed FMA on the subnormal reading of x (x * 2^-24 * 2^14 - centre * 2^-10;
+// the result is a multiple of 2^-11 below 2^-3, so no rounding happens).
+template <int L, int K>
+__device__ __forceinline__ uint32_t centred_f16x2(uint32_t x) {
+  constexpr _Float16 c = (_Float16)(-feature_centre<L, K>() / 1024.0f);
+  const h2 v = __builtin_bit_cast(h2, x) * (h2){(_Float16)16384.0f, (_Float16)16384.0f} +
+               (h2){c, c};
   return __builtin_bit_cast(uint32_t, v);
 }
 
@@ -434,12 +457,12 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
         features<L>(p1, f11, f21);
         features<L>(p2, f12, f22);
         features<L>(p3, f13, f23);
-        const h8 B0 = as_h8(int_to_f16x2(p0), int_to_f16x2(p1), int_to_f16x2(p2),
-                            int_to_f16x2(p3));
-        const h8 B1 = as_h8(int_to_f16x2(f10), int_to_f16x2(f11), int_to_f16x2(f12),
-                            int_to_f16x2(f13));
-        const h8 B2 = as_h8(int_to_f16x2(f20), int_to_f16x2(f21), int_to_f16x2(f22),
-                            int_to_f16x2(f23));
+        const h8 B0 = as_h8(centred_f16x2<L, 0>(p0), centred_f16x2<L, 0>(p1),
+                            centred_f16x2<L, 0>(p2), centred_f16x2<L, 0>(p3));
+        const h8 B1 = as_h8(centred_f16x2<L, 1>(f10), centred_f16x2<L, 1>(f11),
+                            centred_f16x2<L, 1>(f12), centred_f16x2<L, 1>(f13));
+        const h8 B2 = as_h8(centred_f16x2<L, 2>(f20), centred_f16x2<L, 2>(f21),
+                            centred_f16x2<L, 2>(f22), centred_f16x2<L, 2>(f23));
         acc[set][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B0, acc[set][0], 0, 0, 0);
         acc[set][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B1, acc[set][1], 0, 0, 0);
         acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B2, acc[set][2], 0, 0, 0);
@@ -460,6 +483,13 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
     for (int k = 0; k < 3; ++k)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[set][k][r] += __shfl_xor(acc[set][k][r], 16, 64);
+  // Centred features: with centres a_k = m (L^(3-k) - 1) / (L - 1) every
+  // digit sum is (its combination of centred sums) + m * sum(w).  Column 15
+  // of set 2 (field 47) holds no field: its features are 0, centred -a_k, so
+  // its feature-2 sum is exactly -m * sum(w).
+  float corr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) corr[r] = __shfl(acc[2][2][r], 15, 64);
   float* wsu = a.ws + u * 4 * kPartialStride;
   const float back = ldexpf(1.0f, 10 - E);   // features enter as f * 2^-10
   if (lane < 16) {
@@ -472,11 +502,12 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
           const float F0 = acc[set][0][r] * back;
           const float F1 = acc[set][1][r] * back;
           const float F2 = acc[set][2][r] * back;
+          const float base = msum[r] - corr[r] * back;
           float* o = wsu + r * kPartialStride + 2;
           const int d = 3 * j;
-          o[d] = msum[r] + fmaf(-(float)L, F1, F0);
-          o[d + 1] = msum[r] + fmaf(-(float)L, F2, F1);
-          if (d + 2 < kHeadDim) o[d + 2] = msum[r] + F2;
+          o[d] = base + fmaf(-(float)L, F1, F0);
+          o[d + 1] = base + fmaf(-(float)L, F2, F1);
+          if (d + 2 < kHeadDim) o[d + 2] = base + F2;
         }
       }
     }

@@ -64,3 +64,23 @@ def to_dev(a, dtype=None):
     if dtype is not None:
         t = t.to(dtype)
     return t.cuda()
+
+
+def gpu_plane_rows(cache, sk, b, layer, head):
+    """Valid rows of one (sequence, layer, KV head) of both device pools:
+    {"codes_high": [2][n_high][R], "meta_high": [2][n_high][2], ...} with
+    index 0 = K, 1 = V (V un-transposed from its byte-planar tiles)."""
+    g = cache.geom
+    out = {}
+    for name, high, n in (("high", True, cache.n_high), ("low", False, cache.n_low)):
+        L = g.L_high if high else g.L_low
+        cap = g.cap_high if high else g.cap_low
+        R = sk.semkv_row_bytes(L)
+        codes = (cache.codes_high if high else cache.codes_low).view(
+            g.batch, g.layers, g.kv_heads, 2, cap * R)[b, layer, head].cpu().numpy()
+        k_rows = codes[0, :n * R].reshape(n, R)
+        v_rows = planar_rows(codes[1], R, n)
+        out["codes_" + name] = np.stack([k_rows, v_rows])
+        out["meta_" + name] = cache.meta_view(high)[b, layer, head, :, :n, :].cpu().numpy().view(
+            np.uint16)
+    return out
