@@ -66,64 +66,69 @@ __device__ __forceinline__ h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t
   return __builtin_bit_cast(h8, make_uint4(a, b, c, d));
 }
 
-// Per 16-bit slot: x < 216 (3 base-6 digits) or x < 128 (3 base-5 digits).
+// Field values enter as fp16 in [1024, 2048), where the spacing is 1: a
+// 16-bit slot 0x6600 | x is the value 1536 + x (x < 512).  One packed fp16
+// FMA then gives 1536 + floor(x / L) exactly: RNE((1536 + x) * m + k) with
+// the constants below, checked exhaustively for every field value (x < 216
+// for 6 levels, x < 125 for 5) and so also for floor(f1 / L).
+constexpr uint32_t kBias = 0x66666666u;   // perm source of the 0x66 high bytes
+constexpr float kBase = 1536.0f;
+template <int L> constexpr float floor_m() { return L == 6 ? 0.1663818359375f : 0.1995849609375f; }
+template <int L> constexpr float floor_k() { return L == 6 ? 1280.0f : 1229.0f; }
+
+template <int L>
+__device__ __forceinline__ h2 floor_div(h2 v) {   // 1536 + x -> 1536 + floor(x / L)
+  constexpr _Float16 m = (_Float16)floor_m<L>(), k = (_Float16)floor_k<L>();
+  return __builtin_elementwise_fma(v, (h2){m, m}, (h2){k, k});
+}
+
+// Two biased field values -> their three base-L digits as exact fp16 integers.
 template <int L>
 __device__ __forceinline__ void digits(uint32_t x, uint32_t& c0, uint32_t& c1, uint32_t& c2) {
-  const u16x2 v = v2(x);
-  u16x2 f1, f2;
-  if (L == 6) {
-    f1 = (v * (u16x2){171, 171}) >> (u16x2){10, 10};   // floor(v / 6), v < 216
-    f2 = (v * (u16x2){57, 57}) >> (u16x2){11, 11};     // floor(v / 36)
-  } else {
-    f1 = (v * (u16x2){205, 205}) >> (u16x2){10, 10};   // floor(v / 5), v < 128
-    f2 = (v * (u16x2){41, 41}) >> (u16x2){10, 10};     // floor(v / 25)
-  }
-  c2 = u32(f2);
-  c1 = u32(f1 - f2 * (u16x2){(unsigned short)L, (unsigned short)L});
-  c0 = u32(v - f1 * (u16x2){(unsigned short)L, (unsigned short)L});
+  constexpr _Float16 B = (_Float16)kBase, nL = (_Float16)(-L);
+  const h2 X = __builtin_bit_cast(h2, x);
+  const h2 F1 = floor_div<L>(X);
+  const h2 F2 = floor_div<L>(F1);
+  const h2 d2 = F2 - (h2){B, B};
+  const h2 f1 = F1 - (h2){B, B};
+  const h2 d1 = __builtin_elementwise_fma(d2, (h2){nL, nL}, f1);
+  const h2 d0 = __builtin_elementwise_fma(f1, (h2){nL, nL}, X - (h2){B, B});
+  c0 = __builtin_bit_cast(uint32_t, d0);
+  c1 = __builtin_bit_cast(uint32_t, d1);
+  c2 = __builtin_bit_cast(uint32_t, d2);
 }
 
+// Integer centres of the PV features f, floor(f/L), floor(f/L^2) near the
+// middle of their ranges.  The digit sums are then the centred combinations
+// plus coef_k * sum(w), coef = (a0 - L a1, a1 - L a2, a2).
+template <int L, int K>
+constexpr int feature_centre() {
+  return L == 6 ? (K == 0 ? 108 : K == 1 ? 18 : 3) : (K == 0 ? 62 : K == 1 ? 12 : 2);
+}
+template <int L, int K>
+constexpr float centre_coef() {
+  return K == 0 ? (float)(feature_centre<L, 0>() - L * feature_centre<L, 1>())
+       : K == 1 ? (float)(feature_centre<L, 1>() - L * feature_centre<L, 2>())
+                : (float)feature_centre<L, 2>();
+}
+
+// Two biased field values -> their centred features as exact fp16 integers.
 template <int L>
-__device__ __forceinline__ void features(uint32_t x, uint32_t& f1o, uint32_t& f2o) {
-  const u16x2 v = v2(x);
-  if (L == 6) {
-    f1o = u32((v * (u16x2){171, 171}) >> (u16x2){10, 10});
-    f2o = u32((v * (u16x2){57, 57}) >> (u16x2){11, 11});
-  } else {
-    f1o = u32((v * (u16x2){205, 205}) >> (u16x2){10, 10});
-    f2o = u32((v * (u16x2){41, 41}) >> (u16x2){10, 10});
-  }
-}
-
-// Two 16-bit integers (< 2048) -> the normal fp16 values c * 2^-10, exactly.
-__device__ __forceinline__ uint32_t int_to_f16x2(uint32_t x) {
-  const h2 v = __builtin_bit_cast(h2, x) * (h2){(_Float16)16384.0f, (_Float16)16384.0f};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-// Centre of PV feature k (0: f, 1: floor(f/L), 2: floor(f/L^2)) of a field of
-// three base-L digits: m * (L^(3-k) - 1) / (L - 1) with m = (L - 1) / 2, the
-// middle of its range.
-template <int L, int K>
-constexpr float feature_centre() {
-  return 0.5f * (float)((K == 0 ? L * L * L : K == 1 ? L * L : L) - 1);
-}
-
-// Two 16-bit feature values x -> (x - centre) * 2^-10 as fp16, exactly: one
-// packed FMA on the subnormal reading of x (x * 2^-24 * 2^14 - centre * 2^-10;
-// the result is a multiple of 2^-11 below 2^-3, so no rounding happens).
-template <int L, int K>
-__device__ __forceinline__ uint32_t centred_f16x2(uint32_t x) {
-  constexpr _Float16 c = (_Float16)(-feature_centre<L, K>() / 1024.0f);
-  const h2 v = __builtin_bit_cast(h2, x) * (h2){(_Float16)16384.0f, (_Float16)16384.0f} +
-               (h2){c, c};
-  return __builtin_bit_cast(uint32_t, v);
+__device__ __forceinline__ void features(uint32_t x, uint32_t& g0, uint32_t& g1, uint32_t& g2) {
+  constexpr _Float16 a0 = (_Float16)(kBase + feature_centre<L, 0>());
+  constexpr _Float16 a1 = (_Float16)(kBase + feature_centre<L, 1>());
+  constexpr _Float16 a2 = (_Float16)(kBase + feature_centre<L, 2>());
+  const h2 X = __builtin_bit_cast(h2, x);
+  const h2 F1 = floor_div<L>(X);
+  const h2 F2 = floor_div<L>(F1);
+  g0 = __builtin_bit_cast(uint32_t, X - (h2){a0, a0});
+  g1 = __builtin_bit_cast(uint32_t, F1 - (h2){a1, a1});
+  g2 = __builtin_bit_cast(uint32_t, F2 - (h2){a2, a2});
 }
 
 template <int S>
 __device__ __forceinline__ f4 qk_mfma(const h4 (&qf)[3], uint32_t lo, uint32_t hi, f4 acc) {
-  return __builtin_amdgcn_mfma_f32_4x4x4f16(qf[S / 16], as_h4(int_to_f16x2(lo), int_to_f16x2(hi)),
-                                            acc, 4, S % 16, 0);
+  return __builtin_amdgcn_mfma_f32_4x4x4f16(qf[S / 16], as_h4(lo, hi), acc, 4, S % 16, 0);
 }
 
 // ---- 6 levels: one K row = 43 bytes = 11 dwords (the 44th byte masked)
@@ -131,8 +136,8 @@ template <int W>
 __device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const h4 (&qf)[3],
                                           f4 (&acc)[3]) {
   const uint32_t X = d[W];
-  const uint32_t xe = X & 0x00FF00FFu;            // bytes 4W, 4W+2 -> 16-bit slots
-  const uint32_t xo = perm(0u, X, 0x0C030C01u);   // bytes 4W+1, 4W+3
+  const uint32_t xe = perm(kBias, X, 0x04020400u);   // bytes 4W, 4W+2 -> biased slots
+  const uint32_t xo = perm(kBias, X, 0x04030401u);   // bytes 4W+1, 4W+3
   uint32_t e0, e1, e2, o0, o1, o2;
   digits<6>(xe, e0, e1, e2);
   digits<6>(xo, o0, o1, o2);
@@ -149,9 +154,9 @@ __device__ __forceinline__ void qk6(const uint32_t (&d)[12], const h4 (&qf)[3], 
 // ---- 5 levels: one K row = 38 bytes; 7-byte units hold 8 fields of 7 bits.
 // From a word W with fields at bits 0, 7, 14, 21: slots (F0, F2) and (F1, F3).
 __device__ __forceinline__ void field_pairs(uint32_t W, uint32_t& pa, uint32_t& pb) {
-  pa = (W & 0x7Fu) | ((W << 2) & 0x7F0000u);
+  pa = (W & 0x7Fu) | (((W << 2) & 0x7F0000u) | 0x66006600u);
   const uint32_t Wp = W >> 7;
-  pb = (Wp & 0x7Fu) | ((Wp << 2) & 0x7F0000u);
+  pb = (Wp & 0x7Fu) | (((Wp << 2) & 0x7F0000u) | 0x66006600u);
 }
 template <int Q>   // Q = 2u + quad
 __device__ __forceinline__ void qk5_quad(uint32_t W, const h4 (&qf)[3], f4 (&acc)[3]) {
@@ -382,7 +387,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
         qk5(d, qf, sacc, std::make_integer_sequence<int, 6>{});
       }
     }
-    const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu)) * 1024.0f;   // digits enter as c * 2^-10
+    const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
     const float kbias = sm * h2f((uint16_t)(km >> 16));
     float z[4];
 #pragma unroll
@@ -437,32 +442,28 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
         uint32_t p0, p1, p2, p3;
         if (L == 6) {
           const uint2 w8 = vr[G][set][0];
-          p0 = perm(0u, w8.x, 0x0C010C00u);
-          p1 = perm(0u, w8.x, 0x0C030C02u);
-          p2 = perm(0u, w8.y, 0x0C010C00u);
-          p3 = perm(0u, w8.y, 0x0C030C02u);
+          p0 = perm(kBias, w8.x, 0x04010400u);
+          p1 = perm(kBias, w8.x, 0x04030402u);
+          p2 = perm(kBias, w8.y, 0x04010400u);
+          p3 = perm(kBias, w8.y, 0x04030402u);
         } else {
           const int bit = 7 * j;
           const uint2 b0 = vr[G][set][0];
           const uint2 b1 = vr[G][set][L == 6 ? 0 : 1];
           const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
-          const u16x2 m7 = {0x7F, 0x7F};
-          p0 = u32((v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & m7);
-          p1 = u32((v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & m7);
-          p2 = u32((v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & m7);
-          p3 = u32((v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & m7);
+          p0 = (u32(v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
+          p1 = (u32(v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
+          p2 = (u32(v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
+          p3 = (u32(v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
         }
-        uint32_t f10, f20, f11, f21, f12, f22, f13, f23;
-        features<L>(p0, f10, f20);
-        features<L>(p1, f11, f21);
-        features<L>(p2, f12, f22);
-        features<L>(p3, f13, f23);
-        const h8 B0 = as_h8(centred_f16x2<L, 0>(p0), centred_f16x2<L, 0>(p1),
-                            centred_f16x2<L, 0>(p2), centred_f16x2<L, 0>(p3));
-        const h8 B1 = as_h8(centred_f16x2<L, 1>(f10), centred_f16x2<L, 1>(f11),
-                            centred_f16x2<L, 1>(f12), centred_f16x2<L, 1>(f13));
-        const h8 B2 = as_h8(centred_f16x2<L, 2>(f20), centred_f16x2<L, 2>(f21),
-                            centred_f16x2<L, 2>(f22), centred_f16x2<L, 2>(f23));
+        uint32_t g0[4], g1[4], g2[4];
+        features<L>(p0, g0[0], g1[0], g2[0]);
+        features<L>(p1, g0[1], g1[1], g2[1]);
+        features<L>(p2, g0[2], g1[2], g2[2]);
+        features<L>(p3, g0[3], g1[3], g2[3]);
+        const h8 B0 = as_h8(g0[0], g0[1], g0[2], g0[3]);
+        const h8 B1 = as_h8(g1[0], g1[1], g1[2], g1[3]);
+        const h8 B2 = as_h8(g2[0], g2[1], g2[2], g2[3]);
         acc[set][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B0, acc[set][0], 0, 0, 0);
         acc[set][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B1, acc[set][1], 0, 0, 0);
         acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B2, acc[set][2], 0, 0, 0);
@@ -483,15 +484,15 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
     for (int k = 0; k < 3; ++k)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[set][k][r] += __shfl_xor(acc[set][k][r], 16, 64);
-  // Centred features: with centres a_k = m (L^(3-k) - 1) / (L - 1) every
-  // digit sum is (its combination of centred sums) + m * sum(w).  Column 15
-  // of set 2 (field 47) holds no field: its features are 0, centred -a_k, so
-  // its feature-2 sum is exactly -m * sum(w).
-  float corr[4];
+  // Centred features: every digit sum is its centred combination plus
+  // coef_k * sum(w).  Column 15 of set 2 (field 47) holds no field: its
+  // features are 0, centred -a_k, so its feature-2 sum is -a2 * sum(w).
+  float wsum[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) corr[r] = __shfl(acc[2][2][r], 15, 64);
+  for (int r = 0; r < 4; ++r)
+    wsum[r] = __shfl(acc[2][2][r], 15, 64) * (-1.0f / (float)feature_centre<L, 2>());
   float* wsu = a.ws + u * 4 * kPartialStride;
-  const float back = ldexpf(1.0f, 10 - E);   // features enter as f * 2^-10
+  const float back = ldexpf(1.0f, -E);       // undo the chunk exponent of w
   if (lane < 16) {
 #pragma unroll
     for (int set = 0; set < 3; ++set) {
@@ -502,12 +503,12 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
           const float F0 = acc[set][0][r] * back;
           const float F1 = acc[set][1][r] * back;
           const float F2 = acc[set][2][r] * back;
-          const float base = msum[r] - corr[r] * back;
+          const float W = wsum[r] * back;
           float* o = wsu + r * kPartialStride + 2;
           const int d = 3 * j;
-          o[d] = base + fmaf(-(float)L, F1, F0);
-          o[d + 1] = base + fmaf(-(float)L, F2, F1);
-          if (d + 2 < kHeadDim) o[d + 2] = base + F2;
+          o[d] = msum[r] + fmaf(centre_coef<L, 0>(), W, fmaf(-(float)L, F1, F0));
+          o[d + 1] = msum[r] + fmaf(centre_coef<L, 1>(), W, fmaf(-(float)L, F2, F1));
+          if (d + 2 < kHeadDim) o[d + 2] = msum[r] + fmaf(centre_coef<L, 2>(), W, F2);
         }
       }
     }

@@ -204,12 +204,190 @@ __device__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
   }
 }
 
+// ---- fast path for the 6- and 5-level pools when the tile's first slot is
+// a multiple of 16 (every tile of a prompt): the tile's packed bytes form one
+// contiguous, 16-byte aligned range of the plane in both layouts, which is
+// assembled in LDS and stored with 16-byte writes.
+constexpr int kCode8Stride = 136;                 // u8 codes per LDS row: 128 + 8 zero pad
+constexpr int kCode8Bytes = kRows * kCode8Stride + 16;
+constexpr int kImgBytes = kRows * 43;             // largest packed tile (6 levels)
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+template <int L>
+__device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_pool,
+                                   uint8_t* codes8, uint8_t* img) {
+  constexpr int R = L == 6 ? 43 : 38;
+  const int count = pool == 0 ? a.k_high : a.n - a.k_high;
+  const int perm_off = pool == 0 ? 0 : a.k_high;
+  const int y = blockIdx.y;
+  const int kvsel = y & 1;
+  const int head = (y >> 1) % a.kv_heads;
+  const int layer = (y >> 1) / a.kv_heads;
+  const int b = blockIdx.z;
+  const int row0 = tile_in_pool * kRows;
+  const int nrows = min(kRows, count - row0);
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, q = tid & 3;
+  const bool valid = r < nrows;
+  const int64_t plane = (((int64_t)b * a.layers + layer) * a.kv_heads + head) * 2 + kvsel;
+  const int64_t slot0 = a.start[pool] + row0;
+
+  // ---- 32 values of this row as 16 fp16 pairs (dims 8q + 32i + 2e + {0,1})
+  int token = 0;
+  half2_t v[16];
+  if (valid) {
+    token = a.perm[(int64_t)b * a.n + perm_off + row0 + r];
+    const uint16_t* src = a.src[kvsel] + (int64_t)b * a.sb + (int64_t)layer * a.sl +
+                          (int64_t)head * a.sh + (int64_t)token * a.st;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * q + 32 * i);
+      v[4 * i + 0] = __builtin_bit_cast(half2_t, w.x);
+      v[4 * i + 1] = __builtin_bit_cast(half2_t, w.y);
+      v[4 * i + 2] = __builtin_bit_cast(half2_t, w.z);
+      v[4 * i + 3] = __builtin_bit_cast(half2_t, w.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (half2_t){0, 0};
+  }
+
+  // ---- row min / max: packed fp16 (exact), then the quad
+  half2_t mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    mn = __builtin_elementwise_min(mn, v[i]);
+    mx = __builtin_elementwise_max(mx, v[i]);
+  }
+  float lo = fminf((float)mn[0], (float)mn[1]);
+  float hi = fmaxf((float)mx[0], (float)mx[1]);
+  lo = fminf(lo, __shfl_xor(lo, 1, 64));
+  lo = fminf(lo, __shfl_xor(lo, 2, 64));
+  hi = fmaxf(hi, __shfl_xor(hi, 1, 64));
+  hi = fmaxf(hi, __shfl_xor(hi, 2, 64));
+  lo = lo + 0.0f;   // a zero minimum is stored as +0
+
+  const uint16_t sbits = scale_ceil_bits(lo, hi, L);
+  const float s = h2f(sbits);
+
+  // ---- codes: y = x * (1/s) - m * (1/s) in one fma from the fp16 value.
+  // |y - (x - m)/s| <= 2^-23 ((L-1) + |m|/s) (1 + 2^-20); a code whose y lies
+  // within that of a half-integer is settled exactly.  v_cvt_pk_u8_f32 rounds
+  // to nearest even and clamps to [0, 255], which is the code elsewhere.
+  uint32_t cw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (s > 0.0f) {
+    const float rs = 1.0f / s;
+    const float nb = -lo * rs;
+    const float eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
+    float dmin = 1.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const float yv = fmaf((float)v[k >> 1][k & 1], rs, nb);
+      dmin = fminf(dmin, fabsf(__builtin_amdgcn_fractf(yv) - 0.5f));
+      cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(yv, k & 3, cw[k >> 2]);
+    }
+    if (dmin <= eps) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const float x = (float)v[k >> 1][k & 1];
+        const float yv = fmaf(x, rs, nb);
+        if (fabsf(__builtin_amdgcn_fractf(yv) - 0.5f) <= eps) {
+          const float c = exact_code(x, lo, s, rintf(yv));
+          const int sh = 8 * (k & 3);
+          cw[k >> 2] = (cw[k >> 2] & ~(0xFFu << sh)) | ((uint32_t)(int)c << sh);
+        }
+      }
+    }
+  }
+  // dims 8q + 32i .. +8 -> row r of the LDS code array; lane 0 of the quad
+  // clears the 8 pad bytes (fields read up to code 131)
+  uint8_t* crow = codes8 + r * kCode8Stride;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint2*>(crow + 8 * q + 32 * i) = make_uint2(cw[2 * i], cw[2 * i + 1]);
+  if (q == 0) *reinterpret_cast<uint2*>(crow + 128) = make_uint2(0u, 0u);
+  if (tid < 4) reinterpret_cast<uint32_t*>(codes8 + kRows * kCode8Stride)[tid] = 0u;
+
+  if (valid && q == 0) {
+    const int64_t slot = slot0 + r;
+    a.meta[pool][plane * a.cap[pool] + slot] = (uint32_t)sbits | ((uint32_t)f2h(lo) << 16);
+    if (layer == 0 && head == 0 && kvsel == 0)
+      a.tok[pool][(int64_t)b * a.cap[pool] + slot] = (int32_t)(a.token_base + token);
+  }
+  __syncthreads();
+
+  // ---- fields (sum_i code[3j+i] L^i, one udot4 each) -> the tile's byte
+  // image: K rows back to back, V byte-planar in 16-row tiles
+  auto put = [&](int row, int j, uint32_t byte) {
+    const int at = kvsel == 0 ? row * R + j : (row >> 4) * 16 * R + 16 * j + (row & 15);
+    img[at] = (uint8_t)byte;
+  };
+  if (L == 6) {
+    constexpr uint32_t W = 0x00240601u;              // bytes {1, 6, 36, 0}
+    for (int item = tid; item < kRows * 11; item += kThreads) {
+      const int row = item / 11, u = item - 11 * row;  // fields 4u .. 4u+3
+      const uint32_t* c = reinterpret_cast<const uint32_t*>(codes8 + row * kCode8Stride + 12 * u);
+      const uint32_t c0 = c[0], c1 = c[1], c2 = c[2];
+      put(row, 4 * u, __builtin_amdgcn_udot4(c0, W, 0u, false));
+      put(row, 4 * u + 1, __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c1, c0, 3), W, 0u, false));
+      put(row, 4 * u + 2, __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c2, c1, 2), W, 0u, false));
+      if (u < 10) put(row, 4 * u + 3, __builtin_amdgcn_udot4(c2 >> 8, W, 0u, false));
+    }
+  } else {
+    constexpr uint32_t W = 0x00190501u;              // bytes {1, 5, 25, 0}
+    for (int item = tid; item < kRows * 6; item += kThreads) {
+      const int row = item / 6, u = item - 6 * row;  // fields 8u .. 8u+7 = bytes 7u .. 7u+6
+      const uint32_t* c = reinterpret_cast<const uint32_t*>(codes8 + row * kCode8Stride + 24 * u);
+      const uint32_t a0 = c[0], a1 = c[1], a2 = c[2], a3 = c[3], a4 = c[4], a5 = c[5];
+      uint32_t f[8];
+      f[0] = __builtin_amdgcn_udot4(a0, W, 0u, false);
+      f[1] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a1, a0, 3), W, 0u, false);
+      f[2] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a2, a1, 2), W, 0u, false);
+      f[3] = __builtin_amdgcn_udot4(a2 >> 8, W, 0u, false);
+      f[4] = __builtin_amdgcn_udot4(a3, W, 0u, false);
+      f[5] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a4, a3, 3), W, 0u, false);
+      f[6] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a5, a4, 2), W, 0u, false);
+      f[7] = __builtin_amdgcn_udot4(a5 >> 8, W, 0u, false);
+      if (u == 5) f[3] = f[4] = f[5] = f[6] = f[7] = 0u;   // fields 43.. do not exist
+      const uint32_t lo32 = f[0] | (f[1] << 7) | (f[2] << 14) | (f[3] << 21) | (f[4] << 28);
+      const uint32_t hi24 = (f[4] >> 4) | (f[5] << 3) | (f[6] << 10) | (f[7] << 17);
+      const int nb = u == 5 ? 3 : 7;
+#pragma unroll
+      for (int e = 0; e < 7; ++e)
+        if (e < nb) put(row, 7 * u + e, e < 4 ? lo32 >> (8 * e) : hi24 >> (8 * (e - 4)));
+    }
+  }
+  __syncthreads();
+
+  // ---- store the image: slots [slot0, slot0 + nrows) start at byte slot0 * R
+  // in both layouts; whole 16-byte pieces (rows past nrows carry zero codes,
+  // stay inside the plane and belong to no valid row yet)
+  const int bytes = kvsel == 0 ? (nrows * R + 15) & ~15 : ((nrows + 15) >> 4) * 16 * R;
+  uint4* dst = reinterpret_cast<uint4*>(a.codes[pool] + plane * a.cap[pool] * R + slot0 * R);
+  for (int i = tid; i < (bytes >> 4); i += kThreads) dst[i] = reinterpret_cast<const uint4*>(img)[i];
+}
+
 template <int LH, int LL>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, int tiles_high) {
-  __shared__ uint16_t codes[kRows * kCodeStride];
+  constexpr int kGeneric = kRows * kCodeStride * 2;
+  constexpr int kFast = kCode8Bytes + kImgBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kGeneric > kFast ? kGeneric : kFast];
   const int tile = blockIdx.x;
-  if (tile < tiles_high) quantize_tile<LH>(a, 0, tile, codes);
-  else quantize_tile<LL>(a, 1, tile - tiles_high, codes);
+  const int pool = tile < tiles_high ? 0 : 1;
+  const int t = pool == 0 ? tile : tile - tiles_high;
+  const bool aligned16 = (a.start[pool] & 15) == 0;
+  if (pool == 0) {
+    if (LH != 0 && aligned16)
+      quantize_tile_fast<LH == 0 ? 6 : LH>(a, 0, t, smem, smem + kCode8Bytes);
+    else
+      quantize_tile<LH>(a, 0, t, reinterpret_cast<uint16_t*>(smem));
+  } else {
+    if (LL != 0 && aligned16)
+      quantize_tile_fast<LL == 0 ? 5 : LL>(a, 1, t, smem, smem + kCode8Bytes);
+    else
+      quantize_tile<LL>(a, 1, t, reinterpret_cast<uint16_t*>(smem));
+  }
 }
 
 }  // namespace
