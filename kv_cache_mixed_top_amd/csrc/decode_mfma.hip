@@ -53,6 +53,7 @@ constexpr int kTile = 64;
 constexpr int kBuf = 3072;          // 3 x 1 KB load blocks (>= 64 * 43 + 48 read slack)
 constexpr int kPartialStride = 2 + kHeadDim;
 constexpr int kQkInstr = 33;        // 4x4x4 MFMAs per row (132 digit slots)
+constexpr float kFrameMargin = 8.0f; // softmax frame above the running max (natural log)
 
 __device__ __forceinline__ uint32_t u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ u16x2 v2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
@@ -323,9 +324,16 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
   // previous one.  Only the loop head waits for outstanding loads; inside a
   // tile, LDS hand-offs between lanes of the (single) wave only wait for the
   // LDS queue (a workgroup barrier would also wait for the prefetch).
+  // The weights are taken against a per-head frame mref kept kFrameMargin
+  // above the running maximum logit.  A tile with a logit above the frame
+  // (in practice only the first tile) raises the frame, rescales what was
+  // accumulated and runs again from the loop head: the matrix-core
+  // accumulation is reached only when no rescale is pending.
   int buf = 0;
+  uint32_t km = 0, vm = 0;   // meta words of the tile at t0
+  bool fresh = true;         // the tile at t0 has not been started yet
   if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
-  for (int64_t t0 = r0; t0 < r1; t0 += kTile, buf ^= 1) {
+  for (int64_t t0 = r0; t0 < r1;) {
     const int nt = (int)min((int64_t)kTile, r1 - t0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile's loads have landed
     __syncthreads();                                     // every lane is past tile - 1
@@ -358,8 +366,10 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
         }
       }
     }
-    const uint32_t km = km_next;
-    const uint32_t vm = vm_next;
+    if (fresh) {
+      km = km_next;
+      vm = vm_next;
+    }
 
     // ---- QK^T: lane = token
     f4 sacc[3];
@@ -396,13 +406,13 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
       z[h] = lane < nt ? fmaf(kfac, s, kbias * sumq[h]) : -INFINITY;
     }
 
-    // ---- running maximum (all weights <= 1)
+    // ---- frame check (all weights <= 1)
     const bool up = z[0] > mref[0] || z[1] > mref[1] || z[2] > mref[2] || z[3] > mref[3];
     if (__ballot(up) != 0ull) {
       float fac[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const float nm = fmaxf(mref[h], wave_max(z[h]));
+        const float nm = fmaxf(mref[h], wave_max(z[h]) + kFrameMargin);
         fac[h] = __expf(mref[h] - nm);              // exp(-inf) = 0 on the first tile
         mref[h] = nm;
         lsum[h] *= fac[h];
@@ -414,6 +424,8 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
         for (int k = 0; k < 3; ++k)
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[s][k][r] *= fac[r];
+      fresh = false;
+      continue;                                     // run this tile again in the new frame
     }
     const float vs = h2f((uint16_t)(vm & 0xFFFFu)) * two_e;
     const float vmin = h2f((uint16_t)(vm >> 16));
@@ -469,6 +481,9 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
         acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B2, acc[set][2], 0, 0, 0);
       }
     }
+    t0 += kTile;
+    buf ^= 1;
+    fresh = true;
   }
 
   // ---- epilogue: per-head sums, digits from features, partial record
