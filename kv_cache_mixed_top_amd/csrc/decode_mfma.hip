@@ -234,6 +234,61 @@ struct Stage {
   _Float16 w[2 * 4 * kTile];   // hi, lo
 };
 
+// Partial record of a chunk: per-head sums, digit sums from the feature
+// sums, (m, l, o[128]) per query head.
+template <int L>
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t u, int lane, int E,
+                                              f4 (&acc)[3][3], const float (&mref)[4],
+                                              float (&lsum)[4], float (&msum)[4]) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    lsum[h] = wave_sum(lsum[h]);
+    msum[h] = wave_sum(msum[h]);
+  }
+  // C rows 4-7 (lanes 16-31) hold the w_lo products of the heads in rows 0-3
+#pragma unroll
+  for (int set = 0; set < 3; ++set)
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[set][k][r] += __shfl_xor(acc[set][k][r], 16, 64);
+  // Centred features: every digit sum is its centred combination plus
+  // coef_k * sum(w).  Column 15 of set 2 (field 47) holds no field: its
+  // features are 0, centred -a_k, so its feature-2 sum is -a2 * sum(w).
+  float wsum[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    wsum[r] = __shfl(acc[2][2][r], 15, 64) * (-1.0f / (float)feature_centre<L, 2>());
+  float* wsu = a.ws + u * 4 * kPartialStride;
+  const float back = ldexpf(1.0f, -E);       // undo the chunk exponent of w
+  if (lane < 16) {
+#pragma unroll
+    for (int set = 0; set < 3; ++set) {
+      const int j = 16 * set + lane;
+      if (j < 43) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float F0 = acc[set][0][r] * back;
+          const float F1 = acc[set][1][r] * back;
+          const float F2 = acc[set][2][r] * back;
+          const float W = wsum[r] * back;
+          float* o = wsu + r * kPartialStride + 2;
+          const int d = 3 * j;
+          o[d] = msum[r] + fmaf(centre_coef<L, 0>(), W, fmaf(-(float)L, F1, F0));
+          o[d + 1] = msum[r] + fmaf(centre_coef<L, 1>(), W, fmaf(-(float)L, F2, F1));
+          if (d + 2 < kHeadDim) o[d + 2] = msum[r] + fmaf(centre_coef<L, 2>(), W, F2);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    if (lane == h) {
+      wsu[h * kPartialStride + 0] = mref[h];
+      wsu[h * kPartialStride + 1] = lsum[h];
+    }
+}
+
 template <int L>
 __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r1,
                                              int b, int li, int g, int64_t u, Stage& st) {
@@ -486,59 +541,297 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
     fresh = true;
   }
 
-  // ---- epilogue: per-head sums, digits from features, partial record
+  write_partial<L>(a, u, lane, E, acc, mref, lsum, msum);
+}
+
+// ---- two-wave form: one workgroup of two waves per chunk.  Wave 0 streams
+// the K rows and computes the logits; wave 1 streams the V tiles, keeps the
+// softmax and the PV accumulators and writes the partial record.  The
+// logits of a tile pass through LDS (double-buffered) with one workgroup
+// barrier per tile, so wave 0 computes tile t+1 while wave 1 finishes tile
+// t, and each wave holds only its own half of the state.
+// The buffers are separate LDS arrays (pointers into them are selected by
+// tile parity), so that an LDS access can be told apart from an in-flight
+// global->LDS load into another buffer; otherwise the compiler waits for the
+// loads before it.
+struct Stage2 {
+  uint8_t *k0, *k1;            // wave 0 staging, kBuf bytes each
+  uint8_t *v0, *v1;            // wave 1 staging
+  float *z0, *z1;              // logits of the last two tiles, [4][kTile] + maxima [4]
+  _Float16* w;                 // wave 1: weights hi, lo, [2 * 4 * kTile]
+  __device__ uint8_t* k(int b) const { return b ? k1 : k0; }
+  __device__ uint8_t* v(int b) const { return b ? v1 : v0; }
+  __device__ float* z(int b) const { return b ? z1 : z0; }
+};
+
+// One workgroup barrier with no memory fence: the LDS writes before it are
+// waited for by the caller; outstanding global->LDS prefetches stay in flight.
+__device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int L>
+__device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0, int64_t r1, int b, int li,
+                        int g, Stage2& st) {
+  constexpr int R = (L == 6) ? 43 : 38;
+  const int lane = threadIdx.x & 63;
+  const int layer = a.layer0 + li;
+  const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
+  const int64_t cap = a.cap[seg];
+  const uint8_t* kcodes = a.codes[seg] + plane_k * cap * R;
+  const uint32_t* kmg = a.meta[seg] + plane_k * cap;
+  const float sm = a.sm_scale;
+
+  // queries: ABID-packed 4x4x4 A fragments and per-head sums
+  const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
+                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
+  h4 qf[3];
+  {
+    const int head = lane & 3, blk = lane >> 2;
+#pragma unroll
+    for (int P = 0; P < 3; ++P) {
+      const int s = 16 * P + blk;
+      h4 v = {0, 0, 0, 0};
+      if (s < kQkInstr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = qk_slot_dim<L>(s, i);
+          v[i] = d >= 0 ? qg[head * kHeadDim + d] : (_Float16)0.0f;
+        }
+      }
+      qf[P] = v;
+    }
+  }
+  float sumq[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
+
+  // K rows [t0, t0 + nt) -> buffer `buf` (16 bytes per lane per instruction;
+  // chunks past the valid range re-read the last valid chunk); the lane's K
+  // meta word -> register
+  uint32_t km_next = 0;
+  auto issue = [&](int buf, int64_t t0, int nt) {
+    const int nk = (nt * R + 15) >> 4;
+    const uint8_t* ks = kcodes + t0 * R;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      if (64 * i < nk)
+        __builtin_amdgcn_global_load_lds(ks + 16 * min(64 * i + lane, nk - 1),
+                                         (lds_void*)(st.k(buf) + 1024 * i), 16, 0, 0);
+    km_next = kmg[t0 + min(lane, nt - 1)];
+  };
+
+  int buf = 0;
+  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
+  for (int64_t t0 = r0; t0 < r1; t0 += kTile, buf ^= 1) {
+    const int nt = (int)min((int64_t)kTile, r1 - t0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile's rows have landed
+    const uint32_t km = km_next;
+    f4 sacc[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) sacc[k] = (f4){0.f, 0.f, 0.f, 0.f};
+    {
+      const int off = lane * R;
+      const uint32_t* kb32 = reinterpret_cast<const uint32_t*>(st.k(buf) + (off & ~3));
+      const int sh = off & 3;
+      uint32_t raw[12];
+#pragma unroll
+      for (int i = 0; i < 12; ++i) raw[i] = kb32[i];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // staging reads done
+      if (t0 + kTile < r1) issue(buf ^ 1, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
+      uint32_t d[12];
+#pragma unroll
+      for (int i = 0; i < 11; ++i) d[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
+      d[11] = 0;
+      if (L == 6) {
+        d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
+        qk6(d, qf, sacc, std::make_integer_sequence<int, 11>{});
+      } else {
+        d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
+        d[10] = 0;
+        qk5(d, qf, sacc, std::make_integer_sequence<int, 6>{});
+      }
+    }
+    const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
+    const float kbias = sm * h2f((uint16_t)(km >> 16));
+    float zm[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float sq = sacc[0][h] + sacc[1][h] + sacc[2][h];
+      const float z = lane < nt ? fmaf(kfac, sq, kbias * sumq[h]) : -INFINITY;
+      st.z(buf)[h * kTile + lane] = z;
+      zm[h] = wave_max(z);
+    }
+    if (lane == 0)
+      *reinterpret_cast<float4*>(st.z(buf) + 4 * kTile) = make_float4(zm[0], zm[1], zm[2], zm[3]);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // logits written
+    tile_barrier();
+  }
+}
+
+template <int L>
+__device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0, int64_t r1, int b, int li,
+                        int g, int64_t u, Stage2& st) {
+  constexpr int R = (L == 6) ? 43 : 38;
+  const int lane = threadIdx.x & 63;
+  _Float16* wbuf = st.w;
+  const int layer = a.layer0 + li;
+  const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
+  const int64_t cap = a.cap[seg];
+  const uint8_t* vcodes = a.codes[seg] + (plane_k + 1) * cap * R;
+  const uint32_t* vmg = a.meta[seg] + (plane_k + 1) * cap;
+
+  // per-chunk exponent E: w = p * scale_V * 2^E stays below 2^14
+  uint32_t smax = 0;
+  for (int64_t r = r0 + lane; r < r1; r += 64) smax = max(smax, vmg[r] & 0xFFFFu);
+  smax = wave_max_u32(smax);
+  int E = 0;
+  if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
+  const float two_e = ldexpf(1.0f, E);
+
+  float mref[4], lsum[4], msum[4];
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    lsum[h] = wave_sum(lsum[h]);
-    msum[h] = wave_sum(msum[h]);
+    mref[h] = -INFINITY;
+    lsum[h] = 0.f;
+    msum[h] = 0.f;
   }
-  // C rows 4-7 (lanes 16-31) hold the w_lo products of the heads in rows 0-3
+  f4 acc[3][3];
 #pragma unroll
-  for (int set = 0; set < 3; ++set)
+  for (int s = 0; s < 3; ++s)
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
+    for (int k = 0; k < 3; ++k) acc[s][k] = (f4){0.f, 0.f, 0.f, 0.f};
+
+  // V tiles [t0, t0 + nt) -> buffer `buf` (whole 16-row byte-planar tiles);
+  // the lane's V meta word -> register
+  uint32_t vm_next = 0;
+  auto issue = [&](int buf, int64_t t0, int nt) {
+    const int nv = ((nt + 15) >> 4) * R;
+    const uint8_t* vs = vcodes + t0 * R;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[set][k][r] += __shfl_xor(acc[set][k][r], 16, 64);
-  // Centred features: every digit sum is its centred combination plus
-  // coef_k * sum(w).  Column 15 of set 2 (field 47) holds no field: its
-  // features are 0, centred -a_k, so its feature-2 sum is -a2 * sum(w).
-  float wsum[4];
+    for (int i = 0; i < 3; ++i)
+      if (64 * i < nv)
+        __builtin_amdgcn_global_load_lds(vs + 16 * min(64 * i + lane, nv - 1),
+                                         (lds_void*)(st.v(buf) + 1024 * i), 16, 0, 0);
+    vm_next = vmg[t0 + min(lane, nt - 1)];
+  };
+
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  int buf = 0;
+  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
+  for (int64_t t0 = r0; t0 < r1; t0 += kTile, buf ^= 1) {
+    const int nt = (int)min((int64_t)kTile, r1 - t0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile's V has landed
+    const uint32_t vm = vm_next;
+    // this lane's V code bytes (8 tokens x one byte per group and set; two
+    // bytes for 5 levels), read before the next tile's loads are issued
+    uint2 vr[2][3][L == 6 ? 1 : 2];
+    const uint8_t* vbuf = st.v(buf);
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    wsum[r] = __shfl(acc[2][2][r], 15, 64) * (-1.0f / (float)feature_centre<L, 2>());
-  float* wsu = a.ws + u * 4 * kPartialStride;
-  const float back = ldexpf(1.0f, -E);       // undo the chunk exponent of w
-  if (lane < 16) {
+    for (int G = 0; G < 2; ++G) {
+      const int tok0 = 32 * G + 8 * quad;
+      const uint8_t* vt = vbuf + (tok0 >> 4) * (16 * R) + (tok0 & 15);
 #pragma unroll
-    for (int set = 0; set < 3; ++set) {
-      const int j = 16 * set + lane;
-      if (j < 43) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float F0 = acc[set][0][r] * back;
-          const float F1 = acc[set][1][r] * back;
-          const float F2 = acc[set][2][r] * back;
-          const float W = wsum[r] * back;
-          float* o = wsu + r * kPartialStride + 2;
-          const int d = 3 * j;
-          o[d] = msum[r] + fmaf(centre_coef<L, 0>(), W, fmaf(-(float)L, F1, F0));
-          o[d + 1] = msum[r] + fmaf(centre_coef<L, 1>(), W, fmaf(-(float)L, F2, F1));
-          if (d + 2 < kHeadDim) o[d + 2] = msum[r] + fmaf(centre_coef<L, 2>(), W, F2);
+      for (int set = 0; set < 3; ++set) {
+        const int j = 16 * set + col;
+        if (L == 6) {
+          vr[G][set][0] = (32 * G < nt && j < R) ? *reinterpret_cast<const uint2*>(vt + j * 16)
+                                                : make_uint2(0u, 0u);
+        } else {
+          const int j0 = (7 * j) >> 3;
+          const bool ok = 32 * G < nt && j < 43;
+          vr[G][set][0] = ok ? *reinterpret_cast<const uint2*>(vt + j0 * 16) : make_uint2(0u, 0u);
+          vr[G][set][L == 6 ? 0 : 1] =
+              ok ? *reinterpret_cast<const uint2*>(vt + (j0 + 1) * 16) : make_uint2(0u, 0u);
         }
       }
     }
-  }
-  if (lane < 4) {
-    float mv = mref[0], lv = lsum[0];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (t0 + kTile < r1) issue(buf ^ 1, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
+    tile_barrier();                                      // logits of this tile are in LDS
+    float z[4];
 #pragma unroll
-    for (int h = 1; h < 4; ++h)
-      if (lane == h) {
-        mv = mref[h];
-        lv = lsum[h];
+    for (int h = 0; h < 4; ++h) z[h] = st.z(buf)[h * kTile + lane];
+    const float4 zm = *reinterpret_cast<const float4*>(st.z(buf) + 4 * kTile);   // all lanes alike
+
+    // frame check: weights are taken against a per-head frame kept
+    // kFrameMargin above the running maximum; a tile maximum above it (in
+    // practice only on the first tile) raises the frame and rescales what
+    // was accumulated
+    if (zm.x > mref[0] || zm.y > mref[1] || zm.z > mref[2] || zm.w > mref[3]) {
+      const float zmh[4] = {zm.x, zm.y, zm.z, zm.w};
+      float fac[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float nm = fmaxf(mref[h], zmh[h] + kFrameMargin);
+        fac[h] = __expf(mref[h] - nm);              // exp(-inf) = 0 on the first tile
+        mref[h] = nm;
+        lsum[h] *= fac[h];
+        msum[h] *= fac[h];
       }
-    wsu[lane * kPartialStride + 0] = mv;
-    wsu[lane * kPartialStride + 1] = lv;
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[s][k][r] *= fac[r];
+    }
+    const float vs = h2f((uint16_t)(vm & 0xFFFFu)) * two_e;
+    const float vmin = h2f((uint16_t)(vm >> 16));
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float p = __expf(z[h] - mref[h]);
+      lsum[h] += p;
+      msum[h] = fmaf(p, vmin, msum[h]);
+      const float w = p * vs;
+      const _Float16 whi = (_Float16)w;
+      wbuf[h * kTile + lane] = whi;
+      wbuf[4 * kTile + h * kTile + lane] = (_Float16)(w - (float)whi);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // weights visible to the wave
+
+    // PV: 32 tokens per MFMA
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+      if (32 * G >= nt) break;
+      // A rows 0-3: w_hi of the 4 heads, rows 4-7: w_lo; rows 8-15 repeat
+      // them and only feed C rows 8-15, which are never read.
+      const h8 aw = *reinterpret_cast<const h8*>(wbuf + (col & 7) * kTile + 32 * G + 8 * quad);
+#pragma unroll
+      for (int set = 0; set < 3; ++set) {
+        const int j = 16 * set + col;                     // byte (L=6) or field (L=5)
+        uint32_t p0, p1, p2, p3;
+        if (L == 6) {
+          const uint2 w8 = vr[G][set][0];
+          p0 = perm(kBias, w8.x, 0x04010400u);
+          p1 = perm(kBias, w8.x, 0x04030402u);
+          p2 = perm(kBias, w8.y, 0x04010400u);
+          p3 = perm(kBias, w8.y, 0x04030402u);
+        } else {
+          const int bit = 7 * j;
+          const uint2 b0 = vr[G][set][0];
+          const uint2 b1 = vr[G][set][L == 6 ? 0 : 1];
+          const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
+          p0 = (u32(v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
+          p1 = (u32(v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
+          p2 = (u32(v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
+          p3 = (u32(v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
+        }
+        uint32_t g0[4], g1[4], g2[4];
+        features<L>(p0, g0[0], g1[0], g2[0]);
+        features<L>(p1, g0[1], g1[1], g2[1]);
+        features<L>(p2, g0[2], g1[2], g2[2]);
+        features<L>(p3, g0[3], g1[3], g2[3]);
+        const h8 B0 = as_h8(g0[0], g0[1], g0[2], g0[3]);
+        const h8 B1 = as_h8(g1[0], g1[1], g1[2], g1[3]);
+        const h8 B2 = as_h8(g2[0], g2[1], g2[2], g2[3]);
+        acc[set][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B0, acc[set][0], 0, 0, 0);
+        acc[set][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B1, acc[set][1], 0, 0, 0);
+        acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B2, acc[set][2], 0, 0, 0);
+      }
+    }
   }
+  write_partial<L>(a, u, lane, E, acc, mref, lsum, msum);
 }
 
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
@@ -560,23 +853,67 @@ void decode_mfma_kernel(DecodeArgs a) {
     decode_chunk<5>(a, seg, r0, r1, b, li, g, u, st);
 }
 
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_mfma2_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t k0[kBuf], k1[kBuf], v0[kBuf], v1[kBuf];
+  __shared__ __attribute__((aligned(16))) float z0[4 * kTile + 4], z1[4 * kTile + 4];
+  __shared__ __attribute__((aligned(16))) _Float16 w[2 * 4 * kTile];
+  Stage2 st;
+  st.k0 = k0;
+  st.k1 = k1;
+  st.v0 = v0;
+  st.v1 = v1;
+  st.z0 = z0;
+  st.z1 = z1;
+  st.w = w;
+
+  const int x = blockIdx.x;
+  const int seg = x < a.nch[0] ? 0 : 1;
+  const int ch = seg == 0 ? x : x - a.nch[0];
+  const int64_t r0 = (int64_t)ch * a.chunk;
+  const int64_t r1 = min(r0 + (int64_t)a.chunk, a.rows[seg]);
+  const int li = blockIdx.y / a.kv_heads;
+  const int g = blockIdx.y % a.kv_heads;
+  const int b = blockIdx.z;
+  const int64_t u = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (a.fmt[seg].L == 6) {
+    if (wave == 0) qk_wave<6>(a, seg, r0, r1, b, li, g, st);
+    else pv_wave<6>(a, seg, r0, r1, b, li, g, u, st);
+  } else {
+    if (wave == 0) qk_wave<5>(a, seg, r0, r1, b, li, g, st);
+    else pv_wave<5>(a, seg, r0, r1, b, li, g, u, st);
+  }
+}
+
+// SEMKV_DECODE=mfma1 selects the single-wave kernel (for comparison).
+bool single_wave() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("SEMKV_DECODE");
+    v = (e && e[0] == 'm' && e[4] == '1') ? 1 : 0;
+  }
+  return v == 1;
+}
+
 }  // namespace
 
 // Workgroups of the matrix-core kernel resident on the device at once
 // (registers and LDS both limit it); the pool chunking fills them once.
 int64_t decode_mfma_resident_waves() {
-  static int64_t slots = 0;
-  if (slots <= 0) {
+  static int64_t slots[2] = {0, 0};
+  const int w = single_wave() ? 0 : 1;
+  if (slots[w] <= 0) {
     int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
+    const hipError_t e =
+        w == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel, 64, 0)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma2_kernel, 128, 0);
+    if (e != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel, 64, 0) !=
-            hipSuccess ||
         cus <= 0 || per_cu <= 0)
-      return 2816;
-    slots = (int64_t)cus * per_cu;
+      return 2048;
+    slots[w] = (int64_t)cus * per_cu;
   }
-  return slots;
+  return slots[w];
 }
 
 bool decode_mfma_supported(const DecodeArgs& a) {
@@ -590,7 +927,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int pool_chunks = a.nch[0] + a.nch[1];
   if (pool_chunks == 0) return hipSuccess;
   dim3 grid(pool_chunks, a.nl * a.kv_heads, a.batch);
-  hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(64), 0, stream, a);
+  if (single_wave())
+    hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_mfma2_kernel, grid, dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 
