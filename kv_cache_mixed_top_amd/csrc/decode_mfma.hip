@@ -54,6 +54,7 @@ constexpr int kBuf = 3072;          // 3 x 1 KB load blocks (>= 64 * 43 + 48 rea
 constexpr int kPartialStride = 2 + kHeadDim;
 constexpr int kQkInstr = 33;        // 4x4x4 MFMAs per row (132 digit slots)
 constexpr float kFrameMargin = 8.0f; // softmax frame above the running max (natural log)
+constexpr int kFullRead = 96;       // rows spanned by an unclamped 3 KB tile read (> 3072/38)
 
 __device__ __forceinline__ uint32_t u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ u16x2 v2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
@@ -608,18 +609,30 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   // K rows [t0, t0 + nt) -> buffer `buf` (16 bytes per lane per instruction;
   // chunks past the valid range re-read the last valid chunk); the lane's K
   // meta word -> register
+  // A full tile whose 3 KB read stays inside the plane loads unclamped from a
+  // uniform base (the bytes past the tile are not used).
   uint32_t km_next = 0;
+  const uint32_t lane16 = 16u * (uint32_t)lane;
   auto issue = [&](int buf, int64_t t0, int nt) {
-    const int nk = (nt * R + 15) >> 4;
     const uint8_t* ks = kcodes + t0 * R;
+    if (nt == kTile && t0 + kFullRead <= cap) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      if (64 * i < nk)
-        __builtin_amdgcn_global_load_lds(ks + 16 * min(64 * i + lane, nk - 1),
+      for (int i = 0; i < 3; ++i)
+        __builtin_amdgcn_global_load_lds(ks + (lane16 + 1024u * i),
                                          (lds_void*)(st.k(buf) + 1024 * i), 16, 0, 0);
-    km_next = kmg[t0 + min(lane, nt - 1)];
+      km_next = kmg[t0 + lane];
+    } else {
+      const int nk = (nt * R + 15) >> 4;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (64 * i < nk)
+          __builtin_amdgcn_global_load_lds(ks + 16 * min(64 * i + lane, nk - 1),
+                                           (lds_void*)(st.k(buf) + 1024 * i), 16, 0, 0);
+      km_next = kmg[t0 + min(lane, nt - 1)];
+    }
   };
 
+  float frame[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   int buf = 0;
   if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
   for (int64_t t0 = r0; t0 < r1; t0 += kTile, buf ^= 1) {
@@ -653,16 +666,23 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     }
     const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
     const float kbias = sm * h2f((uint16_t)(km >> 16));
-    float zm[4];
+    float z[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float sq = sacc[0][h] + sacc[1][h] + sacc[2][h];
-      const float z = lane < nt ? fmaf(kfac, sq, kbias * sumq[h]) : -INFINITY;
-      st.z(buf)[h * kTile + lane] = z;
-      zm[h] = wave_max(z);
+      z[h] = lane < nt ? fmaf(kfac, sq, kbias * sumq[h]) : -INFINITY;
+      st.z(buf)[h * kTile + lane] = z[h];
+    }
+    // softmax frame per head, kFrameMargin above the running maximum; it is
+    // raised only when a logit exceeds it (in practice on the first tile)
+    const bool up = z[0] > frame[0] || z[1] > frame[1] || z[2] > frame[2] || z[3] > frame[3];
+    if (__ballot(up) != 0ull) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) frame[h] = fmaxf(frame[h], wave_max(z[h]) + kFrameMargin);
     }
     if (lane == 0)
-      *reinterpret_cast<float4*>(st.z(buf) + 4 * kTile) = make_float4(zm[0], zm[1], zm[2], zm[3]);
+      *reinterpret_cast<float4*>(st.z(buf) + 4 * kTile) =
+          make_float4(frame[0], frame[1], frame[2], frame[3]);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // logits written
     tile_barrier();
   }
@@ -704,15 +724,24 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   // V tiles [t0, t0 + nt) -> buffer `buf` (whole 16-row byte-planar tiles);
   // the lane's V meta word -> register
   uint32_t vm_next = 0;
+  const uint32_t lane16 = 16u * (uint32_t)lane;
   auto issue = [&](int buf, int64_t t0, int nt) {
-    const int nv = ((nt + 15) >> 4) * R;
     const uint8_t* vs = vcodes + t0 * R;
+    if (nt == kTile && t0 + kFullRead <= cap) {
 #pragma unroll
-    for (int i = 0; i < 3; ++i)
-      if (64 * i < nv)
-        __builtin_amdgcn_global_load_lds(vs + 16 * min(64 * i + lane, nv - 1),
+      for (int i = 0; i < 3; ++i)
+        __builtin_amdgcn_global_load_lds(vs + (lane16 + 1024u * i),
                                          (lds_void*)(st.v(buf) + 1024 * i), 16, 0, 0);
-    vm_next = vmg[t0 + min(lane, nt - 1)];
+      vm_next = vmg[t0 + lane];
+    } else {
+      const int nv = ((nt + 15) >> 4) * R;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (64 * i < nv)
+          __builtin_amdgcn_global_load_lds(vs + 16 * min(64 * i + lane, nv - 1),
+                                           (lds_void*)(st.v(buf) + 1024 * i), 16, 0, 0);
+      vm_next = vmg[t0 + min(lane, nt - 1)];
+    }
   };
 
   const int col = lane & 15;
@@ -752,20 +781,17 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
     float z[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) z[h] = st.z(buf)[h * kTile + lane];
-    const float4 zm = *reinterpret_cast<const float4*>(st.z(buf) + 4 * kTile);   // all lanes alike
+    const float4 fr = *reinterpret_cast<const float4*>(st.z(buf) + 4 * kTile);   // all lanes alike
 
-    // frame check: weights are taken against a per-head frame kept
-    // kFrameMargin above the running maximum; a tile maximum above it (in
-    // practice only on the first tile) raises the frame and rescales what
-    // was accumulated
-    if (zm.x > mref[0] || zm.y > mref[1] || zm.z > mref[2] || zm.w > mref[3]) {
-      const float zmh[4] = {zm.x, zm.y, zm.z, zm.w};
+    // the weights are taken against the frame of wave 0; when it was raised
+    // (in practice only on the first tile) what was accumulated is rescaled
+    if (fr.x != mref[0] || fr.y != mref[1] || fr.z != mref[2] || fr.w != mref[3]) {
+      const float nf[4] = {fr.x, fr.y, fr.z, fr.w};
       float fac[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        const float nm = fmaxf(mref[h], zmh[h] + kFrameMargin);
-        fac[h] = __expf(mref[h] - nm);              // exp(-inf) = 0 on the first tile
-        mref[h] = nm;
+        fac[h] = __expf(mref[h] - nf[h]);           // exp(-inf) = 0 on the first tile
+        mref[h] = nf[h];
         lsum[h] *= fac[h];
         msum[h] *= fac[h];
       }

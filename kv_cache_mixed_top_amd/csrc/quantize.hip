@@ -28,7 +28,7 @@ constexpr int kThreads = 256;
 constexpr int kCodeStride = kHeadDim + 2;   // u16 codes per LDS row (pad)
 
 // Exact round-half-even of (x - m)/s given a candidate c0 within 1 of it.
-__device__ __noinline__ float exact_code(float x, float m, float s, float c0) {
+__device__ __forceinline__ float exact_code(float x, float m, float s, float c0) {
   const double d = (double)x - (double)m;           // exact: fp16 operands
   const double sd = (double)s;
   const double c = (double)c0;
@@ -214,6 +214,27 @@ constexpr int kImgBytes = kRows * 43;             // largest packed tile (6 leve
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+// Smallest fp16 >= (hi - lo) / (L - 1) without a division: the fp32 quotient
+// is within 2^-22 of the exact one, so its nearest fp16 is the ceiling or
+// the fp16 just below it; s * (L - 1) >= hi - lo is then decided exactly in
+// double (an fp16 times an integer below 2^16 and a difference of two fp16).
+template <int L>
+__device__ __forceinline__ uint16_t scale_ceil_fast(float lo, float hi) {
+  const double d = (double)hi - (double)lo;
+  if (!(d > 0.0)) return 0;
+  uint16_t h = f2h((float)d * (1.0f / (float)(L - 1)));
+  if ((double)h2f(h) * (double)(L - 1) < d) ++h;
+  return h;
+}
+
+// Exchange with lane ^ 1 / lane ^ 2 inside each quad (DPP quad permutes).
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+
 template <int L>
 __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_pool,
                                    uint8_t* codes8, uint8_t* img) {
@@ -236,10 +257,11 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   // ---- 32 values of this row as 16 fp16 pairs (dims 8q + 32i + 2e + {0,1})
   int token = 0;
   half2_t v[16];
+  const uint16_t* src = nullptr;
   if (valid) {
     token = a.perm[(int64_t)b * a.n + perm_off + row0 + r];
-    const uint16_t* src = a.src[kvsel] + (int64_t)b * a.sb + (int64_t)layer * a.sl +
-                          (int64_t)head * a.sh + (int64_t)token * a.st;
+    src = a.src[kvsel] + (int64_t)b * a.sb + (int64_t)layer * a.sl + (int64_t)head * a.sh +
+          (int64_t)token * a.st;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * q + 32 * i);
@@ -257,47 +279,36 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   half2_t mn = v[0], mx = v[0];
 #pragma unroll
   for (int i = 1; i < 16; ++i) {
-    mn = __builtin_elementwise_min(mn, v[i]);
-    mx = __builtin_elementwise_max(mx, v[i]);
+    mn = __builtin_elementwise_minimum(mn, v[i]);
+    mx = __builtin_elementwise_maximum(mx, v[i]);
   }
   float lo = fminf((float)mn[0], (float)mn[1]);
   float hi = fmaxf((float)mx[0], (float)mx[1]);
-  lo = fminf(lo, __shfl_xor(lo, 1, 64));
-  lo = fminf(lo, __shfl_xor(lo, 2, 64));
-  hi = fmaxf(hi, __shfl_xor(hi, 1, 64));
-  hi = fmaxf(hi, __shfl_xor(hi, 2, 64));
+  lo = fminf(lo, quad_xor1(lo));
+  lo = fminf(lo, quad_xor2(lo));
+  hi = fmaxf(hi, quad_xor1(hi));
+  hi = fmaxf(hi, quad_xor2(hi));
   lo = lo + 0.0f;   // a zero minimum is stored as +0
 
-  const uint16_t sbits = scale_ceil_bits(lo, hi, L);
+  const uint16_t sbits = scale_ceil_fast<L>(lo, hi);
   const float s = h2f(sbits);
 
-  // ---- codes: y = x * (1/s) - m * (1/s) in one fma from the fp16 value.
-  // |y - (x - m)/s| <= 2^-23 ((L-1) + |m|/s) (1 + 2^-20); a code whose y lies
-  // within that of a half-integer is settled exactly.  v_cvt_pk_u8_f32 rounds
-  // to nearest even and clamps to [0, 255], which is the code elsewhere.
+  // ---- codes: y = x * r - m * r in one fma from the fp16 value, r = v_rcp(s)
+  // (within 1 ulp).  |y - (x - m)/s| <= 2^-23 (1.5 (L-1) + |m|/s) (1 + 2^-20);
+  // a code whose y lies within 2^-22 ((L-1) + |m| r) of a half-integer is
+  // settled exactly.  v_cvt_pk_u8_f32 rounds to nearest even and clamps to
+  // [0, 255], which is the code elsewhere.
   uint32_t cw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float rs = 0.f, nb = 0.f, eps = 0.f, dmin = 1.0f;
   if (s > 0.0f) {
-    const float rs = 1.0f / s;
-    const float nb = -lo * rs;
-    const float eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
-    float dmin = 1.0f;
+    rs = __builtin_amdgcn_rcpf(s);
+    nb = -lo * rs;
+    eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const float yv = fmaf((float)v[k >> 1][k & 1], rs, nb);
       dmin = fminf(dmin, fabsf(__builtin_amdgcn_fractf(yv) - 0.5f));
       cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(yv, k & 3, cw[k >> 2]);
-    }
-    if (dmin <= eps) {
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const float x = (float)v[k >> 1][k & 1];
-        const float yv = fmaf(x, rs, nb);
-        if (fabsf(__builtin_amdgcn_fractf(yv) - 0.5f) <= eps) {
-          const float c = exact_code(x, lo, s, rintf(yv));
-          const int sh = 8 * (k & 3);
-          cw[k >> 2] = (cw[k >> 2] & ~(0xFFu << sh)) | ((uint32_t)(int)c << sh);
-        }
-      }
     }
   }
   // dims 8q + 32i .. +8 -> row r of the LDS code array; lane 0 of the quad
@@ -306,6 +317,26 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<uint2*>(crow + 8 * q + 32 * i) = make_uint2(cw[2 * i], cw[2 * i + 1]);
+  if (dmin <= eps) {
+    // Rare: a code of this lane lies near a half-integer.  The lane's values
+    // are read again, 8 at a time, and every code is settled exactly, so
+    // that this path holds few registers.
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i) {
+      const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * q + 32 * i);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      uint32_t c8[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = h2f((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
+        const float yv = fmaf(x, rs, nb);
+        float c = rintf(yv);
+        if (fabsf(__builtin_amdgcn_fractf(yv) - 0.5f) <= eps) c = exact_code(x, lo, s, c);
+        c8[e >> 2] |= (uint32_t)(int)c << (8 * (e & 3));
+      }
+      *reinterpret_cast<uint2*>(crow + 8 * q + 32 * i) = make_uint2(c8[0], c8[1]);
+    }
+  }
   if (q == 0) *reinterpret_cast<uint2*>(crow + 128) = make_uint2(0u, 0u);
   if (tid < 4) reinterpret_cast<uint32_t*>(codes8 + kRows * kCode8Stride)[tid] = 0u;
 
@@ -325,8 +356,9 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   };
   if (L == 6) {
     constexpr uint32_t W = 0x00240601u;              // bytes {1, 6, 36, 0}
-    for (int item = tid; item < kRows * 11; item += kThreads) {
-      const int row = item / 11, u = item - 11 * row;  // fields 4u .. 4u+3
+    const int row = r;
+#pragma unroll
+    for (int u = q; u < 11; u += 4) {                // fields 4u .. 4u+3 of this thread's row
       const uint32_t* c = reinterpret_cast<const uint32_t*>(codes8 + row * kCode8Stride + 12 * u);
       const uint32_t c0 = c[0], c1 = c[1], c2 = c[2];
       put(row, 4 * u, __builtin_amdgcn_udot4(c0, W, 0u, false));
@@ -336,8 +368,9 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
     }
   } else {
     constexpr uint32_t W = 0x00190501u;              // bytes {1, 5, 25, 0}
-    for (int item = tid; item < kRows * 6; item += kThreads) {
-      const int row = item / 6, u = item - 6 * row;  // fields 8u .. 8u+7 = bytes 7u .. 7u+6
+    const int row = r;
+#pragma unroll
+    for (int u = q; u < 6; u += 4) {                 // fields 8u .. 8u+7 = bytes 7u .. 7u+6
       const uint32_t* c = reinterpret_cast<const uint32_t*>(codes8 + row * kCode8Stride + 24 * u);
       const uint32_t a0 = c[0], a1 = c[1], a2 = c[2], a3 = c[3], a4 = c[4], a5 = c[5];
       uint32_t f[8];
