@@ -134,7 +134,7 @@ __device__ __forceinline__ f4 qk_mfma(const h4 (&qf)[3], uint32_t lo, uint32_t h
 }
 
 // ---- 6 levels: one K row = 43 bytes = 11 dwords (the 44th byte masked)
-template <int W>
+template <int W, int NC>
 __device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const h4 (&qf)[3],
                                           f4 (&acc)[3]) {
   const uint32_t X = d[W];
@@ -143,14 +143,14 @@ __device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const h4 (&qf
   uint32_t e0, e1, e2, o0, o1, o2;
   digits<6>(xe, e0, e1, e2);
   digits<6>(xo, o0, o1, o2);
-  acc[0] = qk_mfma<3 * W + 0>(qf, e0, o0, acc[0]);
-  acc[1] = qk_mfma<3 * W + 1>(qf, e1, o1, acc[1]);
-  acc[2] = qk_mfma<3 * W + 2>(qf, e2, o2, acc[2]);
+  acc[0 % NC] = qk_mfma<3 * W + 0>(qf, e0, o0, acc[0 % NC]);
+  acc[1 % NC] = qk_mfma<3 * W + 1>(qf, e1, o1, acc[1 % NC]);
+  acc[2 % NC] = qk_mfma<3 * W + 2>(qf, e2, o2, acc[2 % NC]);
 }
-template <int... Ws>
+template <int NC, int... Ws>
 __device__ __forceinline__ void qk6(const uint32_t (&d)[12], const h4 (&qf)[3], f4 (&acc)[3],
                                     std::integer_sequence<int, Ws...>) {
-  (qk6_dword<Ws>(d, qf, acc), ...);
+  (qk6_dword<Ws, NC>(d, qf, acc), ...);
 }
 
 // ---- 5 levels: one K row = 38 bytes; 7-byte units hold 8 fields of 7 bits.
@@ -160,17 +160,17 @@ __device__ __forceinline__ void field_pairs(uint32_t W, uint32_t& pa, uint32_t& 
   const uint32_t Wp = W >> 7;
   pb = (Wp & 0x7Fu) | (((Wp << 2) & 0x7F0000u) | 0x66006600u);
 }
-template <int Q>   // Q = 2u + quad
+template <int Q, int NC>   // Q = 2u + quad
 __device__ __forceinline__ void qk5_quad(uint32_t W, const h4 (&qf)[3], f4 (&acc)[3]) {
   uint32_t pa, pb, a0, a1, a2, b0, b1, b2;
   field_pairs(W, pa, pb);
   digits<5>(pa, a0, a1, a2);
   digits<5>(pb, b0, b1, b2);
-  acc[0] = qk_mfma<3 * Q + 0>(qf, a0, b0, acc[0]);
-  acc[1] = qk_mfma<3 * Q + 1>(qf, a1, b1, acc[1]);
-  acc[2] = qk_mfma<3 * Q + 2>(qf, a2, b2, acc[2]);
+  acc[0 % NC] = qk_mfma<3 * Q + 0>(qf, a0, b0, acc[0 % NC]);
+  acc[1 % NC] = qk_mfma<3 * Q + 1>(qf, a1, b1, acc[1 % NC]);
+  acc[2 % NC] = qk_mfma<3 * Q + 2>(qf, a2, b2, acc[2 % NC]);
 }
-template <int U>
+template <int U, int NC>
 __device__ __forceinline__ void qk5_unit(const uint32_t (&d)[12], const h4 (&qf)[3],
                                          f4 (&acc)[3]) {
   constexpr int b0 = 7 * U;
@@ -179,16 +179,16 @@ __device__ __forceinline__ void qk5_unit(const uint32_t (&d)[12], const h4 (&qf)
     constexpr int b1 = 7 * U + 4;
     const uint32_t hi = __builtin_amdgcn_alignbyte(d[b1 / 4 + 1], d[b1 / 4], b1 % 4);
     const uint32_t m = __builtin_amdgcn_alignbit(hi, lo, 28);
-    qk5_quad<2 * U>(lo, qf, acc);
-    qk5_quad<2 * U + 1>(m, qf, acc);
+    qk5_quad<2 * U, NC>(lo, qf, acc);
+    qk5_quad<2 * U + 1, NC>(m, qf, acc);
   } else {
-    qk5_quad<2 * U>(lo, qf, acc);   // fields 40..42 and one zero pad field
+    qk5_quad<2 * U, NC>(lo, qf, acc);   // fields 40..42 and one zero pad field
   }
 }
-template <int... Us>
+template <int NC, int... Us>
 __device__ __forceinline__ void qk5(const uint32_t (&d)[12], const h4 (&qf)[3], f4 (&acc)[3],
                                     std::integer_sequence<int, Us...>) {
-  (qk5_unit<Us>(d, qf, acc), ...);
+  (qk5_unit<Us, NC>(d, qf, acc), ...);
 }
 
 // d index of slot `i` (0..3) of QK instruction s, or -1 for a zero slot.
@@ -446,11 +446,11 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
       d[11] = 0;
       if (L == 6) {
         d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
-        qk6(d, qf, sacc, std::make_integer_sequence<int, 11>{});
+        qk6<3>(d, qf, sacc, std::make_integer_sequence<int, 11>{});
       } else {
         d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
         d[10] = 0;
-        qk5(d, qf, sacc, std::make_integer_sequence<int, 6>{});
+        qk5<3>(d, qf, sacc, std::make_integer_sequence<int, 6>{});
       }
     }
     const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
@@ -657,11 +657,11 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
       d[11] = 0;
       if (L == 6) {
         d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
-        qk6(d, qf, sacc, std::make_integer_sequence<int, 11>{});
+        qk6<1>(d, qf, sacc, std::make_integer_sequence<int, 11>{});
       } else {
         d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
         d[10] = 0;
-        qk5(d, qf, sacc, std::make_integer_sequence<int, 6>{});
+        qk5<1>(d, qf, sacc, std::make_integer_sequence<int, 6>{});
       }
     }
     const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
@@ -669,8 +669,8 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     float z[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float sq = sacc[0][h] + sacc[1][h] + sacc[2][h];
-      z[h] = lane < nt ? fmaf(kfac, sq, kbias * sumq[h]) : -INFINITY;
+      const float zf = fmaf(kfac, sacc[0][h], kbias * sumq[h]);   // one accumulator chain
+      z[h] = (nt == kTile || lane < nt) ? zf : -INFINITY;
       st.z(buf)[h * kTile + lane] = z[h];
     }
     // softmax frame per head, kFrameMargin above the running maximum; it is
