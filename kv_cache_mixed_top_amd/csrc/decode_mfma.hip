@@ -224,7 +224,29 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Largest V scale (the low half of the meta word) over rows [r0, r1), as
+// fp16 bits, in every lane.  Sixteen independent loads per lane are in
+// flight at a time, so a chunk costs a few memory latencies, not one per
+// 64 rows.
+__device__ __forceinline__ uint32_t chunk_scale_max(const uint32_t* vmg, int64_t r0, int64_t r1,
+                                                    int lane) {
+  constexpr int kDepth = 16;
+  uint32_t smax = 0;
+  for (int64_t r = r0 + lane; r < r1; r += 64 * kDepth) {
+    uint32_t v[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) v[i] = vmg[min(r + 64 * i, r1 - 1)];   // repeats are harmless
+#pragma unroll
+    for (int i = 0; i < kDepth; ++i) smax = max(smax, v[i] & 0xFFFFu);
+  }
+  return wave_max_u32(smax);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+// LDS address of byte `off` of a shared buffer; the offset is added in the
+// LDS address space, so the DMA target stays visibly inside its buffer.
+__device__ __forceinline__ lds_void* lds_at(uint8_t* p, int off) { return (lds_void*)((lds_u8*)p + off); }
 
 // LDS of one wave (a workgroup is one wave): two staging buffers of K rows
 // and V tiles filled by direct global->LDS loads, plus the softmax weights.
@@ -331,9 +353,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
     sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
 
   // ---- per-chunk exponent E: w = p * scale_V * 2^E stays below 2^14
-  uint32_t smax = 0;
-  for (int64_t r = r0 + lane; r < r1; r += 64) smax = max(smax, vmg[r] & 0xFFFFu);
-  smax = wave_max_u32(smax);
+  const uint32_t smax = chunk_scale_max(vmg, r0, r1, lane);
   int E = 0;
   if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
   const float two_e = ldexpf(1.0f, E);
@@ -406,19 +426,19 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       const int tok0 = 32 * G + 8 * quad;
-      const uint8_t* vt = vbuf + (tok0 >> 4) * (16 * R) + (tok0 & 15);
+      const int vo = (tok0 >> 4) * (16 * R) + (tok0 & 15);
 #pragma unroll
       for (int set = 0; set < 3; ++set) {
         const int j = 16 * set + col;
         if (L == 6) {
-          vr[G][set][0] = (32 * G < nt && j < R) ? *reinterpret_cast<const uint2*>(vt + j * 16)
+          vr[G][set][0] = (32 * G < nt && j < R) ? *reinterpret_cast<const uint2*>(vbuf + (vo + j * 16))
                                                 : make_uint2(0u, 0u);
         } else {
           const int j0 = (7 * j) >> 3;
           const bool ok = 32 * G < nt && j < 43;
-          vr[G][set][0] = ok ? *reinterpret_cast<const uint2*>(vt + j0 * 16) : make_uint2(0u, 0u);
+          vr[G][set][0] = ok ? *reinterpret_cast<const uint2*>(vbuf + (vo + j0 * 16)) : make_uint2(0u, 0u);
           vr[G][set][L == 6 ? 0 : 1] =
-              ok ? *reinterpret_cast<const uint2*>(vt + (j0 + 1) * 16) : make_uint2(0u, 0u);
+              ok ? *reinterpret_cast<const uint2*>(vbuf + (vo + (j0 + 1) * 16)) : make_uint2(0u, 0u);
         }
       }
     }
@@ -568,6 +588,21 @@ struct Stage2 {
 // One workgroup barrier with no memory fence: the LDS writes before it are
 // waited for by the caller; outstanding global->LDS prefetches stay in flight.
 __device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// s_waitcnt through the builtin (not inline asm), so that the compiler's own
+// wait insertion knows what has completed; the encodings are those of the
+// CDNA s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt in 6:4,
+// lgkmcnt in 11:8).
+// 16-byte LDS read that also waits for it (and every LDS access before it)
+// inside the same asm block, so that the result register is written when
+// the block ends.
+__device__ __forceinline__ h8 lds_read_h8_wait(const _Float16* p) {
+  h8 r;
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) _Float16*)p;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a) : "memory");
+  return r;
+}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int L>
 __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0, int64_t r1, int b, int li,
@@ -619,7 +654,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
       for (int i = 0; i < 3; ++i)
         __builtin_amdgcn_global_load_lds(ks + (lane16 + 1024u * i),
-                                         (lds_void*)(st.k(buf) + 1024 * i), 16, 0, 0);
+                                         lds_at(st.k(buf), 1024 * i), 16, 0, 0);
       km_next = kmg[t0 + lane];
     } else {
       const int nk = (nt * R + 15) >> 4;
@@ -627,33 +662,30 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
       for (int i = 0; i < 3; ++i)
         if (64 * i < nk)
           __builtin_amdgcn_global_load_lds(ks + 16 * min(64 * i + lane, nk - 1),
-                                           (lds_void*)(st.k(buf) + 1024 * i), 16, 0, 0);
+                                           lds_at(st.k(buf), 1024 * i), 16, 0, 0);
       km_next = kmg[t0 + min(lane, nt - 1)];
     }
   };
 
   float frame[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  int buf = 0;
-  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
-  for (int64_t t0 = r0; t0 < r1; t0 += kTile, buf ^= 1) {
+  // One tile in staging buffer B (a compile-time constant, so that reads of
+  // buffer B are known not to overlap the loads in flight into 1 - B).
+  auto tile = [&](int64_t t0, auto Bc) {
+    constexpr int B = decltype(Bc)::value;
     const int nt = (int)min((int64_t)kTile, r1 - t0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile's rows have landed
+    wait_vm0();   // this tile's rows have landed
     const uint32_t km = km_next;
+    if (t0 + kTile < r1) issue(1 - B, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
     f4 sacc[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) sacc[k] = (f4){0.f, 0.f, 0.f, 0.f};
     {
       const int off = lane * R;
-      const uint32_t* kb32 = reinterpret_cast<const uint32_t*>(st.k(buf) + (off & ~3));
+      const uint32_t* kb32 = reinterpret_cast<const uint32_t*>(st.k(B) + (off & ~3));
       const int sh = off & 3;
-      uint32_t raw[12];
-#pragma unroll
-      for (int i = 0; i < 12; ++i) raw[i] = kb32[i];
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // staging reads done
-      if (t0 + kTile < r1) issue(buf ^ 1, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
       uint32_t d[12];
 #pragma unroll
-      for (int i = 0; i < 11; ++i) d[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
+      for (int i = 0; i < 11; ++i) d[i] = __builtin_amdgcn_alignbyte(kb32[i + 1], kb32[i], sh);
       d[11] = 0;
       if (L == 6) {
         d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
@@ -671,7 +703,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     for (int h = 0; h < 4; ++h) {
       const float zf = fmaf(kfac, sacc[0][h], kbias * sumq[h]);   // one accumulator chain
       z[h] = (nt == kTile || lane < nt) ? zf : -INFINITY;
-      st.z(buf)[h * kTile + lane] = z[h];
+      st.z(B)[h * kTile + lane] = z[h];
     }
     // softmax frame per head, kFrameMargin above the running maximum; it is
     // raised only when a logit exceeds it (in practice on the first tile)
@@ -681,10 +713,15 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
       for (int h = 0; h < 4; ++h) frame[h] = fmaxf(frame[h], wave_max(z[h]) + kFrameMargin);
     }
     if (lane == 0)
-      *reinterpret_cast<float4*>(st.z(buf) + 4 * kTile) =
+      *reinterpret_cast<float4*>(st.z(B) + 4 * kTile) =
           make_float4(frame[0], frame[1], frame[2], frame[3]);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // logits written
+    wait_lgkm0();  // logits written
     tile_barrier();
+  };
+  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
+  for (int64_t t0 = r0; t0 < r1; t0 += 2 * kTile) {   // same tile sequence as wave 1
+    tile(t0, std::integral_constant<int, 0>{});
+    if (t0 + kTile < r1) tile(t0 + kTile, std::integral_constant<int, 1>{});
   }
 }
 
@@ -701,9 +738,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   const uint32_t* vmg = a.meta[seg] + (plane_k + 1) * cap;
 
   // per-chunk exponent E: w = p * scale_V * 2^E stays below 2^14
-  uint32_t smax = 0;
-  for (int64_t r = r0 + lane; r < r1; r += 64) smax = max(smax, vmg[r] & 0xFFFFu);
-  smax = wave_max_u32(smax);
+  const uint32_t smax = chunk_scale_max(vmg, r0, r1, lane);
   int E = 0;
   if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
   const float two_e = ldexpf(1.0f, E);
@@ -731,7 +766,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
       for (int i = 0; i < 3; ++i)
         __builtin_amdgcn_global_load_lds(vs + (lane16 + 1024u * i),
-                                         (lds_void*)(st.v(buf) + 1024 * i), 16, 0, 0);
+                                         lds_at(st.v(buf), 1024 * i), 16, 0, 0);
       vm_next = vmg[t0 + lane];
     } else {
       const int nv = ((nt + 15) >> 4) * R;
@@ -739,49 +774,27 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
       for (int i = 0; i < 3; ++i)
         if (64 * i < nv)
           __builtin_amdgcn_global_load_lds(vs + 16 * min(64 * i + lane, nv - 1),
-                                           (lds_void*)(st.v(buf) + 1024 * i), 16, 0, 0);
+                                           lds_at(st.v(buf), 1024 * i), 16, 0, 0);
       vm_next = vmg[t0 + min(lane, nt - 1)];
     }
   };
 
   const int col = lane & 15;
   const int quad = lane >> 4;
-  int buf = 0;
-  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
-  for (int64_t t0 = r0; t0 < r1; t0 += kTile, buf ^= 1) {
+  // One tile in staging buffer B (a compile-time constant, so that reads of
+  // buffer B are known not to overlap the loads in flight into 1 - B: the
+  // next tile's loads go out first and the V bytes are read where used).
+  auto tile = [&](int64_t t0, auto Bc) {
+    constexpr int B = decltype(Bc)::value;
     const int nt = (int)min((int64_t)kTile, r1 - t0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile's V has landed
+    wait_vm0();   // this tile's V has landed
     const uint32_t vm = vm_next;
-    // this lane's V code bytes (8 tokens x one byte per group and set; two
-    // bytes for 5 levels), read before the next tile's loads are issued
-    uint2 vr[2][3][L == 6 ? 1 : 2];
-    const uint8_t* vbuf = st.v(buf);
-#pragma unroll
-    for (int G = 0; G < 2; ++G) {
-      const int tok0 = 32 * G + 8 * quad;
-      const uint8_t* vt = vbuf + (tok0 >> 4) * (16 * R) + (tok0 & 15);
-#pragma unroll
-      for (int set = 0; set < 3; ++set) {
-        const int j = 16 * set + col;
-        if (L == 6) {
-          vr[G][set][0] = (32 * G < nt && j < R) ? *reinterpret_cast<const uint2*>(vt + j * 16)
-                                                : make_uint2(0u, 0u);
-        } else {
-          const int j0 = (7 * j) >> 3;
-          const bool ok = 32 * G < nt && j < 43;
-          vr[G][set][0] = ok ? *reinterpret_cast<const uint2*>(vt + j0 * 16) : make_uint2(0u, 0u);
-          vr[G][set][L == 6 ? 0 : 1] =
-              ok ? *reinterpret_cast<const uint2*>(vt + (j0 + 1) * 16) : make_uint2(0u, 0u);
-        }
-      }
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (t0 + kTile < r1) issue(buf ^ 1, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
+    if (t0 + kTile < r1) issue(1 - B, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
     tile_barrier();                                      // logits of this tile are in LDS
     float z[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) z[h] = st.z(buf)[h * kTile + lane];
-    const float4 fr = *reinterpret_cast<const float4*>(st.z(buf) + 4 * kTile);   // all lanes alike
+    for (int h = 0; h < 4; ++h) z[h] = st.z(B)[h * kTile + lane];
+    const float4 fr = *reinterpret_cast<const float4*>(st.z(B) + 4 * kTile);   // all lanes alike
 
     // the weights are taken against the frame of wave 0; when it was raised
     // (in practice only on the first tile) what was accumulated is rescaled
@@ -814,29 +827,35 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
       wbuf[h * kTile + lane] = whi;
       wbuf[4 * kTile + h * kTile + lane] = (_Float16)(w - (float)whi);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // weights visible to the wave
+    wait_lgkm0();  // weights visible to the wave
 
     // PV: 32 tokens per MFMA
+    const uint8_t* vbuf = st.v(B);
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       if (32 * G >= nt) break;
       // A rows 0-3: w_hi of the 4 heads, rows 4-7: w_lo; rows 8-15 repeat
       // them and only feed C rows 8-15, which are never read.
-      const h8 aw = *reinterpret_cast<const h8*>(wbuf + (col & 7) * kTile + 32 * G + 8 * quad);
+      const h8 aw = lds_read_h8_wait(wbuf + (col & 7) * kTile + 32 * G + 8 * quad);
+      const int tok0 = 32 * G + 8 * quad;
+      const int vo = (tok0 >> 4) * (16 * R) + (tok0 & 15);
 #pragma unroll
       for (int set = 0; set < 3; ++set) {
         const int j = 16 * set + col;                     // byte (L=6) or field (L=5)
+        // this lane's code byte(s) of 8 tokens
         uint32_t p0, p1, p2, p3;
         if (L == 6) {
-          const uint2 w8 = vr[G][set][0];
+          const uint2 w8 = j < R ? *reinterpret_cast<const uint2*>(vbuf + (vo + j * 16)) : make_uint2(0u, 0u);
           p0 = perm(kBias, w8.x, 0x04010400u);
           p1 = perm(kBias, w8.x, 0x04030402u);
           p2 = perm(kBias, w8.y, 0x04010400u);
           p3 = perm(kBias, w8.y, 0x04030402u);
         } else {
+          const int j0 = (7 * j) >> 3;
+          const bool ok = j < 43;
+          const uint2 b0 = ok ? *reinterpret_cast<const uint2*>(vbuf + (vo + j0 * 16)) : make_uint2(0u, 0u);
+          const uint2 b1 = ok ? *reinterpret_cast<const uint2*>(vbuf + (vo + (j0 + 1) * 16)) : make_uint2(0u, 0u);
           const int bit = 7 * j;
-          const uint2 b0 = vr[G][set][0];
-          const uint2 b1 = vr[G][set][L == 6 ? 0 : 1];
           const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
           p0 = (u32(v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
           p1 = (u32(v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
@@ -856,6 +875,11 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
         acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B2, acc[set][2], 0, 0, 0);
       }
     }
+  };
+  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
+  for (int64_t t0 = r0; t0 < r1; t0 += 2 * kTile) {   // same tile sequence as wave 0
+    tile(t0, std::integral_constant<int, 0>{});
+    if (t0 + kTile < r1) tile(t0 + kTile, std::integral_constant<int, 1>{});
   }
   write_partial<L>(a, u, lane, E, acc, mref, lsum, msum);
 }
