@@ -54,6 +54,8 @@ constexpr int kBuf = 3072;          // 3 x 1 KB load blocks (>= 64 * 43 + 48 rea
 constexpr int kPartialStride = 2 + kHeadDim;
 constexpr int kQkInstr = 33;        // 4x4x4 MFMAs per row (132 digit slots)
 constexpr float kFrameMargin = 8.0f; // softmax frame above the running max (natural log)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kFullRead = 96;       // rows spanned by an unclamped 3 KB tile read (> 3072/38)
 
 __device__ __forceinline__ uint32_t u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -155,15 +157,25 @@ __device__ __forceinline__ void qk6(const uint32_t (&d)[12], const h4 (&qf)[3], 
 
 // ---- 5 levels: one K row = 38 bytes; 7-byte units hold 8 fields of 7 bits.
 // From a word W with fields at bits 0, 7, 14, 21: slots (F0, F2) and (F1, F3).
-__device__ __forceinline__ void field_pairs(uint32_t W, uint32_t& pa, uint32_t& pb) {
-  pa = (W & 0x7Fu) | (((W << 2) & 0x7F0000u) | 0x66006600u);
-  const uint32_t Wp = W >> 7;
-  pb = (Wp & 0x7Fu) | (((Wp << 2) & 0x7F0000u) | 0x66006600u);
+// `bias` is 0x66006600 held in a register, so that each mask and OR is one
+// AND-OR.
+__device__ __forceinline__ void field_pairs(uint32_t W, uint32_t& pa, uint32_t& pb,
+                                            uint32_t bias) {
+  pa = (((W << 2) & 0x7F0000u) | ((W & 0x7Fu) | bias));
+  pb = (((W >> 5) & 0x7F0000u) | (((W >> 7) & 0x7Fu) | bias));
+}
+// 0x66006600 in a vector register (the compiler cannot fold it back into a
+// literal, which these instructions cannot take together with a mask).
+__device__ __forceinline__ uint32_t bias_register() {
+  uint32_t b;
+  asm volatile("v_mov_b32 %0, 0x66006600" : "=v"(b));
+  return b;
 }
 template <int Q, int NC>   // Q = 2u + quad
-__device__ __forceinline__ void qk5_quad(uint32_t W, const h4 (&qf)[3], f4 (&acc)[3]) {
+__device__ __forceinline__ void qk5_quad(uint32_t W, const h4 (&qf)[3], f4 (&acc)[3],
+                                         uint32_t bias) {
   uint32_t pa, pb, a0, a1, a2, b0, b1, b2;
-  field_pairs(W, pa, pb);
+  field_pairs(W, pa, pb, bias);
   digits<5>(pa, a0, a1, a2);
   digits<5>(pb, b0, b1, b2);
   acc[0 % NC] = qk_mfma<3 * Q + 0>(qf, a0, b0, acc[0 % NC]);
@@ -172,23 +184,23 @@ __device__ __forceinline__ void qk5_quad(uint32_t W, const h4 (&qf)[3], f4 (&acc
 }
 template <int U, int NC>
 __device__ __forceinline__ void qk5_unit(const uint32_t (&d)[12], const h4 (&qf)[3],
-                                         f4 (&acc)[3]) {
+                                         f4 (&acc)[3], uint32_t bias) {
   constexpr int b0 = 7 * U;
   const uint32_t lo = __builtin_amdgcn_alignbyte(d[b0 / 4 + 1], d[b0 / 4], b0 % 4);
   if (U < 5) {
     constexpr int b1 = 7 * U + 4;
     const uint32_t hi = __builtin_amdgcn_alignbyte(d[b1 / 4 + 1], d[b1 / 4], b1 % 4);
     const uint32_t m = __builtin_amdgcn_alignbit(hi, lo, 28);
-    qk5_quad<2 * U, NC>(lo, qf, acc);
-    qk5_quad<2 * U + 1, NC>(m, qf, acc);
+    qk5_quad<2 * U, NC>(lo, qf, acc, bias);
+    qk5_quad<2 * U + 1, NC>(m, qf, acc, bias);
   } else {
-    qk5_quad<2 * U, NC>(lo, qf, acc);   // fields 40..42 and one zero pad field
+    qk5_quad<2 * U, NC>(lo, qf, acc, bias);   // fields 40..42 and one zero pad field
   }
 }
 template <int NC, int... Us>
 __device__ __forceinline__ void qk5(const uint32_t (&d)[12], const h4 (&qf)[3], f4 (&acc)[3],
-                                    std::integer_sequence<int, Us...>) {
-  (qk5_unit<Us, NC>(d, qf, acc), ...);
+                                    uint32_t bias, std::integer_sequence<int, Us...>) {
+  (qk5_unit<Us, NC>(d, qf, acc, bias), ...);
 }
 
 // d index of slot `i` (0..3) of QK instruction s, or -1 for a zero slot.
@@ -262,7 +274,8 @@ struct Stage {
 template <int L>
 __device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t u, int lane, int E,
                                               f4 (&acc)[3][3], const float (&mref)[4],
-                                              float (&lsum)[4], float (&msum)[4]) {
+                                              float (&lsum)[4], float (&msum)[4],
+                                              float m_unit = 1.0f) {
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
     lsum[h] = wave_sum(lsum[h]);
@@ -307,7 +320,7 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t u, in
 #pragma unroll
   for (int h = 0; h < 4; ++h)
     if (lane == h) {
-      wsu[h * kPartialStride + 0] = mref[h];
+      wsu[h * kPartialStride + 0] = mref[h] * m_unit;   // natural-log units
       wsu[h * kPartialStride + 1] = lsum[h];
     }
 }
@@ -326,6 +339,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
   const uint32_t* kmg = a.meta[seg] + plane_k * cap;
   const uint32_t* vmg = kmg + cap;
   const float sm = a.sm_scale;
+  const uint32_t bias5 = L == 5 ? bias_register() : 0u;   // 5-level field bias
 
   // ---- queries: ABID-packed 4x4x4 A fragments and per-head sums
   const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
@@ -470,7 +484,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
       } else {
         d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
         d[10] = 0;
-        qk5<3>(d, qf, sacc, std::make_integer_sequence<int, 6>{});
+        qk5<3>(d, qf, sacc, bias5, std::make_integer_sequence<int, 6>{});
       }
     }
     const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
@@ -614,7 +628,8 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   const int64_t cap = a.cap[seg];
   const uint8_t* kcodes = a.codes[seg] + plane_k * cap * R;
   const uint32_t* kmg = a.meta[seg] + plane_k * cap;
-  const float sm = a.sm_scale;
+  const float sm = a.sm_scale * kLog2e;   // logits in log2 units
+  const uint32_t bias5 = L == 5 ? bias_register() : 0u;   // 5-level field bias
 
   // queries: ABID-packed 4x4x4 A fragments and per-head sums
   const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
@@ -693,7 +708,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
       } else {
         d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
         d[10] = 0;
-        qk5<1>(d, qf, sacc, std::make_integer_sequence<int, 6>{});
+        qk5<1>(d, qf, sacc, bias5, std::make_integer_sequence<int, 6>{});
       }
     }
     const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
@@ -710,7 +725,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     const bool up = z[0] > frame[0] || z[1] > frame[1] || z[2] > frame[2] || z[3] > frame[3];
     if (__ballot(up) != 0ull) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) frame[h] = fmaxf(frame[h], wave_max(z[h]) + kFrameMargin);
+      for (int h = 0; h < 4; ++h) frame[h] = fmaxf(frame[h], wave_max(z[h]) + kFrameMargin * kLog2e);
     }
     if (lane == 0)
       *reinterpret_cast<float4*>(st.z(B) + 4 * kTile) =
@@ -781,6 +796,9 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
 
   const int col = lane & 15;
   const int quad = lane >> 4;
+  // the 0x66 bias bytes of 5-level fields, held in a register so that the
+  // mask and the bias go into one AND-OR
+  const uint32_t bias5 = L == 5 ? bias_register() : 0u;
   // One tile in staging buffer B (a compile-time constant, so that reads of
   // buffer B are known not to overlap the loads in flight into 1 - B: the
   // next tile's loads go out first and the V bytes are read where used).
@@ -803,7 +821,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
       float fac[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        fac[h] = __expf(mref[h] - nf[h]);           // exp(-inf) = 0 on the first tile
+        fac[h] = __builtin_amdgcn_exp2f(mref[h] - nf[h]);   // 2^-inf = 0 on the first tile
         mref[h] = nf[h];
         lsum[h] *= fac[h];
         msum[h] *= fac[h];
@@ -819,7 +837,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
     const float vmin = h2f((uint16_t)(vm >> 16));
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float p = __expf(z[h] - mref[h]);
+      const float p = __builtin_amdgcn_exp2f(z[h] - mref[h]);
       lsum[h] += p;
       msum[h] = fmaf(p, vmin, msum[h]);
       const float w = p * vs;
@@ -857,10 +875,10 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
           const uint2 b1 = ok ? *reinterpret_cast<const uint2*>(vbuf + (vo + (j0 + 1) * 16)) : make_uint2(0u, 0u);
           const int bit = 7 * j;
           const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
-          p0 = (u32(v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
-          p1 = (u32(v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
-          p2 = (u32(v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
-          p3 = (u32(v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
+          p0 = (u32(v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & 0x007F007Fu) | bias5;
+          p1 = (u32(v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & 0x007F007Fu) | bias5;
+          p2 = (u32(v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & 0x007F007Fu) | bias5;
+          p3 = (u32(v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & 0x007F007Fu) | bias5;
         }
         uint32_t g0[4], g1[4], g2[4];
         features<L>(p0, g0[0], g1[0], g2[0]);
@@ -881,7 +899,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
     tile(t0, std::integral_constant<int, 0>{});
     if (t0 + kTile < r1) tile(t0 + kTile, std::integral_constant<int, 1>{});
   }
-  write_partial<L>(a, u, lane, E, acc, mref, lsum, msum);
+  write_partial<L>(a, u, lane, E, acc, mref, lsum, msum, kLn2);
 }
 
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
