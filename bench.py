@@ -68,6 +68,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=16,
                     help="layers of the bounded oracle sample")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the generation, per-layer graph and copy legs")
+    ap.add_argument("--gen-steps", type=int, default=None,
+                    help="generated tokens per sequence in the generation leg "
+                         "(default: the gen_16x8k workload's)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a streaming copy of MIB MiB (read + write) three times, "
                          "the reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE")
@@ -225,10 +230,26 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_extra:
+        result["decode_graph_per_layer"] = graph_leg(sk, torch, cache, q, D, layers, B, Hq,
+                                                     decode_bytes, stream)
+        log(f"per-layer graph: {result['decode_graph_per_layer']['us_per_step']} us/step")
+        result["hbm_copy_context"] = copy_leg(torch, stream)
+        log(f"copy context: {result['hbm_copy_context']['GB/s']} GB/s")
+        del K, V
+        torch.cuda.empty_cache()
+        result["generation"] = gen_leg(sk, W, torch, dev, stream, args.gen_steps)
+        g = result["generation"]
+        log(f"generation: decode {g['decode_us_per_step']} us/step, "
+            f"{g['decode_tokens/s']} tok/s; block quantize {g['block_quantize_us']} us")
+        K = V = None
+
     if not args.no_cpu_baseline:
         import cpu_baseline
         import oracle as O
         ls = max(1, min(args.cpu_layers, layers))
+        if K is None:                      # freed by the extra legs: draw them again
+            K, V, _ = W.make_kv_torch(w, dev)
         Ks = K[0, :ls].cpu().numpy()
         Vs = V[0, :ls].cpu().numpy()
         ps = perm[0].cpu().numpy()
@@ -252,6 +273,165 @@ def main():
         log(f"cpu baseline: {cpu_step_s:.1f} s/step extrapolated ({workers} workers)")
 
     print(json.dumps(result), flush=True)
+
+
+def graph_leg(sk, torch, cache, q, D, layers, B, Hq, decode_bytes, stream):
+    """Decode as 32 per-layer launch pairs (partials + merge) captured once in
+    a HIP graph and replayed per step; the output is checked against the
+    one-launch form."""
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    steps = min(D, 32)
+    out_g = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device=q.device)
+    out_e = torch.empty_like(out_g)
+    qbuf = torch.empty_like(q[0])
+    cap_stream = torch.cuda.Stream(device=q.device)   # default priority
+    graph = torch.cuda.CUDAGraph()
+    qbuf.copy_(q[0])
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cap_stream):
+        for layer in range(layers):
+            sk.semkv_decode_partials(cache, qbuf[:, layer:layer + 1], layer0=layer,
+                                     stream=cap_stream)
+            sk.semkv_decode_merge(cache, out_g[:, layer:layer + 1], stream=cap_stream)
+    worst = 0.0
+    for j in (0, steps - 1):                    # replays against the one-launch result
+        with torch.cuda.stream(stream):
+            qbuf.copy_(q[j])
+        stream.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        sk.semkv_decode_attn(cache, q[j], out_e, stream=stream)
+        stream.synchronize()
+        rel = (out_g - out_e).abs() / out_e.abs().clamp(min=1.0)
+        worst = max(worst, float(rel.max()))
+    # per-layer launches split the rows into different chunks, so the two
+    # forms agree to the rounding of the split, well inside the parity bound
+    assert worst <= 2e-3, f"graph replay differs from the one-launch decode by {worst}"
+    times = []
+    for j in range(steps):
+        with torch.cuda.stream(stream):
+            qbuf.copy_(q[j])
+        a, b = Ev(), Ev()
+        torch.cuda.synchronize()
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    us = 1e3 * sum(times) / len(times)
+    sk.semkv_sync_check(stream)
+    return {"launches_per_step": 2 * layers, "steps": steps, "us_per_step": round(us, 2),
+            "GB/s": round(decode_bytes / (us * 1e-6) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * decode_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "max_rel_diff_vs_one_launch": worst}
+
+
+def copy_leg(torch, stream, mib=2048):
+    """Device-to-device copy of `mib` MiB (read + write), as the achievable
+    HBM rate on this machine for context; not a roofline peak."""
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    n = mib * (1 << 20) // 4
+    with torch.cuda.stream(stream):
+        src = torch.ones(n, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+    stream.synchronize()
+    best = float("inf")
+    for _ in range(5):
+        a, b = Ev(), Ev()
+        a.record(stream)
+        with torch.cuda.stream(stream):
+            dst.copy_(src)
+        b.record(stream)
+        b.synchronize()
+        best = min(best, a.elapsed_time(b))
+    gbs = 2 * n * 4 / (best * 1e-3) / 1e9
+    del src, dst
+    return {"kind": "torch device copy, best of 5", "bytes_moved": 2 * n * 4,
+            "ms": round(best, 4), "GB/s": round(gbs, 1),
+            "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
+
+
+def gen_leg(sk, W, torch, dev, stream, gen_steps=None):
+    """Generation workload (16 x 8,192-token prompts, r = 0.25): quantize the
+    prompts, then per step append one token per sequence (a block of 128 is
+    ranked, quantized and packed when the tail fills) and decode all layers
+    over the pools plus the fp16 tail."""
+    w = W.WORKLOADS["gen_16x8k"]
+    T = w.gen_tokens if gen_steps is None else gen_steps
+    B, n = w.batch, w.n
+    k = sk.semkv_topr_count(n, w.r)
+    kb = sk.semkv_topr_count(w.block, w.r)
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        K, V, _ = W.make_kv_torch(w, dev)
+        scores = W.attention_mass_torch(K, w, dev)
+        Kg, Vg, Sg = W.make_gen_tokens_torch(w, T, dev)
+        Qg = W.make_q_torch(w, T, dev)
+        cache = sk.SemKVCache(B, w.layers, w.kv_heads, w.q_heads, w.L_high, w.L_low,
+                              cap16(k + (T // w.block + 1) * kb),
+                              cap16(n - k + (T // w.block + 1) * (w.block - kb)),
+                              block=w.block, max_tokens=n + T)
+        perm = torch.empty((B, n), dtype=torch.int32, device=dev)
+        out = torch.empty((B, w.layers, w.q_heads, 128), dtype=torch.float32, device=dev)
+    stream.synchronize()
+    Rh, Rl = sk.semkv_row_bytes(w.L_high), sk.semkv_row_bytes(w.L_low)
+    planes = B * w.layers * w.kv_heads * 2
+    qa, qb = Ev(), Ev()
+    qa.record(stream)
+    sk.semkv_rank_topr(scores, k, perm, stream=stream)
+    sk.semkv_quantize_pack(cache, K, V, perm, k, stream=stream)
+    qb.record(stream)
+    del K, V
+    ev_app = [(Ev(), Ev()) for _ in range(T)]
+    ev_dec = [(Ev(), Ev()) for _ in range(T)]
+    pool_rows = []
+    start, end = Ev(), Ev()
+    start.record(stream)
+    for i in range(T):
+        ev_app[i][0].record(stream)
+        sk.semkv_append_block(cache, Kg[i].unsqueeze(3), Vg[i].unsqueeze(3), Sg[i].unsqueeze(1),
+                              w.r, stream=stream)
+        ev_app[i][1].record(stream)
+        pool_rows.append((cache.n_high, cache.n_low, cache.n_tail))
+        ev_dec[i][0].record(stream)
+        sk.semkv_decode_attn(cache, Qg[i], out, sm_scale=w.sm_scale, stream=stream)
+        ev_dec[i][1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    sk.semkv_sync_check(stream)
+    t_app = [a.elapsed_time(b) for a, b in ev_app]
+    t_dec = [a.elapsed_time(b) for a, b in ev_dec]
+    blocks = [i for i in range(T) if pool_rows[i][2] == 0]
+    plain = [t_app[i] for i in range(T) if pool_rows[i][2] != 0]
+    dec_bytes = []
+    for nh, nl_, nt in pool_rows:
+        dec_bytes.append(B * w.layers * w.kv_heads * 2 * (nh * (Rh + 4) + nl_ * (Rl + 4)
+                                                            + nt * 256)
+                         + B * w.layers * w.q_heads * 128 * (2 + 4))
+    ms_dec = sum(t_dec) / T
+    dec_gbs = sum(dec_bytes) / (sum(t_dec) * 1e-3) / 1e9
+    blk_bytes = planes * (kb * (256 + Rh + 4) + (w.block - kb) * (256 + Rl + 4))
+    ms_blk = sum(t_app[i] for i in blocks) / max(1, len(blocks))
+    prompt_ms = qa.elapsed_time(qb)
+    prompt_bytes = planes * (k * (256 + Rh + 4) + (n - k) * (256 + Rl + 4))
+    res = {"workload": "gen_16x8k", "batch": B, "prompt_tokens": n, "r": w.r,
+           "generated_tokens": T,
+           "prompt_rank_quantize_ms": round(prompt_ms, 3),
+           "prompt_quantize_GB/s": round(prompt_bytes / (prompt_ms * 1e-3) / 1e9, 1),
+           "append_us_per_step": round(1e3 * sum(plain) / max(1, len(plain)), 2),
+           "blocks": len(blocks),
+           "block_quantize_us": round(1e3 * ms_blk, 2),
+           "block_GB/s": round(blk_bytes / (ms_blk * 1e-3) / 1e9, 1) if blocks else None,
+           "decode_us_per_step": round(1e3 * ms_dec, 2),
+           "decode_tokens/s": round(B / (ms_dec * 1e-3), 1),
+           "decode_GB/s": round(dec_gbs, 1),
+           "decode_pct_hbm_peak": round(100.0 * dec_gbs / HBM_PEAK_GBS, 2),
+           "ms_total": round(start.elapsed_time(end), 2)}
+    del cache, Kg, Vg, Qg
+    torch.cuda.empty_cache()
+    return res
 
 
 if __name__ == "__main__":
