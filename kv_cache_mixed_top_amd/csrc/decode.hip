@@ -230,6 +230,171 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
   }
 }
 
+// fp16 tail chunks next to the matrix-core pool kernel (query group of 4).
+// The tail holds fewer than `block` <= 1024 rows per (sequence, layer, KV
+// head), read once each for K and V: every thread keeps eight independent
+// 16-byte loads in flight per 128 rows, and the chunk's logits stay in LDS,
+// so the chunk costs a few memory latencies.  It writes the same partial
+// record (m, l, o[128]) per query head as the other decode kernels.
+constexpr int kTailGroup = 4;
+constexpr int kTailRows = 128;     // rows per pass over the chunk
+constexpr int kTailMax = 1024;     // rows per chunk, >= block
+
+__global__ __launch_bounds__(kThreads) void decode_tail_kernel(DecodeArgs a) {
+  __shared__ float qs[kTailGroup][kHeadDim];
+  __shared__ float z[kTailGroup][kTailMax];
+  __shared__ __attribute__((aligned(16))) float part[kThreads / 64][kTailGroup][kHeadDim];
+  __shared__ float red[kThreads / 64][2 * kTailGroup];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int x = a.x0 + blockIdx.x;
+  const int ch = x - a.nch[0] - a.nch[1];
+  const int64_t t0 = (int64_t)ch * a.chunk;
+  const int n = (int)(min(t0 + (int64_t)a.chunk, a.n_tail) - t0);
+  const int li = blockIdx.y / a.kv_heads;
+  const int g = blockIdx.y % a.kv_heads;
+  const int b = blockIdx.z;
+  const int layer = a.layer0 + li;
+  const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
+  const uint16_t* kt = a.tail_kv + (plane_k * a.block + t0) * kHeadDim;
+  const uint16_t* vt = a.tail_kv + ((plane_k + 1) * a.block + t0) * kHeadDim;
+
+  for (int i = tid; i < kTailGroup * kHeadDim; i += kThreads) {
+    const int h = i / kHeadDim, d = i - h * kHeadDim;
+    qs[h][d] = h2f(a.q[(((int64_t)b * a.nl + li) * a.q_heads + g * kTailGroup + h) * kHeadDim + d]);
+  }
+  __syncthreads();
+
+  // ---- logits: two threads per row, 64 dimensions each
+  {
+    const int rr = tid >> 1, half = tid & 1;
+    for (int r0 = 0; r0 < n; r0 += kTailRows) {
+      const int r = r0 + rr;
+      uint4 kv[8];
+      if (r < n) {
+        const uint4* src = reinterpret_cast<const uint4*>(kt + (int64_t)r * kHeadDim + 64 * half);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kv[i] = src[i];
+      }
+      float dot[kTailGroup] = {0.f, 0.f, 0.f, 0.f};
+      if (r < n) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t w4[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float xv = h2f((uint16_t)(w4[e >> 1] >> (16 * (e & 1))));
+            const int d = 64 * half + 8 * i + e;
+#pragma unroll
+            for (int h = 0; h < kTailGroup; ++h) dot[h] = fmaf(qs[h][d], xv, dot[h]);
+          }
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < kTailGroup; ++h) dot[h] += __shfl_xor(dot[h], 1, 64);
+      if (r < n && half == 0) {
+#pragma unroll
+        for (int h = 0; h < kTailGroup; ++h) z[h][r] = a.sm_scale * dot[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- softmax statistics per head: max, then p = exp(z - max) and the sum
+  float mx[kTailGroup], sum[kTailGroup];
+#pragma unroll
+  for (int h = 0; h < kTailGroup; ++h) {
+    float m = -INFINITY;
+    for (int r = tid; r < n; r += kThreads) m = fmaxf(m, z[h][r]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    mx[h] = m;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < kTailGroup; ++h) red[wave][h] = mx[h];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < kTailGroup; ++h) {
+    mx[h] = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
+    float sl = 0.f;
+    for (int r = tid; r < n; r += kThreads) {
+      const float pr = __expf(z[h][r] - mx[h]);
+      z[h][r] = pr;
+      sl += pr;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sl += __shfl_xor(sl, o, 64);
+    sum[h] = sl;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < kTailGroup; ++h) red[wave][kTailGroup + h] = sum[h];
+  }
+  __syncthreads();
+
+  // ---- values: 16 threads per row (8 dimensions each), 16 rows per pass
+  const int dg = tid & 15, rs = tid >> 4;
+  float acc[kTailGroup][8];
+#pragma unroll
+  for (int h = 0; h < kTailGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  for (int r0 = 0; r0 < n; r0 += kTailRows) {
+    uint4 vv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = r0 + rs + 16 * i;
+      if (r < n) vv[i] = reinterpret_cast<const uint4*>(vt + (int64_t)r * kHeadDim)[dg];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = r0 + rs + 16 * i;
+      if (r < n) {
+        const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+        for (int h = 0; h < kTailGroup; ++h) {
+          const float pr = z[h][r];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[h][e] = fmaf(pr, h2f((uint16_t)(w4[e >> 1] >> (16 * (e & 1)))), acc[h][e]);
+        }
+      }
+    }
+  }
+  // rows rs and rs + 4k of a wave share dimensions: reduce over the 4 row
+  // groups of the wave, then over the 4 waves through LDS
+#pragma unroll
+  for (int h = 0; h < kTailGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[h][e] += __shfl_xor(acc[h][e], 16, 64);
+      acc[h][e] += __shfl_xor(acc[h][e], 32, 64);
+    }
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < kTailGroup; ++h) {
+      float4* dst = reinterpret_cast<float4*>(&part[wave][h][8 * dg]);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  __syncthreads();
+
+  const int64_t u = ((((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x);
+  float* wsu = a.ws + u * kTailGroup * kPartialStride;
+  for (int i = tid; i < kTailGroup * kHeadDim; i += kThreads) {
+    const int h = i / kHeadDim, d = i - h * kHeadDim;
+    wsu[h * kPartialStride + 2 + d] = part[0][h][d] + part[1][h][d] + part[2][h][d] + part[3][h][d];
+  }
+  if (tid < kTailGroup) {
+    wsu[tid * kPartialStride + 0] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+    wsu[tid * kPartialStride + 1] = red[0][kTailGroup + tid] + red[1][kTailGroup + tid] +
+                                    red[2][kTailGroup + tid] + red[3][kTailGroup + tid];
+  }
+}
+
 // Log-sum-exp merge of the chunk partials of one (sequence, layer, query
 // head): the chunk maxima and sums are read in parallel, the weights
 // exp(m_c - M) go to LDS, then each thread combines one output dimension
@@ -317,7 +482,10 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
     hipError_t e = launch_decode_mfma(a, stream);
     if (e != hipSuccess) return e;
     g.x0 = a.nch[0] + a.nch[1];          // the fp16 tail chunks
-    return launch_decode_generic(g, a.nch[2], stream);
+    if (a.nch[2] <= 0) return hipSuccess;
+    dim3 grid(a.nch[2], a.nl * a.kv_heads, a.batch);
+    hipLaunchKernelGGL(decode_tail_kernel, grid, dim3(kThreads), 0, stream, g);
+    return hipGetLastError();
   }
   g.x0 = 0;
   return launch_decode_generic(g, a.nchunks, stream);

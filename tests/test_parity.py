@@ -242,7 +242,8 @@ def test_decode_partials_merge_equals_fused():
 
 # ------------------------------------------------------------------ generation
 
-@pytest.mark.parametrize("block,steps,r", [(128, 300, 0.25), (16, 53, 0.35), (128, 128, 0.5)])
+@pytest.mark.parametrize("block,steps,r", [(128, 300, 0.25), (16, 53, 0.35), (128, 128, 0.5),
+                                           (512, 300, 0.25)])
 def test_generation_block_exact(block, steps, r):
     _print("generation", block, steps, r)
     rng = np.random.default_rng(block + steps)
