@@ -213,6 +213,14 @@ constexpr int kCode8Bytes = kRows * kCode8Stride + 16;
 constexpr int kImgBytes = kRows * 43;             // largest packed tile (6 levels)
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The packed image is written once and not read back by this pass: its
+// stores are non-temporal.  (Non-temporal loads of the fp16 rows, which are
+// read in permuted order, measured slower.)
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+  __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
 
 // Smallest fp16 >= (hi - lo) / (L - 1) without a division: the fp32 quotient
 // is within 2^-22 of the exact one, so its nearest fp16 is the ceiling or
@@ -398,7 +406,8 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   // stay inside the plane and belong to no valid row yet)
   const int bytes = kvsel == 0 ? (nrows * R + 15) & ~15 : ((nrows + 15) >> 4) * 16 * R;
   uint4* dst = reinterpret_cast<uint4*>(a.codes[pool] + plane * a.cap[pool] * R + slot0 * R);
-  for (int i = tid; i < (bytes >> 4); i += kThreads) dst[i] = reinterpret_cast<const uint4*>(img)[i];
+  for (int i = tid; i < (bytes >> 4); i += kThreads)
+    store_stream(dst + i, reinterpret_cast<const uint4*>(img)[i]);
 }
 
 template <int LH, int LL>
