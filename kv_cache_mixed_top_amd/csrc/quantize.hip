@@ -306,18 +306,36 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   // a code whose y lies within 2^-22 ((L-1) + |m| r) of a half-integer is
   // settled exactly.  v_cvt_pk_u8_f32 rounds to nearest even and clamps to
   // [0, 255], which is the code elsewhere.
-  uint32_t cw[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float rs = 0.f, nb = 0.f, eps = 0.f, dmin = 1.0f;
+  //
+  // The fast pass computes y + 10 instead, which lies in [8, 16) where the
+  // fraction is the low 20 mantissa bits: the distance of the fraction from
+  // 1/2 is then one shift-and-add of the bits and an unsigned minimum, and
+  // the packed bytes are code + 10 (10 is even, so ties round alike).  Its
+  // error bound grows by the two roundings at that magnitude; the window
+  // below is twice the one above plus 2^-20.  The LDS code array keeps
+  // code + 10 (pads and constant rows too); the field sums take the offset
+  // back out in the dot product's accumulator.
+  constexpr uint32_t kTen = 0x0A0A0A0Au;
+  uint32_t cw[8] = {kTen, kTen, kTen, kTen, kTen, kTen, kTen, kTen};
+  float rs = 0.f, nb = 0.f, eps = 0.f;
+  bool near = false;
   if (s > 0.0f) {
     rs = __builtin_amdgcn_rcpf(s);
     nb = -lo * rs;
     eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
+    const float nb10 = fmaf(-lo, rs, 10.0f);
+    const float win = (2.0f * eps + 0x1p-20f) * 1048576.0f;    // in units of 2^-20
+    const bool wide = !(win < 131072.0f);                       // then every code is settled
+    const uint32_t E = wide ? 131072u : (uint32_t)win + 1u;
+    const uint32_t bias = (E - 0x80000u) << 12;   // (frac - 1/2 + E) mod 2^20, in the top bits
+    uint32_t umin = 0xFFFFFFFFu;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      const float yv = fmaf((float)v[k >> 1][k & 1], rs, nb);
-      dmin = fminf(dmin, fabsf(__builtin_amdgcn_fractf(yv) - 0.5f));
-      cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(yv, k & 3, cw[k >> 2]);
+      const float y = fmaf((float)v[k >> 1][k & 1], rs, nb10);
+      umin = min(umin, (__builtin_bit_cast(uint32_t, y) << 12) + bias);
+      cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(y, k & 3, cw[k >> 2]);
     }
+    near = wide || umin <= ((2u * E) << 12);
   }
   // dims 8q + 32i .. +8 -> row r of the LDS code array; lane 0 of the quad
   // clears the 8 pad bytes (fields read up to code 131)
@@ -325,7 +343,7 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<uint2*>(crow + 8 * q + 32 * i) = make_uint2(cw[2 * i], cw[2 * i + 1]);
-  if (dmin <= eps) {
+  if (near) {
     // Rare: a code of this lane lies near a half-integer.  The lane's values
     // are read again, 8 at a time, and every code is settled exactly, so
     // that this path holds few registers.
@@ -333,20 +351,20 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
     for (int i = 0; i < 4; ++i) {
       const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * q + 32 * i);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      uint32_t c8[2] = {0u, 0u};
+      uint32_t c8[2] = {0u, 0u};   // code + 10
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = h2f((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
         const float yv = fmaf(x, rs, nb);
         float c = rintf(yv);
         if (fabsf(__builtin_amdgcn_fractf(yv) - 0.5f) <= eps) c = exact_code(x, lo, s, c);
-        c8[e >> 2] |= (uint32_t)(int)c << (8 * (e & 3));
+        c8[e >> 2] |= (uint32_t)((int)c + 10) << (8 * (e & 3));
       }
       *reinterpret_cast<uint2*>(crow + 8 * q + 32 * i) = make_uint2(c8[0], c8[1]);
     }
   }
-  if (q == 0) *reinterpret_cast<uint2*>(crow + 128) = make_uint2(0u, 0u);
-  if (tid < 4) reinterpret_cast<uint32_t*>(codes8 + kRows * kCode8Stride)[tid] = 0u;
+  if (q == 0) *reinterpret_cast<uint2*>(crow + 128) = make_uint2(kTen, kTen);
+  if (tid < 4) reinterpret_cast<uint32_t*>(codes8 + kRows * kCode8Stride)[tid] = kTen;
 
   if (valid && q == 0) {
     const int64_t slot = slot0 + r;
@@ -364,32 +382,34 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   };
   if (L == 6) {
     constexpr uint32_t W = 0x00240601u;              // bytes {1, 6, 36, 0}
+    constexpr uint32_t Z = 0u - 10u * 43u;           // removes the +10 of three codes
     const int row = r;
 #pragma unroll
     for (int u = q; u < 11; u += 4) {                // fields 4u .. 4u+3 of this thread's row
       const uint32_t* c = reinterpret_cast<const uint32_t*>(codes8 + row * kCode8Stride + 12 * u);
       const uint32_t c0 = c[0], c1 = c[1], c2 = c[2];
-      put(row, 4 * u, __builtin_amdgcn_udot4(c0, W, 0u, false));
-      put(row, 4 * u + 1, __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c1, c0, 3), W, 0u, false));
-      put(row, 4 * u + 2, __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c2, c1, 2), W, 0u, false));
-      if (u < 10) put(row, 4 * u + 3, __builtin_amdgcn_udot4(c2 >> 8, W, 0u, false));
+      put(row, 4 * u, __builtin_amdgcn_udot4(c0, W, Z, false));
+      put(row, 4 * u + 1, __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c1, c0, 3), W, Z, false));
+      put(row, 4 * u + 2, __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c2, c1, 2), W, Z, false));
+      if (u < 10) put(row, 4 * u + 3, __builtin_amdgcn_udot4(c2 >> 8, W, Z, false));
     }
   } else {
     constexpr uint32_t W = 0x00190501u;              // bytes {1, 5, 25, 0}
+    constexpr uint32_t Z = 0u - 10u * 31u;           // removes the +10 of three codes
     const int row = r;
 #pragma unroll
     for (int u = q; u < 6; u += 4) {                 // fields 8u .. 8u+7 = bytes 7u .. 7u+6
       const uint32_t* c = reinterpret_cast<const uint32_t*>(codes8 + row * kCode8Stride + 24 * u);
       const uint32_t a0 = c[0], a1 = c[1], a2 = c[2], a3 = c[3], a4 = c[4], a5 = c[5];
       uint32_t f[8];
-      f[0] = __builtin_amdgcn_udot4(a0, W, 0u, false);
-      f[1] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a1, a0, 3), W, 0u, false);
-      f[2] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a2, a1, 2), W, 0u, false);
-      f[3] = __builtin_amdgcn_udot4(a2 >> 8, W, 0u, false);
-      f[4] = __builtin_amdgcn_udot4(a3, W, 0u, false);
-      f[5] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a4, a3, 3), W, 0u, false);
-      f[6] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a5, a4, 2), W, 0u, false);
-      f[7] = __builtin_amdgcn_udot4(a5 >> 8, W, 0u, false);
+      f[0] = __builtin_amdgcn_udot4(a0, W, Z, false);
+      f[1] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a1, a0, 3), W, Z, false);
+      f[2] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a2, a1, 2), W, Z, false);
+      f[3] = __builtin_amdgcn_udot4(a2 >> 8, W, Z, false);
+      f[4] = __builtin_amdgcn_udot4(a3, W, Z, false);
+      f[5] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a4, a3, 3), W, Z, false);
+      f[6] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a5, a4, 2), W, Z, false);
+      f[7] = __builtin_amdgcn_udot4(a5 >> 8, W, Z, false);
       if (u == 5) f[3] = f[4] = f[5] = f[6] = f[7] = 0u;   // fields 43.. do not exist
       const uint32_t lo32 = f[0] | (f[1] << 7) | (f[2] << 14) | (f[3] << 21) | (f[4] << 28);
       const uint32_t hi24 = (f[4] >> 4) | (f[5] << 3) | (f[6] << 10) | (f[7] << 17);
