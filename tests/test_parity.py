@@ -240,6 +240,42 @@ def test_decode_partials_merge_equals_fused():
     assert torch.equal(a, b)
 
 
+def test_decode_per_layer_graph_replay():
+    """Per-layer partials + merge captured once in a HIP graph: every replay,
+    with eager work and synchronisation between replays and a new query
+    copied into the captured buffer, equals the same calls issued eagerly."""
+    _print("decode per-layer graph")
+    rng = np.random.default_rng(17)
+    B, layers, kv, n = 1, 3, 2, 700
+    K, V = _kv(rng, B, layers, kv, n)
+    s = rng.random((B, n)).astype(np.float32)
+    cache, op = _quantize_case(K, V, s, 0.5, 6, 5, "graph")
+    qs = [(rng.standard_normal((B, layers, 8, 128)) / 11.3).astype(np.float16) for _ in range(3)]
+    qbuf = to_dev(qs[0])
+    out_g = torch.empty((B, layers, 8, 128), dtype=torch.float32, device="cuda")
+    out_e = torch.empty_like(out_g)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def per_layer(out, stream):
+        for layer in range(layers):
+            sk.semkv_decode_partials(cache, qbuf[:, layer:layer + 1], layer0=layer, stream=stream)
+            sk.semkv_decode_merge(cache, out[:, layer:layer + 1], stream=stream)
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        per_layer(out_g, side)
+    for i, q in enumerate(qs + qs[:1]):
+        qbuf.copy_(to_dev(q))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        per_layer(out_e, None)                       # eager, on the default stream
+        sk.semkv_sync_check()
+        assert torch.equal(out_g, out_e), f"replay {i}"
+        assert_attention_close(out_g.cpu().numpy(), O.decode_attention(q, op, 1.0), f"replay {i}")
+
+
 # ------------------------------------------------------------------ generation
 
 @pytest.mark.parametrize("block,steps,r", [(128, 300, 0.25), (16, 53, 0.35), (128, 128, 0.5),
