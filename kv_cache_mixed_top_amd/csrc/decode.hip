@@ -399,25 +399,33 @@ __global__ __launch_bounds__(kThreads) void decode_tail_kernel(DecodeArgs a) {
 // head): the chunk maxima and sums are read in parallel, the weights
 // exp(m_c - M) go to LDS, then each thread combines one output dimension
 // with an unrolled loop over the chunks.
-__global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
+constexpr int kMergeParts = 4;                      // chunk groups per workgroup
+constexpr int kMergeThreads = kMergeParts * kHeadDim;
+
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
   extern __shared__ float wch[];           // nchunks weights
-  __shared__ float red[2];
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float part[kMergeParts][kHeadDim];
   const int h = blockIdx.x, li = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
   const int g = h / G, hl = h - g * G;
-  const int d = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int d = tid & (kHeadDim - 1), pi = tid / kHeadDim;
   const int64_t u0 = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks;
   const float* ws = a.ws;
   const int nc = a.nchunks;
+  constexpr int kWaves = kMergeThreads / 64;
   float M = -INFINITY;
-  for (int c = d; c < nc; c += kHeadDim) M = fmaxf(M, ws[((u0 + c) * G + hl) * kPartialStride]);
+  for (int c = tid; c < nc; c += kMergeThreads) M = fmaxf(M, ws[((u0 + c) * G + hl) * kPartialStride]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if ((d & 63) == 0) red[d >> 6] = M;
+  if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
-  M = fmaxf(red[0], red[1]);
+  M = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red[w]);
   float den = 0.f;
-  for (int c = d; c < nc; c += kHeadDim) {
+  for (int c = tid; c < nc; c += kMergeThreads) {
     const float* p = ws + ((u0 + c) * G + hl) * kPartialStride;
     const float w = __expf(p[0] - M);
     wch[c] = w;
@@ -426,23 +434,32 @@ __global__ __launch_bounds__(kHeadDim) void decode_merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
   __syncthreads();
-  if ((d & 63) == 0) red[d >> 6] = den;
+  if ((tid & 63) == 0) red[tid >> 6] = den;
   __syncthreads();
-  den = red[0] + red[1];
+  den = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) den += red[w];
+  // chunks pi, pi + 4, ... of this dimension, eight loads in flight
   float num = 0.f;
   const float* pd = ws + (u0 * G + hl) * kPartialStride + 2 + d;
   const int64_t step = (int64_t)G * kPartialStride;
-  int c = 0;
-  for (; c + 4 <= nc; c += 4) {
-    const float v0 = pd[(c + 0) * step], v1 = pd[(c + 1) * step];
-    const float v2 = pd[(c + 2) * step], v3 = pd[(c + 3) * step];
-    num = fmaf(wch[c], v0, num);
-    num = fmaf(wch[c + 1], v1, num);
-    num = fmaf(wch[c + 2], v2, num);
-    num = fmaf(wch[c + 3], v3, num);
+  int c = pi;
+  for (; c + 7 * kMergeParts < nc; c += 8 * kMergeParts) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = pd[(int64_t)(c + e * kMergeParts) * step];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) num = fmaf(wch[c + e * kMergeParts], v[e], num);
   }
-  for (; c < nc; ++c) num = fmaf(wch[c], pd[c * step], num);
-  a.out[(((int64_t)b * a.nl + li) * a.q_heads + h) * kHeadDim + d] = num / den;
+  for (; c < nc; c += kMergeParts) num = fmaf(wch[c], pd[(int64_t)c * step], num);
+  part[pi][d] = num;
+  __syncthreads();
+  if (pi == 0) {
+    num = part[0][d];
+#pragma unroll
+    for (int k = 1; k < kMergeParts; ++k) num += part[k][d];
+    a.out[(((int64_t)b * a.nl + li) * a.q_heads + h) * kHeadDim + d] = num / den;
+  }
 }
 
 }  // namespace
@@ -493,7 +510,7 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.q_heads, a.nl, a.batch);
-  hipLaunchKernelGGL(decode_merge_kernel, grid, dim3(kHeadDim), a.nchunks * sizeof(float),
+  hipLaunchKernelGGL(decode_merge_kernel, grid, dim3(kMergeThreads), a.nchunks * sizeof(float),
                      stream, a);
   return hipGetLastError();
 }
