@@ -317,25 +317,25 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   // back out in the dot product's accumulator.
   constexpr uint32_t kTen = 0x0A0A0A0Au;
   uint32_t cw[8] = {kTen, kTen, kTen, kTen, kTen, kTen, kTen, kTen};
-  float rs = 0.f, nb = 0.f, eps = 0.f;
-  bool near = false;
+  float rs = 0.f, nb10 = 0.f;
+  bool wide = false;
+  uint32_t bias = 0u, thr = 0u;
+  uint32_t umin[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};   // per 8 values
   if (s > 0.0f) {
     rs = __builtin_amdgcn_rcpf(s);
-    nb = -lo * rs;
-    eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
-    const float nb10 = fmaf(-lo, rs, 10.0f);
+    const float eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
+    nb10 = fmaf(-lo, rs, 10.0f);
     const float win = (2.0f * eps + 0x1p-20f) * 1048576.0f;    // in units of 2^-20
-    const bool wide = !(win < 131072.0f);                       // then every code is settled
+    wide = !(win < 131072.0f);                                  // then every code is settled
     const uint32_t E = wide ? 131072u : (uint32_t)win + 1u;
-    const uint32_t bias = (E - 0x80000u) << 12;   // (frac - 1/2 + E) mod 2^20, in the top bits
-    uint32_t umin = 0xFFFFFFFFu;
+    bias = (E - 0x80000u) << 12;   // (frac - 1/2 + E) mod 2^20, in the top bits
+    thr = (2u * E) << 12;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       const float y = fmaf((float)v[k >> 1][k & 1], rs, nb10);
-      umin = min(umin, (__builtin_bit_cast(uint32_t, y) << 12) + bias);
+      umin[k >> 3] = min(umin[k >> 3], (__builtin_bit_cast(uint32_t, y) << 12) + bias);
       cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(y, k & 3, cw[k >> 2]);
     }
-    near = wide || umin <= ((2u * E) << 12);
   }
   // dims 8q + 32i .. +8 -> row r of the LDS code array; lane 0 of the quad
   // clears the 8 pad bytes (fields read up to code 131)
@@ -343,24 +343,28 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     *reinterpret_cast<uint2*>(crow + 8 * q + 32 * i) = make_uint2(cw[2 * i], cw[2 * i + 1]);
-  if (near) {
-    // Rare: a code of this lane lies near a half-integer.  The lane's values
-    // are read again, 8 at a time, and every code is settled exactly, so
-    // that this path holds few registers.
+  uint32_t flag = 0u;   // groups of 8 values with a value near a half-integer
+#pragma unroll
+  for (int i = 0; i < 4; ++i) flag |= (uint32_t)(s > 0.0f && (wide || umin[i] <= thr)) << i;
+  if (flag) {
+    // Rare per group: one of its values lies near a half-integer (with fp16
+    // data nearly always an exact tie).  The group's 8 values are read
+    // again, and those near a half-integer are settled exactly and their
+    // code bytes rewritten; the loop holds few registers.
 #pragma unroll 1
     for (int i = 0; i < 4; ++i) {
+      if (!((flag >> i) & 1u)) continue;
       const uint4 w = *reinterpret_cast<const uint4*>(src + 8 * q + 32 * i);
       const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      uint32_t c8[2] = {0u, 0u};   // code + 10
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = h2f((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
-        const float yv = fmaf(x, rs, nb);
-        float c = rintf(yv);
-        if (fabsf(__builtin_amdgcn_fractf(yv) - 0.5f) <= eps) c = exact_code(x, lo, s, c);
-        c8[e >> 2] |= (uint32_t)((int)c + 10) << (8 * (e & 3));
+        const float y = fmaf(x, rs, nb10);
+        if (wide || (__builtin_bit_cast(uint32_t, y) << 12) + bias <= thr) {
+          const float c = exact_code(x, lo, s, rintf(y - 10.0f));
+          crow[8 * q + 32 * i + e] = (uint8_t)((int)c + 10);
+        }
       }
-      *reinterpret_cast<uint2*>(crow + 8 * q + 32 * i) = make_uint2(c8[0], c8[1]);
     }
   }
   if (q == 0) *reinterpret_cast<uint2*>(crow + 128) = make_uint2(kTen, kTen);
