@@ -399,13 +399,15 @@ __global__ __launch_bounds__(kThreads) void decode_tail_kernel(DecodeArgs a) {
 // head): the chunk maxima and sums are read in parallel, the weights
 // exp(m_c - M) go to LDS, then each thread combines one output dimension
 // with an unrolled loop over the chunks.
-constexpr int kMergeParts = 4;                      // chunk groups per workgroup
-constexpr int kMergeThreads = kMergeParts * kHeadDim;
-
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs a) {
+// P chunk groups per workgroup: 4 when a head has many chunks (short
+// per-layer launches), 1 otherwise.
+template <int P>
+__global__ __launch_bounds__(P * kHeadDim) void decode_merge_kernel(DecodeArgs a) {
+  constexpr int kMergeParts = P;
+  constexpr int kMergeThreads = P * kHeadDim;
   extern __shared__ float wch[];           // nchunks weights
   __shared__ float red[kMergeThreads / 64];
-  __shared__ float part[kMergeParts][kHeadDim];
+  __shared__ float part[P][kHeadDim];
   const int h = blockIdx.x, li = blockIdx.y, b = blockIdx.z;
   const int G = a.group;
   const int g = h / G, hl = h - g * G;
@@ -439,7 +441,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
   den = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) den += red[w];
-  // chunks pi, pi + 4, ... of this dimension, eight loads in flight
+  // chunks pi, pi + P, ... of this dimension, eight loads in flight
   float num = 0.f;
   const float* pd = ws + (u0 * G + hl) * kPartialStride + 2 + d;
   const int64_t step = (int64_t)G * kPartialStride;
@@ -510,8 +512,12 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.q_heads, a.nl, a.batch);
-  hipLaunchKernelGGL(decode_merge_kernel, grid, dim3(kMergeThreads), a.nchunks * sizeof(float),
-                     stream, a);
+  if (a.nchunks > 32)
+    hipLaunchKernelGGL(decode_merge_kernel<4>, grid, dim3(4 * kHeadDim), a.nchunks * sizeof(float),
+                       stream, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<1>, grid, dim3(kHeadDim), a.nchunks * sizeof(float),
+                       stream, a);
   return hipGetLastError();
 }
 
