@@ -158,11 +158,14 @@ __device__ __forceinline__ void qk6(const uint32_t (&d)[12], const h4 (&qf)[3], 
 // ---- 5 levels: one K row = 38 bytes; 7-byte units hold 8 fields of 7 bits.
 // From a word W with fields at bits 0, 7, 14, 21: slots (F0, F2) and (F1, F3).
 // `bias` is 0x66006600 held in a register, so that each mask and OR is one
-// AND-OR.
+// AND-OR.  The 16-bit halves (W[0:15], W[14:29]) hold F0 and F2 in their low
+// 7 bits, and F1 and F3 seven bits higher.
 __device__ __forceinline__ void field_pairs(uint32_t W, uint32_t& pa, uint32_t& pb,
                                             uint32_t bias) {
-  pa = (((W << 2) & 0x7F0000u) | ((W & 0x7Fu) | bias));
-  pb = (((W >> 5) & 0x7F0000u) | (((W >> 7) & 0x7Fu) | bias));
+  const uint32_t h = perm(W >> 14, W, 0x05040100u);
+  pa = (h & 0x007F007Fu) | bias;                                       // (F0, F2)
+  const u16x2 seven = {7, 7};
+  pb = (u32(v2(h) >> seven) & 0x007F007Fu) | bias;                     // (F1, F3)
 }
 // 0x66006600 in a vector register (the compiler cannot fold it back into a
 // literal, which these instructions cannot take together with a mask).
