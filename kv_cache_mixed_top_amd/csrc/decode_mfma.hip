@@ -628,7 +628,8 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   const int lane = threadIdx.x & 63;
   const int layer = a.layer0 + li;
   const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
-  const int64_t cap = a.cap[seg];
+  const int cap = (int)a.cap[seg];            // cap * R < 2^31 (checked by the launcher)
+  const int ir0 = (int)r0, ir1 = (int)r1;
   const uint8_t* kcodes = a.codes[seg] + plane_k * cap * R;
   const uint32_t* kmg = a.meta[seg] + plane_k * cap;
   const float sm = a.sm_scale * kLog2e;   // logits in log2 units
@@ -666,7 +667,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   // uniform base (the bytes past the tile are not used).
   uint32_t km_next = 0;
   const uint32_t lane16 = 16u * (uint32_t)lane;
-  auto issue = [&](int buf, int64_t t0, int nt) {
+  auto issue = [&](int buf, int t0, int nt) {
     const uint8_t* ks = kcodes + t0 * R;
     if (nt == kTile && t0 + kFullRead <= cap) {
 #pragma unroll
@@ -688,12 +689,12 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   float frame[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   // One tile in staging buffer B (a compile-time constant, so that reads of
   // buffer B are known not to overlap the loads in flight into 1 - B).
-  auto tile = [&](int64_t t0, auto Bc) {
+  auto tile = [&](int t0, auto Bc) {
     constexpr int B = decltype(Bc)::value;
-    const int nt = (int)min((int64_t)kTile, r1 - t0);
+    const int nt = min(kTile, ir1 - t0);
     wait_vm0();   // this tile's rows have landed
     const uint32_t km = km_next;
-    if (t0 + kTile < r1) issue(1 - B, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
+    if (t0 + kTile < ir1) issue(1 - B, t0 + kTile, min(kTile, ir1 - t0 - kTile));
     f4 sacc[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) sacc[k] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -736,10 +737,10 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     wait_lgkm0();  // logits written
     tile_barrier();
   };
-  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
-  for (int64_t t0 = r0; t0 < r1; t0 += 2 * kTile) {   // same tile sequence as wave 1
+  if (ir0 < ir1) issue(0, ir0, min(kTile, ir1 - ir0));
+  for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 1
     tile(t0, std::integral_constant<int, 0>{});
-    if (t0 + kTile < r1) tile(t0 + kTile, std::integral_constant<int, 1>{});
+    if (t0 + kTile < ir1) tile(t0 + kTile, std::integral_constant<int, 1>{});
   }
 }
 
@@ -751,7 +752,8 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   _Float16* wbuf = st.w;
   const int layer = a.layer0 + li;
   const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
-  const int64_t cap = a.cap[seg];
+  const int cap = (int)a.cap[seg];            // cap * R < 2^31 (checked by the launcher)
+  const int ir0 = (int)r0, ir1 = (int)r1;
   const uint8_t* vcodes = a.codes[seg] + (plane_k + 1) * cap * R;
   const uint32_t* vmg = a.meta[seg] + (plane_k + 1) * cap;
 
@@ -778,7 +780,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   // the lane's V meta word -> register
   uint32_t vm_next = 0;
   const uint32_t lane16 = 16u * (uint32_t)lane;
-  auto issue = [&](int buf, int64_t t0, int nt) {
+  auto issue = [&](int buf, int t0, int nt) {
     const uint8_t* vs = vcodes + t0 * R;
     if (nt == kTile && t0 + kFullRead <= cap) {
 #pragma unroll
@@ -805,12 +807,12 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   // One tile in staging buffer B (a compile-time constant, so that reads of
   // buffer B are known not to overlap the loads in flight into 1 - B: the
   // next tile's loads go out first and the V bytes are read where used).
-  auto tile = [&](int64_t t0, auto Bc) {
+  auto tile = [&](int t0, auto Bc) {
     constexpr int B = decltype(Bc)::value;
-    const int nt = (int)min((int64_t)kTile, r1 - t0);
+    const int nt = min(kTile, ir1 - t0);
     wait_vm0();   // this tile's V has landed
     const uint32_t vm = vm_next;
-    if (t0 + kTile < r1) issue(1 - B, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
+    if (t0 + kTile < ir1) issue(1 - B, t0 + kTile, min(kTile, ir1 - t0 - kTile));
     tile_barrier();                                      // logits of this tile are in LDS
     float z[4];
 #pragma unroll
@@ -897,10 +899,10 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
       }
     }
   };
-  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
-  for (int64_t t0 = r0; t0 < r1; t0 += 2 * kTile) {   // same tile sequence as wave 0
+  if (ir0 < ir1) issue(0, ir0, min(kTile, ir1 - ir0));
+  for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 0
     tile(t0, std::integral_constant<int, 0>{});
-    if (t0 + kTile < r1) tile(t0 + kTile, std::integral_constant<int, 1>{});
+    if (t0 + kTile < ir1) tile(t0 + kTile, std::integral_constant<int, 1>{});
   }
   write_partial<L>(a, u, lane, E, acc, mref, lsum, msum, kLn2);
 }
@@ -989,8 +991,10 @@ int64_t decode_mfma_resident_waves() {
 
 bool decode_mfma_supported(const DecodeArgs& a) {
   if (a.group != 4) return false;
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < 2; ++s) {
     if (a.rows[s] > 0 && a.fmt[s].L != 5 && a.fmt[s].L != 6) return false;
+    if (a.cap[s] * 43 >= ((int64_t)1 << 31)) return false;   // 32-bit row offsets in the kernels
+  }
   return true;
 }
 
