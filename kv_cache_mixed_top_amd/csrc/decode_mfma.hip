@@ -719,11 +719,13 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     const float kbias = sm * h2f((uint16_t)(km >> 16));
     float z[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float zf = fmaf(kfac, sacc[0][h], kbias * sumq[h]);   // one accumulator chain
-      z[h] = (nt == kTile || lane < nt) ? zf : -INFINITY;
-      st.z(B)[h * kTile + lane] = z[h];
+    for (int h = 0; h < 4; ++h) z[h] = fmaf(kfac, sacc[0][h], kbias * sumq[h]);   // one accumulator chain
+    if (nt < kTile) {                          // rows past the chunk end take no weight
+#pragma unroll
+      for (int h = 0; h < 4; ++h) z[h] = lane < nt ? z[h] : -INFINITY;
     }
+#pragma unroll
+    for (int h = 0; h < 4; ++h) st.z(B)[h * kTile + lane] = z[h];
     // softmax frame per head, kFrameMargin above the running maximum; it is
     // raised only when a logit exceeds it (in practice on the first tile)
     const bool up = z[0] > frame[0] || z[1] > frame[1] || z[2] > frame[2] || z[3] > frame[3];
