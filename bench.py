@@ -264,6 +264,7 @@ def main():
         result["cpu_baseline"] = {
             "value": round(step_bytes / cpu_step_s / 1e9, 4),
             "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_baseline.cpu_model(),
             "sample": (f"oracle rank of 1 sequence, quantize+pack of {ls} of {layers} layers "
                        f"(sequence 0) and one decode step over those layers, in {workers} worker "
                        f"processes; measured rank {t_rank:.2f}s, quantize {tq:.2f}s, decode "

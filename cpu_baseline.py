@@ -38,6 +38,19 @@ def _decode_head(args):
     return np.stack([O.attention(q[h].astype(np.float64), keys, vals, sm) for h in range(q.shape[0])])
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (or the platform string)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def time_oracle(K, V, perm, k, Lh, Ll, q, sm, workers=None):
     """K, V fp16 [layers_s][kv][n][128] (the sample); perm int32 [n]; q fp16
     [layers_s][Hq][128].  Returns (quantize seconds, decode seconds, workers)."""
