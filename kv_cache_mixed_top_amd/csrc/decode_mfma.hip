@@ -240,20 +240,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 }
 
 // Largest V scale (the low half of the meta word) over rows [r0, r1), as
-// fp16 bits, in every lane.  Sixteen independent loads per lane are in
-// flight at a time, so a chunk costs a few memory latencies, not one per
-// 64 rows.
+// fp16 bits, in every lane.  r0 is a multiple of 4 and the meta plane is
+// 16-byte aligned, so the rows are read four to a 16-byte load, sixteen loads
+// per lane in flight: a chunk of up to 4096 rows costs one memory latency.
 __device__ __forceinline__ uint32_t chunk_scale_max(const uint32_t* vmg, int64_t r0, int64_t r1,
                                                     int lane) {
   constexpr int kDepth = 16;
   uint32_t smax = 0;
-  for (int64_t r = r0 + lane; r < r1; r += 64 * kDepth) {
-    uint32_t v[kDepth];
+  const int64_t n4 = (r1 - r0) >> 2;
+  const uint4* g4 = reinterpret_cast<const uint4*>(vmg + r0);
+  for (int64_t i = lane; i < n4; i += 64 * kDepth) {
+    uint4 v[kDepth];
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) v[i] = vmg[min(r + 64 * i, r1 - 1)];   // repeats are harmless
+    for (int k = 0; k < kDepth; ++k) v[k] = g4[min(i + 64 * k, n4 - 1)];   // repeats are harmless
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) smax = max(smax, v[i] & 0xFFFFu);
+    for (int k = 0; k < kDepth; ++k)
+      smax = max(smax, max(max(v[k].x & 0xFFFFu, v[k].y & 0xFFFFu), max(v[k].z & 0xFFFFu, v[k].w & 0xFFFFu)));
   }
+  const int64_t rr = r0 + 4 * n4 + lane;           // the last (r1 - r0) % 4 rows
+  if (rr < r1) smax = max(smax, vmg[rr] & 0xFFFFu);
   return wave_max_u32(smax);
 }
 
@@ -635,31 +640,10 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   const float sm = a.sm_scale * kLog2e;   // logits in log2 units
   const uint32_t bias5 = L == 5 ? bias_register() : 0u;   // 5-level field bias
 
-  // queries: ABID-packed 4x4x4 A fragments and per-head sums
-  const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
-                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
+  // queries: ABID-packed 4x4x4 A fragments and per-head sums (loaded once
+  // the first K tile is in flight)
   h4 qf[3];
-  {
-    const int head = lane & 3, blk = lane >> 2;
-#pragma unroll
-    for (int P = 0; P < 3; ++P) {
-      const int s = 16 * P + blk;
-      h4 v = {0, 0, 0, 0};
-      if (s < kQkInstr) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = qk_slot_dim<L>(s, i);
-          v[i] = d >= 0 ? qg[head * kHeadDim + d] : (_Float16)0.0f;
-        }
-      }
-      qf[P] = v;
-    }
-  }
   float sumq[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h)
-    sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
-
   // K rows [t0, t0 + nt) -> buffer `buf` (16 bytes per lane per instruction;
   // chunks past the valid range re-read the last valid chunk); the lane's K
   // meta word -> register
@@ -740,6 +724,28 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     tile_barrier();
   };
   if (ir0 < ir1) issue(0, ir0, min(kTile, ir1 - ir0));
+  const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
+                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
+  {
+    const int head = lane & 3, blk = lane >> 2;
+#pragma unroll
+    for (int P = 0; P < 3; ++P) {
+      const int s = 16 * P + blk;
+      h4 v = {0, 0, 0, 0};
+      if (s < kQkInstr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = qk_slot_dim<L>(s, i);
+          v[i] = d >= 0 ? qg[head * kHeadDim + d] : (_Float16)0.0f;
+        }
+      }
+      qf[P] = v;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
+
   for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 1
     tile(t0, std::integral_constant<int, 0>{});
     if (t0 + kTile < ir1) tile(t0 + kTile, std::integral_constant<int, 1>{});
@@ -759,11 +765,10 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   const uint8_t* vcodes = a.codes[seg] + (plane_k + 1) * cap * R;
   const uint32_t* vmg = a.meta[seg] + (plane_k + 1) * cap;
 
-  // per-chunk exponent E: w = p * scale_V * 2^E stays below 2^14
-  const uint32_t smax = chunk_scale_max(vmg, r0, r1, lane);
+  // per-chunk exponent E: w = p * scale_V * 2^E stays below 2^14 (set
+  // below, once the first V tile is in flight)
   int E = 0;
-  if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
-  const float two_e = ldexpf(1.0f, E);
+  float two_e = 1.0f;
 
   float mref[4], lsum[4], msum[4];
 #pragma unroll
@@ -902,6 +907,11 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
     }
   };
   if (ir0 < ir1) issue(0, ir0, min(kTile, ir1 - ir0));
+  {
+    const uint32_t smax = chunk_scale_max(vmg, r0, r1, lane);
+    if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
+    two_e = ldexpf(1.0f, E);
+  }
   for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 0
     tile(t0, std::integral_constant<int, 0>{});
     if (t0 + kTile < ir1) tile(t0 + kTile, std::integral_constant<int, 1>{});
