@@ -453,7 +453,18 @@ __global__ __launch_bounds__(P * kHeadDim) void decode_merge_kernel(DecodeArgs a
 #pragma unroll
     for (int e = 0; e < 8; ++e) num = fmaf(wch[c + e * kMergeParts], v[e], num);
   }
+  for (; c + 3 * kMergeParts < nc; c += 4 * kMergeParts) {
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = pd[(int64_t)(c + e * kMergeParts) * step];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num = fmaf(wch[c + e * kMergeParts], v[e], num);
+  }
   for (; c < nc; c += kMergeParts) num = fmaf(wch[c], pd[(int64_t)c * step], num);
+  if (P == 1) {
+    a.out[(((int64_t)b * a.nl + li) * a.q_heads + h) * kHeadDim + d] = num / den;
+    return;
+  }
   part[pi][d] = num;
   __syncthreads();
   if (pi == 0) {
@@ -512,12 +523,13 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(a.q_heads, a.nl, a.batch);
-  if (a.nchunks > 32)
+  if (a.nchunks > 32) {
     hipLaunchKernelGGL(decode_merge_kernel<4>, grid, dim3(4 * kHeadDim), a.nchunks * sizeof(float),
                        stream, a);
-  else
+  } else {
     hipLaunchKernelGGL(decode_merge_kernel<1>, grid, dim3(kHeadDim), a.nchunks * sizeof(float),
                        stream, a);
+  }
   return hipGetLastError();
 }
 
