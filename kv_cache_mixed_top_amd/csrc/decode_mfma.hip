@@ -610,19 +610,20 @@ struct Stage2 {
 // One workgroup barrier with no memory fence: the LDS writes before it are
 // waited for by the caller; outstanding global->LDS prefetches stay in flight.
 __device__ __forceinline__ void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
-// s_waitcnt through the builtin (not inline asm), so that the compiler's own
-// wait insertion knows what has completed; the encodings are those of the
-// CDNA s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt in 6:4,
-// lgkmcnt in 11:8).
 // 16-byte LDS read that also waits for it (and every LDS access before it)
 // inside the same asm block, so that the result register is written when
-// the block ends.
+// the block ends.  Used where the compiler cannot tell the read apart from
+// global->LDS loads in flight into other buffers and would wait for those.
 __device__ __forceinline__ h8 lds_read_h8_wait(const _Float16* p) {
   h8 r;
   const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) _Float16*)p;
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a) : "memory");
   return r;
 }
+// s_waitcnt through the builtin (not inline asm), so that the compiler's own
+// wait insertion knows what has completed; the encodings are those of the
+// CDNA s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt in 6:4,
+// lgkmcnt in 11:8).
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
