@@ -18,6 +18,8 @@
 // in 16-row tiles (the layout the decode kernel reads 8 tokens' byte from).
 // Bytes of a dword shared with rows of another workgroup are stored one by
 // one.
+#include <type_traits>
+
 #include "semkv_internal.h"
 
 namespace semkv {
@@ -379,50 +381,56 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   __syncthreads();
 
   // ---- fields (sum_i code[3j+i] L^i, one udot4 each) -> the tile's byte
-  // image: K rows back to back, V byte-planar in 16-row tiles
-  auto put = [&](int row, int j, uint32_t byte) {
-    const int at = kvsel == 0 ? row * R + j : (row >> 4) * 16 * R + 16 * j + (row & 15);
-    img[at] = (uint8_t)byte;
+  // image: K rows back to back, V byte-planar in 16-row tiles.  The layout
+  // is uniform per workgroup, so each is its own code path: byte j of this
+  // thread's row lands at rowimg + j * kStep.
+  auto pack = [&](auto planar_c) {
+    constexpr bool kPlanar = decltype(planar_c)::value;
+    constexpr int kStep = kPlanar ? 16 : 1;
+    uint8_t* rowimg = kPlanar ? img + (r >> 4) * 16 * R + (r & 15) : img + r * R;
+    const uint8_t* crow8 = codes8 + r * kCode8Stride;
+    if (L == 6) {
+      constexpr uint32_t W = 0x00240601u;              // bytes {1, 6, 36, 0}
+      constexpr uint32_t Z = 0u - 10u * 43u;           // removes the +10 of three codes
+#pragma unroll
+      for (int u = q; u < 11; u += 4) {                // fields 4u .. 4u+3 of this thread's row
+        const uint32_t* c = reinterpret_cast<const uint32_t*>(crow8 + 12 * u);
+        const uint32_t c0 = c[0], c1 = c[1], c2 = c[2];
+        uint8_t* o = rowimg + 4 * u * kStep;
+        o[0] = (uint8_t)__builtin_amdgcn_udot4(c0, W, Z, false);
+        o[kStep] = (uint8_t)__builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c1, c0, 3), W, Z, false);
+        o[2 * kStep] = (uint8_t)__builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c2, c1, 2), W, Z, false);
+        if (u < 10) o[3 * kStep] = (uint8_t)__builtin_amdgcn_udot4(c2 >> 8, W, Z, false);
+      }
+    } else {
+      constexpr uint32_t W = 0x00190501u;              // bytes {1, 5, 25, 0}
+      constexpr uint32_t Z = 0u - 10u * 31u;           // removes the +10 of three codes
+#pragma unroll
+      for (int u = q; u < 6; u += 4) {                 // fields 8u .. 8u+7 = bytes 7u .. 7u+6
+        const uint32_t* c = reinterpret_cast<const uint32_t*>(crow8 + 24 * u);
+        const uint32_t a0 = c[0], a1 = c[1], a2 = c[2], a3 = c[3], a4 = c[4], a5 = c[5];
+        uint32_t f[8];
+        f[0] = __builtin_amdgcn_udot4(a0, W, Z, false);
+        f[1] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a1, a0, 3), W, Z, false);
+        f[2] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a2, a1, 2), W, Z, false);
+        f[3] = __builtin_amdgcn_udot4(a2 >> 8, W, Z, false);
+        f[4] = __builtin_amdgcn_udot4(a3, W, Z, false);
+        f[5] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a4, a3, 3), W, Z, false);
+        f[6] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a5, a4, 2), W, Z, false);
+        f[7] = __builtin_amdgcn_udot4(a5 >> 8, W, Z, false);
+        if (u == 5) f[3] = f[4] = f[5] = f[6] = f[7] = 0u;   // fields 43.. do not exist
+        const uint32_t lo32 = f[0] | (f[1] << 7) | (f[2] << 14) | (f[3] << 21) | (f[4] << 28);
+        const uint32_t hi24 = (f[4] >> 4) | (f[5] << 3) | (f[6] << 10) | (f[7] << 17);
+        const int nb = u == 5 ? 3 : 7;
+        uint8_t* o = rowimg + 7 * u * kStep;
+#pragma unroll
+        for (int e = 0; e < 7; ++e)
+          if (e < nb) o[e * kStep] = (uint8_t)(e < 4 ? lo32 >> (8 * e) : hi24 >> (8 * (e - 4)));
+      }
+    }
   };
-  if (L == 6) {
-    constexpr uint32_t W = 0x00240601u;              // bytes {1, 6, 36, 0}
-    constexpr uint32_t Z = 0u - 10u * 43u;           // removes the +10 of three codes
-    const int row = r;
-#pragma unroll
-    for (int u = q; u < 11; u += 4) {                // fields 4u .. 4u+3 of this thread's row
-      const uint32_t* c = reinterpret_cast<const uint32_t*>(codes8 + row * kCode8Stride + 12 * u);
-      const uint32_t c0 = c[0], c1 = c[1], c2 = c[2];
-      put(row, 4 * u, __builtin_amdgcn_udot4(c0, W, Z, false));
-      put(row, 4 * u + 1, __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c1, c0, 3), W, Z, false));
-      put(row, 4 * u + 2, __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c2, c1, 2), W, Z, false));
-      if (u < 10) put(row, 4 * u + 3, __builtin_amdgcn_udot4(c2 >> 8, W, Z, false));
-    }
-  } else {
-    constexpr uint32_t W = 0x00190501u;              // bytes {1, 5, 25, 0}
-    constexpr uint32_t Z = 0u - 10u * 31u;           // removes the +10 of three codes
-    const int row = r;
-#pragma unroll
-    for (int u = q; u < 6; u += 4) {                 // fields 8u .. 8u+7 = bytes 7u .. 7u+6
-      const uint32_t* c = reinterpret_cast<const uint32_t*>(codes8 + row * kCode8Stride + 24 * u);
-      const uint32_t a0 = c[0], a1 = c[1], a2 = c[2], a3 = c[3], a4 = c[4], a5 = c[5];
-      uint32_t f[8];
-      f[0] = __builtin_amdgcn_udot4(a0, W, Z, false);
-      f[1] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a1, a0, 3), W, Z, false);
-      f[2] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a2, a1, 2), W, Z, false);
-      f[3] = __builtin_amdgcn_udot4(a2 >> 8, W, Z, false);
-      f[4] = __builtin_amdgcn_udot4(a3, W, Z, false);
-      f[5] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a4, a3, 3), W, Z, false);
-      f[6] = __builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(a5, a4, 2), W, Z, false);
-      f[7] = __builtin_amdgcn_udot4(a5 >> 8, W, Z, false);
-      if (u == 5) f[3] = f[4] = f[5] = f[6] = f[7] = 0u;   // fields 43.. do not exist
-      const uint32_t lo32 = f[0] | (f[1] << 7) | (f[2] << 14) | (f[3] << 21) | (f[4] << 28);
-      const uint32_t hi24 = (f[4] >> 4) | (f[5] << 3) | (f[6] << 10) | (f[7] << 17);
-      const int nb = u == 5 ? 3 : 7;
-#pragma unroll
-      for (int e = 0; e < 7; ++e)
-        if (e < nb) put(row, 7 * u + e, e < 4 ? lo32 >> (8 * e) : hi24 >> (8 * (e - 4)));
-    }
-  }
+  if (kvsel == 0) pack(std::false_type{});
+  else pack(std::true_type{});
   __syncthreads();
 
   // ---- store the image: slots [slot0, slot0 + nrows) start at byte slot0 * R
