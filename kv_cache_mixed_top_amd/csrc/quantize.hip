@@ -317,27 +317,26 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   // below is twice the one above plus 2^-20.  The LDS code array keeps
   // code + 10 (pads and constant rows too); the field sums take the offset
   // back out in the dot product's accumulator.
+  // A constant row (s = 0; also the rows past the tile's end, read as
+  // zeros) is coded with scale 1: every value equals m, so y = 10 exactly
+  // and every code is 0, with no branch.
   constexpr uint32_t kTen = 0x0A0A0A0Au;
-  uint32_t cw[8] = {kTen, kTen, kTen, kTen, kTen, kTen, kTen, kTen};
-  float rs = 0.f, nb10 = 0.f;
-  bool wide = false;
-  uint32_t bias = 0u, thr = 0u;
+  const float sq = s > 0.0f ? s : 1.0f;
+  uint32_t cw[8];
+  const float rs = __builtin_amdgcn_rcpf(sq);
+  const float eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
+  const float nb10 = fmaf(-lo, rs, 10.0f);
+  const float win = (2.0f * eps + 0x1p-20f) * 1048576.0f;      // in units of 2^-20
+  const bool wide = !(win < 131072.0f);                         // then every code is settled
+  const uint32_t E = wide ? 131072u : (uint32_t)win + 1u;
+  const uint32_t bias = (E - 0x80000u) << 12;   // (frac - 1/2 + E) mod 2^20, in the top bits
+  const uint32_t thr = (2u * E) << 12;
   uint32_t umin[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};   // per 8 values
-  if (s > 0.0f) {
-    rs = __builtin_amdgcn_rcpf(s);
-    const float eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
-    nb10 = fmaf(-lo, rs, 10.0f);
-    const float win = (2.0f * eps + 0x1p-20f) * 1048576.0f;    // in units of 2^-20
-    wide = !(win < 131072.0f);                                  // then every code is settled
-    const uint32_t E = wide ? 131072u : (uint32_t)win + 1u;
-    bias = (E - 0x80000u) << 12;   // (frac - 1/2 + E) mod 2^20, in the top bits
-    thr = (2u * E) << 12;
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      const float y = fmaf((float)v[k >> 1][k & 1], rs, nb10);
-      umin[k >> 3] = min(umin[k >> 3], (__builtin_bit_cast(uint32_t, y) << 12) + bias);
-      cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(y, k & 3, cw[k >> 2]);
-    }
+  for (int k = 0; k < 32; ++k) {
+    const float y = fmaf((float)v[k >> 1][k & 1], rs, nb10);
+    umin[k >> 3] = min(umin[k >> 3], (__builtin_bit_cast(uint32_t, y) << 12) + bias);
+    cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(y, k & 3, (k & 3) ? cw[k >> 2] : 0u);
   }
   // dims 8q + 32i .. +8 -> row r of the LDS code array; lane 0 of the quad
   // clears the 8 pad bytes (fields read up to code 131)
@@ -347,7 +346,7 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
     *reinterpret_cast<uint2*>(crow + 8 * q + 32 * i) = make_uint2(cw[2 * i], cw[2 * i + 1]);
   uint32_t flag = 0u;   // groups of 8 values with a value near a half-integer
 #pragma unroll
-  for (int i = 0; i < 4; ++i) flag |= (uint32_t)(s > 0.0f && (wide || umin[i] <= thr)) << i;
+  for (int i = 0; i < 4; ++i) flag |= (uint32_t)(wide || umin[i] <= thr) << i;
   if (flag) {
     // Rare per group: one of its values lies near a half-integer (with fp16
     // data nearly always an exact tie).  The group's 8 values are read
@@ -363,7 +362,7 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
         const float x = h2f((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
         const float y = fmaf(x, rs, nb10);
         if (wide || (__builtin_bit_cast(uint32_t, y) << 12) + bias <= thr) {
-          const float c = exact_code(x, lo, s, rintf(y - 10.0f));
+          const float c = exact_code(x, lo, sq, rintf(y - 10.0f));
           crow[8 * q + 32 * i + e] = (uint8_t)((int)c + 10);
         }
       }
