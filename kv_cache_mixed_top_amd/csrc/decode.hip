@@ -395,6 +395,157 @@ __global__ __launch_bounds__(kThreads) void decode_tail_kernel(DecodeArgs a) {
   }
 }
 
+// The same partial record for a tail of at most 128 rows (block <= 128),
+// with every load issued up front: each wave multiplies the queries with
+// 16-row blocks of K on the 16x16x32 f16 matrix core (A rows 0-3 = the 4
+// query heads, B columns = K rows; fp16 products are exact, sums in fp32)
+// while the V rows of the value pass are already in flight.
+using h8t = _Float16 __attribute__((ext_vector_type(8)));
+using f4t = float __attribute__((ext_vector_type(4)));
+constexpr int kTailSmall = 128;
+
+__global__ __launch_bounds__(kThreads) void decode_tail128_kernel(DecodeArgs a) {
+  __shared__ float z[kTailGroup][kTailSmall];
+  __shared__ __attribute__((aligned(16))) float part[kThreads / 64][kTailGroup][kHeadDim];
+  __shared__ float red[kThreads / 64][2 * kTailGroup];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int x = a.x0 + blockIdx.x;
+  const int n = (int)a.n_tail;                 // one chunk: the whole tail
+  const int li = blockIdx.y / a.kv_heads;
+  const int g = blockIdx.y % a.kv_heads;
+  const int b = blockIdx.z;
+  const int layer = a.layer0 + li;
+  const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
+  const uint16_t* kt = a.tail_kv + plane_k * a.block * kHeadDim;
+  const uint16_t* vt = a.tail_kv + (plane_k + 1) * a.block * kHeadDim;
+
+  // V rows rs + 16 i for the value pass (16 threads per row, 8 dimensions each)
+  const int dg = tid & 15, rs = tid >> 4;
+  uint4 vv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rs + 16 * i;
+    vv[i] = r < n ? reinterpret_cast<const uint4*>(vt + (int64_t)r * kHeadDim)[dg]
+                  : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // K: wave w takes the 16-row blocks w and w + 4; lane (col, kg) holds
+  // dimensions 32 ks + 8 kg .. + 8 of row 16 blk + col
+  const int col = lane & 15, kg = lane >> 4;
+  uint4 kb[2][4];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (wave + 4 * j) + col;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kb[j][ks] = r < n ? reinterpret_cast<const uint4*>(kt + (int64_t)r * kHeadDim + 32 * ks + 8 * kg)[0]
+                        : make_uint4(0u, 0u, 0u, 0u);
+  }
+  // queries as the A operand: row col < 4 is head col
+  uint4 qa[4];
+  const uint16_t* qh = a.q + (((int64_t)b * a.nl + li) * a.q_heads + g * kTailGroup + min(col, 3)) * kHeadDim;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qa[ks] = col < kTailGroup ? reinterpret_cast<const uint4*>(qh + 32 * ks + 8 * kg)[0]
+                              : make_uint4(0u, 0u, 0u, 0u);
+  // logits: lanes 0-15 (kg = 0) receive rows 0-3 (the heads) of the product
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    f4t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8t, qa[ks]),
+                                                   __builtin_bit_cast(h8t, kb[j][ks]), acc, 0, 0, 0);
+    const int r = 16 * (wave + 4 * j) + col;
+    if (kg == 0 && r < n) {
+#pragma unroll
+      for (int h = 0; h < kTailGroup; ++h) z[h][r] = a.sm_scale * acc[h];
+    }
+  }
+  __syncthreads();
+
+  // softmax statistics per head (one row per thread)
+  float mx[kTailGroup], sum[kTailGroup];
+#pragma unroll
+  for (int h = 0; h < kTailGroup; ++h) {
+    float m = tid < n ? z[h][tid] : -INFINITY;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    mx[h] = m;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < kTailGroup; ++h) red[wave][h] = mx[h];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < kTailGroup; ++h) {
+    mx[h] = fmaxf(fmaxf(red[0][h], red[1][h]), fmaxf(red[2][h], red[3][h]));
+    float sl = 0.f;
+    if (tid < n) {
+      sl = __expf(z[h][tid] - mx[h]);
+      z[h][tid] = sl;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sl += __shfl_xor(sl, o, 64);
+    sum[h] = sl;
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < kTailGroup; ++h) red[wave][kTailGroup + h] = sum[h];
+  }
+  __syncthreads();
+
+  // values: rows rs + 16 i, dimensions 8 dg .. + 8
+  float acc[kTailGroup][8];
+#pragma unroll
+  for (int h = 0; h < kTailGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = rs + 16 * i;
+    if (r < n) {
+      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+      for (int h = 0; h < kTailGroup; ++h) {
+        const float pr = z[h][r];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          acc[h][e] = fmaf(pr, h2f((uint16_t)(w4[e >> 1] >> (16 * (e & 1)))), acc[h][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kTailGroup; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[h][e] += __shfl_xor(acc[h][e], 16, 64);
+      acc[h][e] += __shfl_xor(acc[h][e], 32, 64);
+    }
+  if (lane < 16) {
+#pragma unroll
+    for (int h = 0; h < kTailGroup; ++h) {
+      float4* dst = reinterpret_cast<float4*>(&part[wave][h][8 * dg]);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  __syncthreads();
+
+  const int64_t u = ((((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x);
+  float* wsu = a.ws + u * kTailGroup * kPartialStride;
+  for (int i = tid; i < kTailGroup * kHeadDim; i += kThreads) {
+    const int h = i / kHeadDim, d = i - h * kHeadDim;
+    wsu[h * kPartialStride + 2 + d] = part[0][h][d] + part[1][h][d] + part[2][h][d] + part[3][h][d];
+  }
+  if (tid < kTailGroup) {
+    wsu[tid * kPartialStride + 0] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
+    wsu[tid * kPartialStride + 1] = red[0][kTailGroup + tid] + red[1][kTailGroup + tid] +
+                                    red[2][kTailGroup + tid] + red[3][kTailGroup + tid];
+  }
+}
+
 // Log-sum-exp merge of the chunk partials of one (sequence, layer, query
 // head): the chunk maxima and sums are read in parallel, the weights
 // exp(m_c - M) go to LDS, then each thread combines one output dimension
@@ -475,6 +626,62 @@ __global__ __launch_bounds__(P * kHeadDim) void decode_merge_kernel(DecodeArgs a
   }
 }
 
+// Merge of one (sequence, layer, KV head) with 4 query heads by one wave,
+// for up to C chunks: every load is issued before the math, so the merge
+// costs about one memory latency.
+// Lane c * 4 + h reads (m, l) of chunk c and head h; the per-head maximum
+// and sum of weighted l are combined across the lanes of a head; each lane
+// then sums dimensions lane and lane + 64 of the 4 heads over the chunks.
+// Chunk order and the combination rule match the other merge kernels up to
+// the order of the floating-point additions.
+template <int C>
+__global__ __launch_bounds__(64) void decode_merge_unit_kernel(DecodeArgs a) {
+  constexpr int G = 4;
+  const int lane = threadIdx.x, h4 = lane & 3, c4 = lane >> 2;
+  const int g = blockIdx.x, li = blockIdx.y, b = blockIdx.z;
+  const int nc = a.nchunks;
+  const int64_t unit = ((int64_t)b * a.nl + li) * a.kv_heads + g;
+  const float* base = a.ws + unit * nc * G * kPartialStride;
+  // all loads first
+  const float* pm = base + ((int64_t)min(c4, nc - 1) * G + h4) * kPartialStride;
+  const float m_own = pm[0], l_own = pm[1];
+  float ov[C][G][2];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float* p = base + ((int64_t)min(c, nc - 1) * G + h) * kPartialStride + 2;
+      ov[c][h][0] = c < nc ? p[lane] : 0.f;
+      ov[c][h][1] = c < nc ? p[lane + 64] : 0.f;
+    }
+  // per-head maximum and denominator over the chunks (lanes of one head)
+  float M = c4 < nc ? m_own : -INFINITY;
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float w_own = c4 < nc ? __expf(m_own - M) : 0.f;
+  float den = w_own * l_own;
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) den += __shfl_xor(den, o, 64);
+  float num[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) num[h][0] = num[h][1] = 0.f;
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float w = __shfl(w_own, 4 * c + h, 64);   // 0 for c >= nc
+      num[h][0] = fmaf(w, ov[c][h][0], num[h][0]);
+      num[h][1] = fmaf(w, ov[c][h][1], num[h][1]);
+    }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float d = __shfl(den, h, 64);
+    float* o = a.out + (((int64_t)b * a.nl + li) * a.q_heads + g * G + h) * kHeadDim;
+    o[lane] = num[h][0] / d;
+    o[lane + 64] = num[h][1] / d;
+  }
+}
+
 }  // namespace
 
 int decode_chunk_tokens(int64_t tokens_per_unit, int64_t units) {
@@ -514,7 +721,10 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
     g.x0 = a.nch[0] + a.nch[1];          // the fp16 tail chunks
     if (a.nch[2] <= 0) return hipSuccess;
     dim3 grid(a.nch[2], a.nl * a.kv_heads, a.batch);
-    hipLaunchKernelGGL(decode_tail_kernel, grid, dim3(kThreads), 0, stream, g);
+    if (a.block <= kTailSmall && a.nch[2] == 1)
+      hipLaunchKernelGGL(decode_tail128_kernel, grid, dim3(kThreads), 0, stream, g);
+    else
+      hipLaunchKernelGGL(decode_tail_kernel, grid, dim3(kThreads), 0, stream, g);
     return hipGetLastError();
   }
   g.x0 = 0;
@@ -522,6 +732,14 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
+  if (a.group == 4 && a.nchunks <= 16) {
+    const dim3 ug(a.kv_heads, a.nl, a.batch);
+    if (a.nchunks <= 8)
+      hipLaunchKernelGGL(decode_merge_unit_kernel<8>, ug, dim3(64), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_merge_unit_kernel<16>, ug, dim3(64), 0, stream, a);
+    return hipGetLastError();
+  }
   dim3 grid(a.q_heads, a.nl, a.batch);
   if (a.nchunks > 32) {
     hipLaunchKernelGGL(decode_merge_kernel<4>, grid, dim3(4 * kHeadDim), a.nchunks * sizeof(float),
