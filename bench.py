@@ -141,10 +141,18 @@ def main():
     partial_bytes = kv_packed + q_bytes                       # per decode_partials launch
     step_bytes = rank_bytes + quant_bytes + D * decode_bytes
 
+    # HIP events on the work stream: quantize-pack and the decode loop of
+    # every timed step, and each decode_partials launch.  An event is a queue
+    # packet between kernels that costs about 1.5 us of the step, so the
+    # merges get one marker each, after them, and the decode time per step is
+    # the loop's.  (With no marker between a merge and the next partials
+    # event, that event pair measured the partials launch about 5 us longer
+    # than rocprofv3's kernel time.)
     Ev = lambda: torch.cuda.Event(enable_timing=True)
     ev_q = [(Ev(), Ev()) for _ in range(args.steps)]
+    ev_l = [Ev() for _ in range(args.steps)]                 # decode loop end
     ev_p = [[(Ev(), Ev()) for _ in range(D)] for _ in range(args.steps)]
-    ev_d = [[(Ev(), Ev()) for _ in range(D)] for _ in range(args.steps)]
+    ev_m = Ev()                                              # marker after a merge
 
     def step(i=None):
         cache.reset()
@@ -156,14 +164,15 @@ def main():
             ev_q[i][1].record(stream)
         for j in range(D):
             if i is not None:
-                ev_d[i][j][0].record(stream)
                 ev_p[i][j][0].record(stream)
             sk.semkv_decode_partials(cache, q[j], stream=stream)
             if i is not None:
                 ev_p[i][j][1].record(stream)
             sk.semkv_decode_merge(cache, out, stream=stream)
             if i is not None:
-                ev_d[i][j][1].record(stream)
+                ev_m.record(stream)
+        if i is not None:
+            ev_l[i].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -182,7 +191,8 @@ def main():
     ms_step = ms_total / args.steps
     ms_quant = float(np.mean([a.elapsed_time(b) for a, b in ev_q]))
     ms_part = float(np.mean([a.elapsed_time(b) for row in ev_p for a, b in row])) if D else 0.0
-    ms_dec = float(np.mean([a.elapsed_time(b) for row in ev_d for a, b in row])) if D else 0.0
+    ms_dec = (float(np.mean([q1.elapsed_time(e) for (_, q1), e in zip(ev_q, ev_l)])) / D
+              if D else 0.0)
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step; quantize {ms_quant:.3f} ms; "
         f"decode {ms_dec * 1e3:.1f} us/step (partials {ms_part * 1e3:.1f} us)")
 
