@@ -8,7 +8,10 @@
 // (k - #{key > T}) tokens with key == T in index order.  perm lists H in
 // ascending order, then the rest ascending.
 //
-// Two kernels:
+// Three kernels:
+//  * rank_select32_kernel -- one 1024-thread workgroup per sequence for
+//                            n <= 32,768: each thread keeps the keys of its
+//                            32 tokens in registers for every pass
 //  * rank_select_kernel   -- one 1024-thread workgroup per sequence, any n
 //  * rank_block_kernel    -- one wave64 per sequence for n <= 128 (generation
 //                            blocks): bitonic sort of 64-bit (key, ~index)
@@ -160,6 +163,124 @@ __global__ __launch_bounds__(kThreads) void rank_select_kernel(
   }
 }
 
+// The same selection and partition for n <= 32 * kThreads, with the keys of
+// tokens [32 tid, 32 tid + 32) loaded once (independent loads, one memory
+// latency) and the radix digit found by a parallel scan of the 256 bins.
+__global__ __launch_bounds__(kThreads) void rank_select32_kernel(
+    const float* __restrict__ scores, int64_t ld, int n, int k, int32_t* __restrict__ perm,
+    uint32_t* __restrict__ mask) {
+  constexpr int kItems = 32;
+  __shared__ uint32_t hist[kWaves][256];
+  __shared__ int scan_buf[kWaves + 1];
+  __shared__ uint32_t sh_prefix;
+  __shared__ int sh_remaining;
+
+  const int b = blockIdx.x;
+  const float* s = scores + (int64_t)b * ld;
+  int32_t* p = perm + (int64_t)b * n;
+  const int nwords = (n + 31) >> 5;
+  uint32_t* mk = mask ? mask + (int64_t)b * nwords : nullptr;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int begin = tid * kItems;
+  const int cnt = max(0, min(kItems, n - begin));
+  uint32_t key[kItems];
+  if (cnt == kItems && ((uintptr_t)(s + begin) & 15u) == 0) {   // 16-byte loads
+#pragma unroll
+    for (int j = 0; j < kItems / 4; ++j) {
+      const float4 v = reinterpret_cast<const float4*>(s + begin)[j];
+      key[4 * j] = score_key(v.x);
+      key[4 * j + 1] = score_key(v.y);
+      key[4 * j + 2] = score_key(v.z);
+      key[4 * j + 3] = score_key(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) key[j] = j < cnt ? score_key(s[begin + j]) : 0u;
+  }
+
+  // -- radix select of the k-th largest key (k >= 1)
+  uint32_t thr = 0xFFFFFFFFu;
+  int need_eq = 0;
+  if (k > 0) {
+    uint32_t prefix = 0, pmask = 0;
+    int remaining = k;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int i = tid; i < kWaves * 256; i += kThreads) (&hist[0][0])[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kItems; ++j)
+        if (j < cnt && (key[j] & pmask) == prefix)
+          atomicAdd(&hist[wave][(key[j] >> shift) & 255u], 1u);
+      __syncthreads();
+      // thread t < 256 takes digit 255 - t; the exclusive scan gives the
+      // candidates above it, and the digit where the count reaches
+      // `remaining` is the next digit of the k-th largest key
+      int c = 0;
+      if (tid < 256) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c += (int)hist[w][255 - tid];
+      }
+      int total;
+      const int above = block_exclusive_scan(c, scan_buf, &total);
+      if (tid < 256 && above < remaining && remaining <= above + c) {
+        sh_prefix = prefix | ((uint32_t)(255 - tid) << shift);
+        sh_remaining = remaining - above;
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      remaining = sh_remaining;
+      pmask |= 0xFFu << shift;
+      __syncthreads();
+    }
+    thr = prefix;
+    need_eq = remaining;
+  }
+
+  // -- membership and stable partition of the thread's tokens
+  int gt = 0, eq = 0;
+  if (k > 0) {
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      gt += j < cnt && key[j] > thr;
+      eq += j < cnt && key[j] == thr;
+    }
+  }
+  int eq_total;
+  const int eq_before = block_exclusive_scan(eq, scan_buf, &eq_total);
+  const int take_eq = min(max(need_eq - eq_before, 0), eq);
+  int in_total;
+  const int in_before = block_exclusive_scan(gt + take_eq, scan_buf, &in_total);
+
+  int pin = in_before;
+  int pout = k + (begin - in_before);
+  int eq_seen = 0;
+  uint32_t word = 0;
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {
+    if (j < cnt) {
+      bool in = false;
+      if (k > 0) {
+        if (key[j] > thr) {
+          in = true;
+        } else if (key[j] == thr) {
+          in = (eq_before + eq_seen) < need_eq;
+          ++eq_seen;
+        }
+      }
+      if (in) {
+        if (pin < k) p[pin] = begin + j;
+        ++pin;
+      } else {
+        if (pout < n) p[pout] = begin + j;
+        ++pout;
+      }
+      word |= (uint32_t)in << j;
+    }
+  }
+  if (mk && cnt > 0) mk[tid] = word;
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
   const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
   const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
@@ -248,6 +369,9 @@ hipError_t launch_rank(const float* scores, int batch, int n, int64_t ld, int k,
   if (n <= 128) {
     hipLaunchKernelGGL(rank_block_kernel, dim3(batch), dim3(64), 0, stream, scores, ld, n, k,
                        perm, mask);
+  } else if (n <= 32 * kThreads) {
+    hipLaunchKernelGGL(rank_select32_kernel, dim3(batch), dim3(kThreads), 0, stream, scores, ld,
+                       n, k, perm, mask);
   } else {
     int items = (n + kThreads - 1) / kThreads;
     items = (items + 31) & ~31;   // each thread owns whole mask words

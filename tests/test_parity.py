@@ -43,7 +43,7 @@ def _check_rank(scores, k, what):
 
 
 @pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 64, 100, 127, 128, 129, 200, 1000, 1024, 1025,
-                               4099, 32768])
+                               4099, 32767, 32768, 32769, 40000])
 def test_rank_random(n):
     _print("rank random n", n)
     rng = np.random.default_rng(n)
@@ -52,7 +52,7 @@ def test_rank_random(n):
         _check_rank(s, O.topr_count(n, r), f"n={n} r={r}")
 
 
-@pytest.mark.parametrize("n", [5, 77, 128, 300, 5000])
+@pytest.mark.parametrize("n", [5, 77, 128, 300, 5000, 32768, 33000])
 def test_rank_ties_nan_signed_zero(n):
     _print("rank ties n", n)
     rng = np.random.default_rng(7 + n)
