@@ -56,7 +56,6 @@ constexpr int kQkInstr = 33;        // 4x4x4 MFMAs per row (132 digit slots)
 constexpr float kFrameMargin = 8.0f; // softmax frame above the running max (natural log)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kFullRead = 96;       // rows spanned by an unclamped 3 KB tile read (> 3072/38)
 
 __device__ __forceinline__ uint32_t u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ u16x2 v2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
@@ -624,6 +623,11 @@ __device__ __forceinline__ h8 lds_read_h8_wait(const _Float16* p) {
 // wait insertion knows what has completed; the encodings are those of the
 // CDNA s_waitcnt immediate (vmcnt in bits 3:0 and 15:14, expcnt in 6:4,
 // lgkmcnt in 11:8).
+// Raw buffer resource over `bytes` bytes from `base` (CDNA buffer
+// descriptor, stride 0): loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
@@ -645,30 +649,19 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   // the first K tile is in flight)
   h4 qf[3];
   float sumq[4];
-  // K rows [t0, t0 + nt) -> buffer `buf` (16 bytes per lane per instruction;
-  // chunks past the valid range re-read the last valid chunk); the lane's K
-  // meta word -> register
-  // A full tile whose 3 KB read stays inside the plane loads unclamped from a
-  // uniform base (the bytes past the tile are not used).
+  // The 3 KB of K bytes from row t0 on -> buffer `buf` (16 bytes per lane per
+  // instruction), and the lane's K meta word -> register.  The plane from
+  // row t0 is a buffer resource built on the scalar unit: the loads need no
+  // per-lane address arithmetic, and bytes past the plane read as zeros (the
+  // rows past the tile are not used).
   uint32_t km_next = 0;
   const uint32_t lane16 = 16u * (uint32_t)lane;
-  auto issue = [&](int buf, int t0, int nt) {
-    const uint8_t* ks = kcodes + t0 * R;
-    if (nt == kTile && t0 + kFullRead <= cap) {
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        __builtin_amdgcn_global_load_lds(ks + (lane16 + 1024u * i),
-                                         lds_at(st.k(buf), 1024 * i), 16, 0, 0);
-      km_next = kmg[t0 + lane];
-    } else {
-      const int nk = (nt * R + 15) >> 4;
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        if (64 * i < nk)
-          __builtin_amdgcn_global_load_lds(ks + 16 * min(64 * i + lane, nk - 1),
-                                           lds_at(st.k(buf), 1024 * i), 16, 0, 0);
-      km_next = kmg[t0 + min(lane, nt - 1)];
-    }
+  auto issue = [&](int buf, int t0) {
+    const __amdgpu_buffer_rsrc_t rk = plane_rsrc(kcodes + t0 * R, (cap - t0) * R);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 2048, 0);
+    km_next = __builtin_amdgcn_raw_buffer_load_b32(plane_rsrc(kmg + t0, (cap - t0) * 4), 4 * lane, 0, 0);
   };
 
   float frame[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -679,7 +672,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     const int nt = min(kTile, ir1 - t0);
     wait_vm0();   // this tile's rows have landed
     const uint32_t km = km_next;
-    if (t0 + kTile < ir1) issue(1 - B, t0 + kTile, min(kTile, ir1 - t0 - kTile));
+    if (t0 + kTile < ir1) issue(1 - B, t0 + kTile);
     f4 sacc[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) sacc[k] = (f4){0.f, 0.f, 0.f, 0.f};
@@ -724,7 +717,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     wait_lgkm0();  // logits written
     tile_barrier();
   };
-  if (ir0 < ir1) issue(0, ir0, min(kTile, ir1 - ir0));
+  if (ir0 < ir1) issue(0, ir0);
   const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
                        (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
   {
@@ -784,27 +777,17 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
     for (int k = 0; k < 3; ++k) acc[s][k] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  // V tiles [t0, t0 + nt) -> buffer `buf` (whole 16-row byte-planar tiles);
-  // the lane's V meta word -> register
+  // The 3 KB of V bytes (16-row byte-planar tiles) from row t0 on -> buffer
+  // `buf`, and the lane's V meta word -> register, through buffer resources
+  // as in the K wave
   uint32_t vm_next = 0;
   const uint32_t lane16 = 16u * (uint32_t)lane;
-  auto issue = [&](int buf, int t0, int nt) {
-    const uint8_t* vs = vcodes + t0 * R;
-    if (nt == kTile && t0 + kFullRead <= cap) {
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        __builtin_amdgcn_global_load_lds(vs + (lane16 + 1024u * i),
-                                         lds_at(st.v(buf), 1024 * i), 16, 0, 0);
-      vm_next = vmg[t0 + lane];
-    } else {
-      const int nv = ((nt + 15) >> 4) * R;
-#pragma unroll
-      for (int i = 0; i < 3; ++i)
-        if (64 * i < nv)
-          __builtin_amdgcn_global_load_lds(vs + 16 * min(64 * i + lane, nv - 1),
-                                           lds_at(st.v(buf), 1024 * i), 16, 0, 0);
-      vm_next = vmg[t0 + min(lane, nt - 1)];
-    }
+  auto issue = [&](int buf, int t0) {
+    const __amdgpu_buffer_rsrc_t rv = plane_rsrc(vcodes + t0 * R, (cap - t0) * R);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_at(st.v(buf), 0), 16, (int)lane16, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_at(st.v(buf), 0), 16, (int)lane16, 0, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_at(st.v(buf), 0), 16, (int)lane16, 0, 2048, 0);
+    vm_next = __builtin_amdgcn_raw_buffer_load_b32(plane_rsrc(vmg + t0, (cap - t0) * 4), 4 * lane, 0, 0);
   };
 
   const int col = lane & 15;
@@ -820,7 +803,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
     const int nt = min(kTile, ir1 - t0);
     wait_vm0();   // this tile's V has landed
     const uint32_t vm = vm_next;
-    if (t0 + kTile < ir1) issue(1 - B, t0 + kTile, min(kTile, ir1 - t0 - kTile));
+    if (t0 + kTile < ir1) issue(1 - B, t0 + kTile);
     tile_barrier();                                      // logits of this tile are in LDS
     float z[4];
 #pragma unroll
@@ -907,7 +890,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
       }
     }
   };
-  if (ir0 < ir1) issue(0, ir0, min(kTile, ir1 - ir0));
+  if (ir0 < ir1) issue(0, ir0);
   {
     const uint32_t smax = chunk_scale_max(vmg, r0, r1, lane);
     if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
