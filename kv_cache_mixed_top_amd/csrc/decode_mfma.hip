@@ -1,41 +1,48 @@
 // Matrix-core decode attention over pools of 6-level and 5-level rows (the
 // SemKV page's operating pair b_high/b_low = log2 6 / log2 5, Fig. 1 and
 // Table 2).  Same split-K contract as the generic kernel in decode.hip: one
-// workgroup (one wave64) per chunk of one pool plane pair (K and V of one
-// sequence, layer and KV head), writing (m, l, o[4][128]) partials.
+// workgroup per chunk of one pool plane pair (K and V of one sequence, layer
+// and KV head) for the 4 query heads of the KV head, writing (m, l, o[128])
+// partials per head.
+//
+// decode_mfma2_kernel (the one launched): two waves per chunk.  Wave 0
+// streams K and computes the logits, wave 1 streams V, keeps the softmax and
+// the PV accumulators; the logits of a tile pass through LDS with one
+// barrier per tile.  decode_mfma_kernel is the single-wave form, kept for
+// comparison (SEMKV_DECODE=mfma1).
 //
 // Per 64-row tile:
+//  * Staging: direct global->LDS loads of the next tile through a buffer
+//    resource over the plane (range-checked, no per-lane address math).
+//  * Digits: a field value x enters as the fp16 value 1536 + x (one v_perm
+//    puts the byte under a 0x66 high byte); one packed fp16 FMA with the
+//    constants below gives 1536 + floor(x / L) exactly, and the digits
+//    follow with exact fp16 subtracts and FMAs.  All MFMA operands are
+//    normal fp16 values (a chain with subnormal operands measured ~100x
+//    larger rounding on gfx950).
 //  * QK^T on the 4x4x4 (16-block) f16 MFMA.  Lane t owns token row t of the
-//    row-major K plane; its base-L digits are computed with packed 16-bit
-//    integer arithmetic.  A 16-bit integer c read as fp16 is the subnormal
-//    c * 2^-24; one packed fp16 multiply by 2^14 makes it the normal value
-//    c * 2^-10 exactly.  (Measured on gfx950: a chain of these MFMAs with
-//    subnormal operands loses ~1e-6 of sum|terms|, 100x more than with
-//    normal operands, which outlier K rows with large scales turn into
-//    visible logit error.)  The 4 query heads of the KV head are the
-//    A operand; cbsz = 4 broadcasts block `abid`'s A to all 16 blocks, so the
-//    q fragments of 16 consecutive instructions share one VGPR pair.  Lane t
-//    ends with the 4 heads' logits of its own token.
-//  * logit z = sm_scale * (scale_K * (q . c) + min_K * sum(q)); softmax
-//    weights are taken against a running per-head maximum (rescaling the
-//    accumulators only when a tile raises it, so every weight is <= 1).
+//    row-major K plane.  The 4 query heads are the A operand; cbsz = 4
+//    broadcasts block `abid`'s A to all 16 blocks, so the q fragments of 16
+//    consecutive instructions share one VGPR pair.
+//  * logit z = sm_scale * log2(e) * (scale_K * (q . c) + min_K * sum(q)), in
+//    log2 units; the weights are taken against a per-head frame a margin
+//    above the running maximum, which rises (and rescales the accumulators)
+//    only when a logit exceeds it.
 //  * PV on the 16x16x32 f16 MFMA with K = 32 tokens.  V planes are stored
 //    byte-planar in 16-row tiles (byte j of 16 consecutive rows is
 //    contiguous), so one 8-byte LDS read gives one code byte of 8 tokens.
 //    The A operand is w = p * scale_V * 2^E (E per chunk keeps w below 2^14)
-//    split into two fp16 terms w_hi (A rows 0-3) + w_lo (rows 4-7), summed
-//    once at the end, so the weights keep ~22 bits: with heavy-tailed V the
-//    min_V and scale_V * code terms nearly cancel and a single fp16 weight
-//    (11 bits) is not enough.  The B operand holds the linear features of
-//    each packed field f: f, floor(f/L), floor(f/L^2).  Digits are linear in
-//    them (c0 = f - L*f1, c1 = f1 - L*f2, c2 = f2), so the digit sums are
-//    recovered from the fp32 accumulators at the end.  The features enter
-//    centred on the middle of their range (and scaled by 2^-10, exact normal
-//    fp16): the weights are all positive, so uncentred sums would grow with
-//    the chunk length and the recovery c0 = F0 - L*F1 would amplify their
-//    rounding ~40x; centred sums stay small.  The centring adds m*sum(w) to
-//    every digit sum (m = (L-1)/2), read from a column that holds no field.
-//    sum_t p_t * min_V(t) is accumulated on the VALU.
+//    split into two fp16 terms w_hi (A rows 0-3) + w_lo (rows 4-7), so the
+//    weights keep ~22 bits: with heavy-tailed V the min_V and scale_V * code
+//    terms nearly cancel and a single fp16 weight (11 bits) is not enough.
+//    The B operand holds the linear features of each packed field f: f,
+//    floor(f/L), floor(f/L^2), centred on integer midpoints of their ranges.
+//    The digits are linear in them (c0 = f - L*f1, c1 = f1 - L*f2, c2 = f2),
+//    so the digit sums are recovered from the fp32 accumulators at the end;
+//    the centring (needed because the weights are all positive: uncentred
+//    sums grow with the chunk and the recovery amplifies their rounding)
+//    adds coef_k * sum(w) to each digit sum, read from a B column that holds
+//    no field.  sum_t p_t * min_V(t) is accumulated on the VALU.
 #include <utility>
 
 #include "semkv_internal.h"
