@@ -8,10 +8,13 @@
 // q of a row loads the 16-byte pieces at byte offsets 16q + 64i (i = 0..3),
 // so each load instruction of a quad covers 64 contiguous bytes.
 //
-// Codes: c = round-half-even((x - m) / s).  The fast path evaluates
-// y = fl(fl(x - m) * fl(1/s)) in fp32, whose relative error is < 2^-21; when
-// y lies within (L-1)*2^-20 of a half-integer the code is settled exactly in
-// double with the exact residuals x - m - (c0 +/- 1/2) s.
+// Codes: c = round-half-even((x - m) / s).  The fast path (6- and 5-level
+// pools) evaluates y = (x - m)/s + 10 as one fp32 FMA with fl(1/s) and
+// converts it to a byte; a group of 8 values with one near a half-integer
+// (within the bound of that evaluation's error) is re-read and settled
+// exactly in double with the residuals x - m - (c0 +/- 1/2) s.  The generic
+// path (any level count) evaluates y = (x - m) * fl(1/s) and settles each
+// value near a half-integer the same way.
 //
 // Packing: codes go to LDS; each output byte is assembled from the fields
 // that overlap it.  K planes hold rows back to back; V planes are byte-planar
