@@ -754,8 +754,13 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
 int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units) {
   // Chunks fill whole rounds of the resident workgroup slots; a chunk holds
   // at most kMfmaChunkMax rows, which bounds the length of the matrix-core
-  // accumulations (longer contexts take more rounds instead).
+  // accumulations (longer contexts take more rounds instead), and at least
+  // kMfmaChunkMin rows: a chunk's fixed work (query fragments, the V scale
+  // pass, the partial record, its share of the merge) then spreads over four
+  // tiles.  (A launch over few (sequence, layer, KV head) units, such as one
+  // layer of one sequence, would otherwise take one- or two-tile chunks.)
   constexpr int64_t kMfmaChunkMax = 4096;
+  constexpr int64_t kMfmaChunkMin = 4 * kTile;
   const int64_t slots = decode_mfma_resident_waves();
   int64_t per_round = slots / (units > 0 ? units : 1);
   if (per_round < 2) per_round = 2;
@@ -769,6 +774,7 @@ int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units) {
   };
   int64_t c = fit(per_round);
   if (c > kMfmaChunkMax) c = fit(per_round * ((c + kMfmaChunkMax - 1) / kMfmaChunkMax));
+  if (c < kMfmaChunkMin) c = kMfmaChunkMin;
   return (int)c;
 }
 

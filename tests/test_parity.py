@@ -219,11 +219,11 @@ def test_decode_configs(case):
     _decode_case(seed=len(str(case)), **case)
 
 
-# One sequence, one layer and 2 KV heads leave room for 64-row chunks, so the
-# chunk count per head grows with n and each merge form runs: one wave per
-# KV head (<= 8 and <= 16 chunks), one workgroup per query head (<= 32), and
-# four chunk groups per query head (more).
-@pytest.mark.parametrize("n", [500, 1000, 2000, 3000, 4100])
+# One sequence, one layer and 2 KV heads take the shortest chunks (256 rows),
+# so the chunk count per head grows with n and each merge form runs: one wave
+# per KV head (<= 8 and <= 16 chunks), one workgroup per query head (<= 32),
+# and four chunk groups per query head (more).
+@pytest.mark.parametrize("n", [500, 2500, 6000, 10000])
 def test_decode_merge_chunk_counts(n):
     _print("decode merge chunks", n)
     _decode_case(B=1, layers=1, kv=2, Hq=8, n=n, r=0.5, Lh=6, Ll=5, sm=1.0, seed=n)
