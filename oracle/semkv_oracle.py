@@ -28,6 +28,13 @@ the reading used here is the plainest one that the rest supports, marked
   * packing: g codes of base L per b-bit field, first code in the least
     significant digit, fields LSB-first in a little-endian bit stream
     (our layout; the pages fix only the rates of SemKV Table 6)
+  * optional Hadamard rotation of every row before quantization (SemKV
+    Table 2 lists one in the default quantizer; which Hadamard matrix and in
+    what precision is open on the pages): the normalized Sylvester H_128
+    without sign changes, applied in float32 by seven butterfly stages in
+    index-bit order, then one multiply by float32(1/sqrt(128)); the minimum
+    of a rotated row is rounded down to fp16.  Decode rotates the query and
+    rotates the output back (H is symmetric and orthogonal).
 
 Parity pins for every function live in tests/test_oracle_pins.py and
 tests/test_oracle_props.py; no function here is "parity unpinned".
@@ -125,11 +132,13 @@ def scale_fp16_ceil(lo: np.ndarray, hi: np.ndarray, L: int) -> np.ndarray:
     """
     lo = np.asarray(lo, dtype=np.float64)
     hi = np.asarray(hi, dtype=np.float64)
-    q = (hi - lo) / float(L - 1)
+    d = hi - lo                                           # exact (float32/fp16 operands)
+    q = d / float(L - 1)
     s = q.astype(np.float16)                              # nearest fp16
-    up = s.astype(np.float64) < q                         # rounded below q
+    # settle the ceiling exactly: fp16 * (L - 1) is exact in float64
+    up = s.astype(np.float64) * (L - 1) < d
     s = np.where(up, np.nextafter(s, np.float16(np.inf)), s)
-    down = np.nextafter(s, np.float16(-np.inf)).astype(np.float64) >= q
+    down = np.nextafter(s, np.float16(-np.inf)).astype(np.float64) * (L - 1) >= d
     s = np.where(down & (q > 0), np.nextafter(s, np.float16(-np.inf)), s)
     s = np.where(q == 0, np.float16(0.0), s)
     return s.astype(np.float16)
@@ -157,6 +166,80 @@ def quantize_rows(x: np.ndarray, L: int):
     safe = np.where(s64 > 0, s64, 1.0)
     t = (x64 - lo[..., None]) / safe[..., None]           # numerator exact
     codes = np.rint(t)                                    # ties to even
+    codes = np.clip(codes, 0, L - 1)
+    codes = np.where((s64 > 0)[..., None], codes, 0.0)
+    return codes.astype(np.int64), s16, lo.astype(np.float16)
+
+
+def hadamard128() -> np.ndarray:
+    """Normalized Sylvester Hadamard matrix, float64: H[i, j] =
+    (-1)^popcount(i & j) / sqrt(128).  Symmetric, H @ H = I."""
+    i = np.arange(HEAD_DIM)
+    par = np.zeros((HEAD_DIM, HEAD_DIM), dtype=np.int64)
+    for bit in range(7):
+        par += ((i[:, None] >> bit) & (i[None, :] >> bit) & 1)
+    return np.where(par % 2 == 0, 1.0, -1.0) / math.sqrt(HEAD_DIM)
+
+
+HADAMARD_SCALE_F32 = np.float32(1.0 / math.sqrt(HEAD_DIM))
+
+
+def rotate_rows_f32(x: np.ndarray) -> np.ndarray:
+    """Hadamard rotation of fp16 rows as the quantizer defines it, float32.
+
+    y = x as float32; for bit = 0 .. 6, every index pair (i, i + 2^bit) with
+    that bit clear in i becomes (y_i + y_j, y_i - y_j), each sum and
+    difference rounded to float32; finally y * float32(1/sqrt(128)).  Up to
+    those roundings this is hadamard128() @ x.
+    """
+    y = np.asarray(x, dtype=np.float16).astype(np.float32).copy()
+    if y.shape[-1] != HEAD_DIM:
+        raise ValueError("rows must hold 128 values")
+    for bit in range(7):
+        lo_idx = np.array([i for i in range(HEAD_DIM) if not (i >> bit) & 1])
+        hi_idx = lo_idx + (1 << bit)
+        a = y[..., lo_idx]
+        b = y[..., hi_idx]
+        y[..., lo_idx] = a + b                            # float32 arithmetic
+        y[..., hi_idx] = a - b
+    return (y * HADAMARD_SCALE_F32).astype(np.float32)
+
+
+def fp16_floor(v: np.ndarray) -> np.ndarray:
+    """Largest fp16 value <= v (elementwise, |v| within the fp16 range)."""
+    v = np.asarray(v, dtype=np.float64)
+    h = v.astype(np.float16)                              # nearest
+    above = h.astype(np.float64) > v
+    h = np.where(above, np.nextafter(h, np.float16(-np.inf)), h)
+    return h.astype(np.float16)
+
+
+def quantize_rows_rotated(x: np.ndarray, L: int):
+    """Hadamard-rotated affine quantization of fp16 rows.
+
+    y = rotate_rows_f32(x); min = fp16_floor(min y) (so that every y - min >=
+    0 is representable by the codes); scale = smallest fp16 >= (max y -
+    min) / (L - 1); codes = clamp(round_half_even((y - min) / scale), 0,
+    L - 1), the division and the rounding decided exactly.
+    Returns (codes int64[..., 128], scale fp16[...], minimum fp16[...]).
+    """
+    y = rotate_rows_f32(x).astype(np.float64)             # float32 values, exact in float64
+    lo = fp16_floor(y.min(axis=-1)).astype(np.float64) + 0.0
+    hi = y.max(axis=-1)
+    s16 = scale_fp16_ceil(lo, hi, L)
+    s64 = s16.astype(np.float64)
+    safe = np.where(s64 > 0, s64, 1.0)
+    num = y - lo[..., None]                               # exact: float32 - fp16 in float64
+    codes = np.rint(num / safe[..., None])
+    # settle near-ties exactly: compare num with (c +/- 1/2) * scale, all exact in float64
+    half = (codes + 0.5) * safe[..., None]                # products of <= 17 + 11 bits: exact
+    below = (codes - 0.5) * safe[..., None]
+    codes = np.where(num > half, codes + 1, codes)
+    codes = np.where(num < below, codes - 1, codes)
+    tie_up = num == half
+    tie_dn = num == below
+    codes = np.where(tie_up & (codes % 2 == 1), codes + 1, codes)
+    codes = np.where(tie_dn & (codes % 2 == 1), codes - 1, codes)
     codes = np.clip(codes, 0, L - 1)
     codes = np.where((s64 > 0)[..., None], codes, 0.0)
     return codes.astype(np.int64), s16, lo.astype(np.float16)
@@ -254,16 +337,20 @@ class Pools:
     codes_low: np.ndarray
     meta_low: np.ndarray
     tok_low: np.ndarray
+    rotate: bool = False        # rows hold Hadamard-rotated values
 
 
 def quantize_pack_cache(K: np.ndarray, V: np.ndarray, perm: np.ndarray, k_high: int,
-                        L_high: int, L_low: int, token_base: int = 0) -> Pools:
+                        L_high: int, L_low: int, token_base: int = 0,
+                        rotate: bool = False) -> Pools:
     """Quantize and pack every row of K and V [B][layers][kv][n][128].
 
     Slot j of the high pool holds token perm[b][j] (j < k_high); slot j of the
     low pool holds token perm[b][k_high + j].  Both K and V of a token use the
-    same level count (SemKV Fig. 5).  tok_* records token_base + token.
+    same level count (SemKV Fig. 5).  tok_* records token_base + token.  With
+    rotate, rows are quantized by quantize_rows_rotated.
     """
+    qrows = quantize_rows_rotated if rotate else quantize_rows
     K = np.asarray(K, dtype=np.float16)
     V = np.asarray(V, dtype=np.float16)
     perm = np.asarray(perm)
@@ -272,11 +359,11 @@ def quantize_pack_cache(K: np.ndarray, V: np.ndarray, perm: np.ndarray, k_high: 
     out = {}
     for name, L, sel in (("high", L_high, perm[:, :k_high]), ("low", L_low, perm[:, k_high:])):
         rows = np.stack([kv[b][:, :, :, sel[b], :] for b in range(B)])   # [B][l][g][2][rows][128]
-        codes, s16, m16 = quantize_rows(rows, L)
+        codes, s16, m16 = qrows(rows, L)
         out["codes_" + name] = pack_rows(codes, L)
         out["meta_" + name] = np.stack([fp16_bits(s16), fp16_bits(m16)], axis=-1)
         out["tok_" + name] = (sel + token_base).astype(np.int32)
-    return Pools(L_high=L_high, L_low=L_low, **out)
+    return Pools(L_high=L_high, L_low=L_low, rotate=rotate, **out)
 
 
 def dequantize_pool(codes: np.ndarray, meta: np.ndarray, L: int) -> np.ndarray:
@@ -316,8 +403,13 @@ def decode_attention(q: np.ndarray, pools: Pools, sm_scale: float, layer0: int =
     tail_kv fp16 [B][layers][kv][2][block][128]; its first n_tail rows are
             the not-yet-quantized newest tokens, read exactly
     returns float64 [B][nl][Hq][128]
+
+    With rotated pools the attention runs in the rotated domain: the query
+    and the tail rows are rotated exactly (H q, H k, H v; logits are
+    unchanged since H is orthogonal) and the output is rotated back, H o.
     """
     q = np.asarray(q, dtype=np.float16).astype(np.float64)
+    H = hadamard128() if pools.rotate else None
     B, nl, Hq, _ = q.shape
     Hkv = pools.codes_high.shape[2]
     group = Hq // Hkv
@@ -335,13 +427,18 @@ def decode_attention(q: np.ndarray, pools: Pools, sm_scale: float, layer0: int =
                 parts_v.append(x[:, 1])
             if tail_kv is not None and n_tail > 0:
                 t = np.asarray(tail_kv[b, layer], dtype=np.float16).astype(np.float64)
+                if H is not None:
+                    t = t @ H                             # each row r -> H r (H symmetric)
                 parts_k.append(t[:, 0, :n_tail])
                 parts_v.append(t[:, 1, :n_tail])
             keys = np.concatenate(parts_k, axis=1)        # [kv][T][128]
             vals = np.concatenate(parts_v, axis=1)
             for h in range(Hq):
                 g = h // group
-                out[b, li, h] = attention(q[b, li, h], keys[g], vals[g], sm_scale)
+                if H is None:
+                    out[b, li, h] = attention(q[b, li, h], keys[g], vals[g], sm_scale)
+                else:
+                    out[b, li, h] = H @ attention(H @ q[b, li, h], keys[g], vals[g], sm_scale)
     return out
 
 
