@@ -62,6 +62,15 @@ typedef struct {
   int32_t L_high, L_low;   /* 3 <= L_low <= L_high <= 65536                  */
   int32_t block;           /* generation block (SemKV Fig. 6), 1..1024       */
   int64_t cap_high, cap_low; /* rows per (b, layer, kv head, K|V); multiple of 16 */
+  int32_t rotate;          /* 0, or 1: Hadamard rotation of every row before
+                            * quantization (SemKV Table 2's quantizer; H is the
+                            * normalized Sylvester H_128, applied in fp32 by
+                            * index-bit butterflies; the row minimum is rounded
+                            * down to fp16).  Decode rotates the queries and
+                            * rotates the outputs back.  With rotate = 1: levels
+                            * (6, 5), 4 query heads per KV head, no generation
+                            * (semkv_append_block returns EUNSUPPORTED); rotated
+                            * rows must stay within the fp16 range. */
 } semkv_geom;
 
 /* A mixed-precision cache.  All buffers are caller-owned device memory whose

@@ -24,6 +24,9 @@ semkv_status check_geom(const semkv_geom* g) {
   if (g->cap_high < 0 || g->cap_low < 0 || g->cap_high % 16 != 0 || g->cap_low % 16 != 0)
     return SEMKV_EINVAL;
   if (g->cap_high > (int64_t)INT32_MAX || g->cap_low > (int64_t)INT32_MAX) return SEMKV_EINVAL;
+  if (g->rotate != 0 && g->rotate != 1) return SEMKV_EINVAL;
+  if (g->rotate && (g->L_high != 6 || g->L_low != 5 || g->q_heads != 4 * g->kv_heads))
+    return SEMKV_EUNSUPPORTED;
   return SEMKV_OK;
 }
 
@@ -98,6 +101,7 @@ QuantArgs quant_args(const semkv_cache* c, const uint16_t* k, const uint16_t* v,
   a.fmt[0] = row_fmt(c->g.L_high);
   a.fmt[1] = row_fmt(c->g.L_low);
   a.token_base = token_base;
+  a.rotate = c->g.rotate;
   return a;
 }
 
@@ -158,6 +162,9 @@ semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0
     if (units * a->nchunks * per_chunk_bytes > ws_bytes && c2 < chunk) set_chunk(chunk);
   }
   a->ws = reinterpret_cast<float*>(ws);
+  a->rotate = g.rotate;
+  // rotated caches decode on the matrix-core path only (levels 6/5, group 4)
+  if (a->rotate && !decode_use_mfma(*a)) return SEMKV_EUNSUPPORTED;
   const int64_t need = units * a->nchunks * per_chunk_bytes;
   if (!ws || !aligned(ws, 256) || ws_bytes < need) return SEMKV_EWORKSPACE;
   return SEMKV_OK;
@@ -243,6 +250,7 @@ semkv_status semkv_append_block(semkv_cache* c, const uint16_t* k_new, const uin
                                 void* stream) {
   semkv_status st = check_cache(c);
   if (st != SEMKV_OK) return st;
+  if (c->g.rotate) return SEMKV_EUNSUPPORTED;   // generation over rotated pools: not built
   if (t_new < 0 || !(r >= 0.0 && r <= 1.0)) return SEMKV_EINVAL;
   if (t_new > 0) {
     if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) || !strides_ok(strides))

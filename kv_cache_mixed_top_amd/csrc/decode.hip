@@ -25,6 +25,7 @@ constexpr int kTile = 64;
 constexpr int kChunkMax = 1024;
 constexpr int kStageBytes = kTile * 256 + 64;
 constexpr int kPartialStride = 2 + kHeadDim;   // m, l, o[128]
+constexpr float kHadamardScale = 0.08838834764831845f;   // 1/sqrt(128), fp32
 
 __device__ __forceinline__ float block_reduce(float v, float* buf, bool is_max) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -612,18 +613,44 @@ __global__ __launch_bounds__(P * kHeadDim) void decode_merge_kernel(DecodeArgs a
     for (int e = 0; e < 4; ++e) num = fmaf(wch[c + e * kMergeParts], v[e], num);
   }
   for (; c < nc; c += kMergeParts) num = fmaf(wch[c], pd[(int64_t)c * step], num);
-  if (P == 1) {
-    a.out[(((int64_t)b * a.nl + li) * a.q_heads + h) * kHeadDim + d] = num / den;
+  float* out = a.out + (((int64_t)b * a.nl + li) * a.q_heads + h) * kHeadDim;
+  if (P == 1 && !a.rotate) {
+    out[d] = num / den;
     return;
   }
-  part[pi][d] = num;
-  __syncthreads();
-  if (pi == 0) {
-    num = part[0][d];
+  float val = 0.f;
+  if (P == 1) {
+    val = num / den;
+  } else {
+    part[pi][d] = num;
+    __syncthreads();
+    if (pi == 0) {
+      num = part[0][d];
 #pragma unroll
-    for (int k = 1; k < kMergeParts; ++k) num += part[k][d];
-    a.out[(((int64_t)b * a.nl + li) * a.q_heads + h) * kHeadDim + d] = num / den;
+      for (int k = 1; k < kMergeParts; ++k) num += part[k][d];
+      val = num / den;
+    }
   }
+  if (a.rotate) {
+    // rotated cache: the output is rotated back, o -> H o, across the 128
+    // threads of chunk group 0 (index bits 0-5 within a wave, bit 6 across
+    // the two waves through LDS)
+    __shared__ float xch[kHeadDim];
+    if (pi == 0) {
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float p = __shfl_xor(val, m, 64);
+        val = (d & m) ? p - val : val + p;
+      }
+      xch[d] = val;
+    }
+    __syncthreads();
+    if (pi == 0) {
+      const float p = xch[d ^ 64];
+      val = ((d & 64) ? p - val : val + p) * kHadamardScale;
+    }
+  }
+  if (pi == 0) out[d] = val;
 }
 
 // Merge of one (sequence, layer, KV head) with 4 query heads by one wave,
@@ -676,9 +703,25 @@ __global__ __launch_bounds__(64) void decode_merge_unit_kernel(DecodeArgs a) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float d = __shfl(den, h, 64);
+    float o0 = num[h][0] / d, o1 = num[h][1] / d;            // dimensions lane, lane + 64
+    if (a.rotate) {
+      // rotated cache: o -> H o (index bit 6 within the lane, bits 0-5 across lanes)
+      const float s0 = o0 + o1, s1 = o0 - o1;
+      o0 = s0;
+      o1 = s1;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(o0, m, 64), p1 = __shfl_xor(o1, m, 64);
+        const bool upper = (lane & m) != 0;
+        o0 = upper ? p0 - o0 : o0 + p0;
+        o1 = upper ? p1 - o1 : o1 + p1;
+      }
+      o0 *= kHadamardScale;
+      o1 *= kHadamardScale;
+    }
     float* o = a.out + (((int64_t)b * a.nl + li) * a.q_heads + g * G + h) * kHeadDim;
-    o[lane] = num[h][0] / d;
-    o[lane + 64] = num[h][1] / d;
+    o[lane] = o0;
+    o[lane + 64] = o1;
   }
 }
 

@@ -608,6 +608,7 @@ struct Stage2 {
   uint8_t *v0, *v1;            // wave 1 staging
   float *z0, *z1;              // logits of the last two tiles, [4][kTile] + maxima [4]
   _Float16* w;                 // wave 1: weights hi, lo, [2 * 4 * kTile]
+  _Float16* qr;                // wave 0: the rotated queries of a rotated cache, [4][128]
   __device__ uint8_t* k(int b) const { return b ? k1 : k0; }
   __device__ uint8_t* v(int b) const { return b ? v1 : v0; }
   __device__ float* z(int b) const { return b ? z1 : z0; }
@@ -727,7 +728,8 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   if (ir0 < ir1) issue(0, ir0);
   const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
                        (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
-  {
+  // A fragments and per-head sums from the 4 heads' queries at `qs`
+  auto load_queries = [&](const _Float16* qs) {
     const int head = lane & 3, blk = lane >> 2;
 #pragma unroll
     for (int P = 0; P < 3; ++P) {
@@ -737,15 +739,38 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = qk_slot_dim<L>(s, i);
-          v[i] = d >= 0 ? qg[head * kHeadDim + d] : (_Float16)0.0f;
+          v[i] = d >= 0 ? qs[head * kHeadDim + d] : (_Float16)0.0f;
         }
       }
       qf[P] = v;
     }
-  }
 #pragma unroll
-  for (int h = 0; h < 4; ++h)
-    sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
+    for (int h = 0; h < 4; ++h)
+      sumq[h] = wave_sum((float)qs[h * kHeadDim + 2 * lane] + (float)qs[h * kHeadDim + 2 * lane + 1]);
+  };
+  if (a.rotate) {
+    // rotated cache: q -> H q in fp32 (lane holds dimensions 2 lane, 2 lane + 1:
+    // index bit 0 within the lane, bits 1-6 across lanes), rounded to fp16
+    constexpr float kRot = 0.08838834764831845f;   // 1/sqrt(128)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float x0 = (float)qg[h * kHeadDim + 2 * lane], x1 = (float)qg[h * kHeadDim + 2 * lane + 1];
+      float y0 = x0 + x1, y1 = x0 - x1;
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+        const bool upper = (lane & m) != 0;
+        y0 = upper ? p0 - y0 : y0 + p0;
+        y1 = upper ? p1 - y1 : y1 + p1;
+      }
+      st.qr[h * kHeadDim + 2 * lane] = (_Float16)(y0 * kRot);
+      st.qr[h * kHeadDim + 2 * lane + 1] = (_Float16)(y1 * kRot);
+    }
+    wait_lgkm0();   // the wave's LDS writes have landed
+    load_queries(st.qr);
+  } else {
+    load_queries(qg);
+  }
 
   for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 1
     tile(t0, std::integral_constant<int, 0>{});
@@ -933,7 +958,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   __shared__ __attribute__((aligned(16))) uint8_t k0[kBuf], k1[kBuf], v0[kBuf], v1[kBuf];
   __shared__ __attribute__((aligned(16))) float z0[4 * kTile + 4], z1[4 * kTile + 4];
   __shared__ __attribute__((aligned(16))) _Float16 w[2 * 4 * kTile];
+  __shared__ __attribute__((aligned(16))) _Float16 qr[4 * kHeadDim];
   Stage2 st;
+  st.qr = qr;
   st.k0 = k0;
   st.k1 = k1;
   st.v0 = v0;
@@ -1005,7 +1032,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int pool_chunks = a.nch[0] + a.nch[1];
   if (pool_chunks == 0) return hipSuccess;
   dim3 grid(pool_chunks, a.nl * a.kv_heads, a.batch);
-  if (single_wave())
+  if (single_wave() && !a.rotate)   // the single-wave form reads unrotated queries only
     hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(64), 0, stream, a);
   else
     hipLaunchKernelGGL(decode_mfma2_kernel, grid, dim3(128), 0, stream, a);

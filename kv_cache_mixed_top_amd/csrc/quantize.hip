@@ -91,6 +91,47 @@ __device__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
     for (int i = 0; i < 32; ++i) v[i] = 0.f;
   }
 
+  // ---- optional Hadamard rotation of the row (normalized Sylvester H_128,
+  // fp32): butterflies on index bits 0 .. 6 in order -- bits 0-2 (e) and
+  // 5-6 (i) within the lane, bits 3-4 (q) across the quad -- each pair
+  // (a, b) -> (a + b, a - b), then one multiply by fp32(1/sqrt(128))
+  if (a.rotate) {
+#pragma unroll
+    for (int bit = 0; bit < 3; ++bit)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!((e >> bit) & 1)) {
+            const float x0 = v[8 * i + e], x1 = v[8 * i + e + (1 << bit)];
+            v[8 * i + e] = x0 + x1;
+            v[8 * i + e + (1 << bit)] = x0 - x1;
+          }
+#pragma unroll
+    for (int m = 1; m <= 2; m <<= 1) {                     // bits 3, 4: lane q ^ m
+      const bool upper = (q & m) != 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const float p = __shfl_xor(v[j], m, 64);
+        v[j] = upper ? p - v[j] : v[j] + p;
+      }
+    }
+#pragma unroll
+    for (int bit = 0; bit < 2; ++bit)                      // bits 5, 6: i ^ (1 << bit)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!((i >> bit) & 1))
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x0 = v[8 * i + e], x1 = v[8 * (i + (1 << bit)) + e];
+            v[8 * i + e] = x0 + x1;
+            v[8 * (i + (1 << bit)) + e] = x0 - x1;
+          }
+    const float kRot = 0.08838834764831845f;                // fp32(1/sqrt(128))
+#pragma unroll
+    for (int j = 0; j < 32; ++j) v[j] *= kRot;
+  }
+
   // ---- row min / max over the quad
   float lo = v[0], hi = v[0];
 #pragma unroll
@@ -102,6 +143,7 @@ __device__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
   lo = fminf(lo, __shfl_xor(lo, 2, 64));
   hi = fmaxf(hi, __shfl_xor(hi, 1, 64));
   hi = fmaxf(hi, __shfl_xor(hi, 2, 64));
+  if (a.rotate) lo = fp16_floor(lo);   // rotated values are fp32: the stored minimum is fp16
   lo = lo + 0.0f;   // a zero minimum is stored as +0
 
   const uint16_t sbits = scale_ceil_bits(lo, hi, f.L);
@@ -475,7 +517,7 @@ hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream) {
   const int tiles = tiles_high + tiles_low;
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, a.layers * a.kv_heads * 2, a.batch);
-  if (a.fmt[0].L == 6 && a.fmt[1].L == 5)
+  if (a.fmt[0].L == 6 && a.fmt[1].L == 5 && !a.rotate)
     hipLaunchKernelGGL((quantize_pack_kernel<6, 5>), grid, dim3(kThreads), 0, stream, a,
                        tiles_high);
   else

@@ -53,17 +53,25 @@ __device__ __forceinline__ uint16_t f2h(float f) {
 }
 
 // Smallest fp16 >= (hi - lo) / (L - 1), as bits; 0 when hi == lo.
-// hi - lo is exact in double; the correctly rounded double quotient has the
-// same fp16 ceiling as the exact quotient (a quotient that is not an fp16
-// value lies >= 2^-24/(L-1) from every fp16 value, far beyond the double
-// rounding error), and the ceiling is then settled by exact comparisons.
+// d = hi - lo is exact in double (float operands), and so is f * (L - 1) for
+// an fp16 f, so the ceiling is settled by exact comparisons of those
+// products with d, starting from the fp16 nearest the quotient.
 __device__ inline uint16_t scale_ceil_bits(float lo, float hi, int L) {
-  const double q = ((double)hi - (double)lo) / (double)(L - 1);
-  if (!(q > 0.0)) return 0;
-  uint16_t h = f2h((float)q);
-  while ((double)h2f(h) < q) ++h;                          // next fp16 up (q > 0)
-  while (h > 1 && (double)h2f((uint16_t)(h - 1)) >= q) --h;
+  const double d = (double)hi - (double)lo;
+  const double lm = (double)(L - 1);
+  if (!(d > 0.0)) return 0;
+  uint16_t h = f2h((float)(d / lm));
+  while ((double)h2f(h) * lm < d) ++h;                     // next fp16 up (d > 0)
+  while (h > 1 && (double)h2f((uint16_t)(h - 1)) * lm >= d) --h;
   return h;
+}
+
+// Largest fp16 <= v, as a float (v within the fp16 range).
+__device__ inline float fp16_floor(float v) {
+  uint16_t h = f2h(v);                                     // nearest
+  if (h2f(h) > v) h = (h & 0x8000u) ? (uint16_t)(h + 1)   // negative: away from zero
+                      : (h == 0 ? (uint16_t)0x8001u : (uint16_t)(h - 1));
+  return h2f(h);
 }
 
 }  // namespace semkv

@@ -24,6 +24,7 @@ struct QuantArgs {
   int64_t start[2];         // first destination slot (n_high, n_low)
   RowFmt fmt[2];
   int64_t token_base;       // tok_* = token_base + token
+  int32_t rotate;           // Hadamard-rotate every row before quantizing
 };
 hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream);
 
@@ -59,6 +60,7 @@ struct DecodeArgs {
   int32_t nchunks;
   int32_t x0;               // first chunk index handled by a launch
   float* ws;                // partials
+  int32_t rotate;           // rows are Hadamard-rotated: rotate q, rotate the output back
 };
 // Chunking rule shared by the launchers and the workspace query.
 int decode_chunk_tokens(int64_t tokens_per_unit, int64_t units);

@@ -32,7 +32,7 @@ SEMKV_OK, SEMKV_EINVAL, SEMKV_EUNSUPPORTED, SEMKV_ECAPACITY, SEMKV_EWORKSPACE, S
 class semkv_geom(ctypes.Structure):
     _fields_ = [("batch", c_i32), ("layers", c_i32), ("kv_heads", c_i32), ("q_heads", c_i32),
                 ("head_dim", c_i32), ("L_high", c_i32), ("L_low", c_i32), ("block", c_i32),
-                ("cap_high", c_i64), ("cap_low", c_i64)]
+                ("cap_high", c_i64), ("cap_low", c_i64), ("rotate", c_i32)]
 
 
 class semkv_cache(ctypes.Structure):
@@ -198,10 +198,11 @@ class SemKVCache:
     """
 
     def __init__(self, batch, layers, kv_heads, q_heads, L_high, L_low, cap_high, cap_low,
-                 block=128, device="cuda", max_decode_layers=None, max_tokens=None):
+                 block=128, device="cuda", max_decode_layers=None, max_tokens=None,
+                 rotate=False):
         g = semkv_geom(batch=batch, layers=layers, kv_heads=kv_heads, q_heads=q_heads,
                        head_dim=128, L_high=L_high, L_low=L_low, block=block,
-                       cap_high=cap_high, cap_low=cap_low)
+                       cap_high=cap_high, cap_low=cap_low, rotate=int(bool(rotate)))
         sizes = semkv_cache_sizes(g)
         self.geom = g
         dev = torch.device(device)

@@ -50,6 +50,11 @@ def geom(**kw):
     return sk.semkv_geom(**d)
 
 
+def test_rotated_geometry_accepted():
+    out = (ctypes.c_int64 * 8)()
+    assert sk._lib.semkv_cache_sizes(ctypes.byref(geom(rotate=1)), out) == sk.SEMKV_OK
+
+
 def test_cache_sizes():
     s = sk.semkv_cache_sizes(geom())
     planes = 32 * 8 * 2
@@ -67,6 +72,9 @@ def test_cache_sizes():
     (dict(cap_high=100), sk.SEMKV_EINVAL),
     (dict(block=0), sk.SEMKV_EINVAL),
     (dict(batch=0), sk.SEMKV_EINVAL),
+    (dict(rotate=2), sk.SEMKV_EINVAL),
+    (dict(rotate=1, L_high=8, L_low=6), sk.SEMKV_EUNSUPPORTED),
+    (dict(rotate=1, q_heads=16), sk.SEMKV_EUNSUPPORTED),
 ])
 def test_geometry_validation(bad, status):
     out = (ctypes.c_int64 * 8)()
