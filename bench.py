@@ -66,6 +66,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="decode steps per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rotate", action="store_true",
+                    help="Hadamard-rotated cache (the optional quantizer rotation); a variant of "
+                         "the workload, not its headline: no extra legs, no CPU baseline")
     ap.add_argument("--cpu-layers", type=int, default=16,
                     help="layers of the bounded oracle sample")
     ap.add_argument("--no-extra", action="store_true",
@@ -121,7 +124,7 @@ def main():
             scores = torch.rand((B, n), generator=g, device=dev)
         q = W.make_q_torch(w, D, dev)
         cache = sk.SemKVCache(B, layers, kv, Hq, w.L_high, w.L_low, cap16(k), cap16(n - k),
-                              block=w.block, max_tokens=n)
+                              block=w.block, max_tokens=n, rotate=args.rotate)
         perm = torch.empty((B, n), dtype=torch.int32, device=dev)
         mask = torch.empty((B, (n + 31) // 32), dtype=torch.int32, device=dev)
         out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device=dev)
@@ -221,7 +224,7 @@ def main():
         "config": {"workload": args.workload, "batch": B, "layers": layers, "kv_heads": kv,
                    "q_heads": Hq, "head_dim": 128, "tokens": n, "r": w.r,
                    "levels": [w.L_high, w.L_low], "decode_steps": D,
-                   "v_dist": w.v_dist, "score": w.score},
+                   "v_dist": w.v_dist, "score": w.score, "rotate": bool(args.rotate)},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "quantize_pack": {"ms": round(ms_quant, 4), "GB/s": round(quant_gbs, 1),
                           "pct_hbm_peak": round(100.0 * quant_gbs / HBM_PEAK_GBS, 2),
@@ -240,7 +243,7 @@ def main():
         "cpu_baseline": None,
     }
 
-    if not args.no_extra:
+    if not args.no_extra and not args.rotate:
         result["decode_graph_per_layer"] = graph_leg(sk, torch, cache, q, D, layers, B, Hq,
                                                      decode_bytes, stream)
         log(f"per-layer graph: {result['decode_graph_per_layer']['us_per_step']} us/step")
@@ -254,7 +257,7 @@ def main():
             f"{g['decode_tokens/s']} tok/s; block quantize {g['block_quantize_us']} us")
         K = V = None
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.rotate:
         import cpu_baseline
         import oracle as O
         ls = max(1, min(args.cpu_layers, layers))

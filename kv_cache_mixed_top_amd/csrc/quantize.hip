@@ -47,10 +47,60 @@ __device__ __forceinline__ float exact_code(float x, float m, float s, float c0)
   return c0;
 }
 
+// Exchange with lane ^ 1 / lane ^ 2 inside each quad (DPP quad permutes).
+__device__ __forceinline__ float quad_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+
+// Hadamard rotation of one row held by a quad (normalized Sylvester H_128,
+// fp32), the lane holding dims 8q + 32i + e as v[8i + e]: butterflies on the
+// index bits 0 .. 6 in order -- bits 0-2 (e) and 5-6 (i) within the lane,
+// bits 3-4 (q) across the quad -- each pair (a, b) -> (a + b, a - b), then
+// one multiply by fp32(1/sqrt(128)).
+__device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (!((e >> bit) & 1)) {
+          const float x0 = v[8 * i + e], x1 = v[8 * i + e + (1 << bit)];
+          v[8 * i + e] = x0 + x1;
+          v[8 * i + e + (1 << bit)] = x0 - x1;
+        }
+#pragma unroll
+  for (int m = 1; m <= 2; m <<= 1) {                       // bits 3, 4: lane q ^ m
+    const bool upper = (q & m) != 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float p = m == 1 ? quad_xor1(v[j]) : quad_xor2(v[j]);
+      v[j] = upper ? p - v[j] : v[j] + p;
+    }
+  }
+#pragma unroll
+  for (int bit = 0; bit < 2; ++bit)                        // bits 5, 6: i ^ (1 << bit)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (!((i >> bit) & 1))
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x0 = v[8 * i + e], x1 = v[8 * (i + (1 << bit)) + e];
+          v[8 * i + e] = x0 + x1;
+          v[8 * (i + (1 << bit)) + e] = x0 - x1;
+        }
+  constexpr float kRot = 0.08838834764831845f;             // fp32(1/sqrt(128))
+#pragma unroll
+  for (int j = 0; j < 32; ++j) v[j] *= kRot;
+}
+
 // One 64-slot tile of one pool plane.  LF = level count known at compile
 // time (6 or 5), or 0 for the runtime format of the pool.
-template <int LF>
-__device__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
+template <int LF, bool kRot>
+__device__ __forceinline__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
                               uint16_t* codes) {
   const RowFmt f = LF ? row_fmt(LF) : a.fmt[pool];
   const int count = pool == 0 ? a.k_high : a.n - a.k_high;
@@ -91,46 +141,8 @@ __device__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
     for (int i = 0; i < 32; ++i) v[i] = 0.f;
   }
 
-  // ---- optional Hadamard rotation of the row (normalized Sylvester H_128,
-  // fp32): butterflies on index bits 0 .. 6 in order -- bits 0-2 (e) and
-  // 5-6 (i) within the lane, bits 3-4 (q) across the quad -- each pair
-  // (a, b) -> (a + b, a - b), then one multiply by fp32(1/sqrt(128))
-  if (a.rotate) {
-#pragma unroll
-    for (int bit = 0; bit < 3; ++bit)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!((e >> bit) & 1)) {
-            const float x0 = v[8 * i + e], x1 = v[8 * i + e + (1 << bit)];
-            v[8 * i + e] = x0 + x1;
-            v[8 * i + e + (1 << bit)] = x0 - x1;
-          }
-#pragma unroll
-    for (int m = 1; m <= 2; m <<= 1) {                     // bits 3, 4: lane q ^ m
-      const bool upper = (q & m) != 0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const float p = __shfl_xor(v[j], m, 64);
-        v[j] = upper ? p - v[j] : v[j] + p;
-      }
-    }
-#pragma unroll
-    for (int bit = 0; bit < 2; ++bit)                      // bits 5, 6: i ^ (1 << bit)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!((i >> bit) & 1))
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x0 = v[8 * i + e], x1 = v[8 * (i + (1 << bit)) + e];
-            v[8 * i + e] = x0 + x1;
-            v[8 * (i + (1 << bit)) + e] = x0 - x1;
-          }
-    const float kRot = 0.08838834764831845f;                // fp32(1/sqrt(128))
-#pragma unroll
-    for (int j = 0; j < 32; ++j) v[j] *= kRot;
-  }
+  // ---- optional Hadamard rotation of the row
+  if constexpr (kRot) rotate_row(v, q);
 
   // ---- row min / max over the quad
   float lo = v[0], hi = v[0];
@@ -143,7 +155,7 @@ __device__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
   lo = fminf(lo, __shfl_xor(lo, 2, 64));
   hi = fmaxf(hi, __shfl_xor(hi, 1, 64));
   hi = fmaxf(hi, __shfl_xor(hi, 2, 64));
-  if (a.rotate) lo = fp16_floor(lo);   // rotated values are fp32: the stored minimum is fp16
+  if constexpr (kRot) lo = fp16_floor(lo);   // rotated values are fp32: the stored minimum is fp16
   lo = lo + 0.0f;   // a zero minimum is stored as +0
 
   const uint16_t sbits = scale_ceil_bits(lo, hi, f.L);
@@ -282,16 +294,10 @@ __device__ __forceinline__ uint16_t scale_ceil_fast(float lo, float hi) {
   return h;
 }
 
-// Exchange with lane ^ 1 / lane ^ 2 inside each quad (DPP quad permutes).
-__device__ __forceinline__ float quad_xor1(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float quad_xor2(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-}
 
-template <int L>
-__device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_pool,
+// kRot: the rows are Hadamard-rotated (fp32 values kept in registers).
+template <int L, bool kRot>
+__device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_pool,
                                    uint8_t* codes8, uint8_t* img) {
   constexpr int R = L == 6 ? 43 : 38;
   const int count = pool == 0 ? a.k_high : a.n - a.k_high;
@@ -330,19 +336,36 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
     for (int i = 0; i < 16; ++i) v[i] = (half2_t){0, 0};
   }
 
-  // ---- row min / max: packed fp16 (exact), then the quad
-  half2_t mn = v[0], mx = v[0];
+  // ---- row min / max: packed fp16 (exact), then the quad; rotated rows:
+  // fp32 values, the stored minimum rounded down to fp16
+  float yr[kRot ? 32 : 1];
+  float lo, hi;
+  if constexpr (kRot) {
 #pragma unroll
-  for (int i = 1; i < 16; ++i) {
-    mn = __builtin_elementwise_minimum(mn, v[i]);
-    mx = __builtin_elementwise_maximum(mx, v[i]);
+    for (int k = 0; k < 32; ++k) yr[k] = (float)v[k >> 1][k & 1];
+    rotate_row(yr, q);
+    lo = yr[0];
+    hi = yr[0];
+#pragma unroll
+    for (int k = 1; k < 32; ++k) {
+      lo = fminf(lo, yr[k]);
+      hi = fmaxf(hi, yr[k]);
+    }
+  } else {
+    half2_t mn = v[0], mx = v[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      mn = __builtin_elementwise_minimum(mn, v[i]);
+      mx = __builtin_elementwise_maximum(mx, v[i]);
+    }
+    lo = fminf((float)mn[0], (float)mn[1]);
+    hi = fmaxf((float)mx[0], (float)mx[1]);
   }
-  float lo = fminf((float)mn[0], (float)mn[1]);
-  float hi = fmaxf((float)mx[0], (float)mx[1]);
   lo = fminf(lo, quad_xor1(lo));
   lo = fminf(lo, quad_xor2(lo));
   hi = fmaxf(hi, quad_xor1(hi));
   hi = fmaxf(hi, quad_xor2(hi));
+  if constexpr (kRot) lo = fp16_floor(lo);
   lo = lo + 0.0f;   // a zero minimum is stored as +0
 
   const uint16_t sbits = scale_ceil_fast<L>(lo, hi);
@@ -379,7 +402,7 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   uint32_t umin[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};   // per 8 values
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const float y = fmaf((float)v[k >> 1][k & 1], rs, nb10);
+    const float y = fmaf(kRot ? yr[k & (kRot ? 31 : 0)] : (float)v[k >> 1][k & 1], rs, nb10);
     umin[k >> 3] = min(umin[k >> 3], (__builtin_bit_cast(uint32_t, y) << 12) + bias);
     cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(y, k & 3, (k & 3) ? cw[k >> 2] : 0u);
   }
@@ -392,7 +415,22 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
   uint32_t flag = 0u;   // groups of 8 values with a value near a half-integer
 #pragma unroll
   for (int i = 0; i < 4; ++i) flag |= (uint32_t)(wide || umin[i] <= thr) << i;
-  if (flag) {
+  if (kRot && flag) {
+    // rotated rows: the values are still in registers
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (!((flag >> i) & 1u)) continue;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = yr[(8 * i + e) & (kRot ? 31 : 0)];
+        const float y = fmaf(x, rs, nb10);
+        if (wide || (__builtin_bit_cast(uint32_t, y) << 12) + bias <= thr) {
+          const float c = exact_code(x, lo, sq, rintf(y - 10.0f));
+          crow[8 * q + 32 * i + e] = (uint8_t)((int)c + 10);
+        }
+      }
+    }
+  } else if (flag) {
     // Rare per group: one of its values lies near a half-integer (with fp16
     // data nearly always an exact tie).  The group's 8 values are read
     // again, and those near a half-integer are settled exactly and their
@@ -486,7 +524,7 @@ __device__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_poo
     store_stream(dst + i, reinterpret_cast<const uint4*>(img)[i]);
 }
 
-template <int LH, int LL>
+template <int LH, int LL, bool kRot = false>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, int tiles_high) {
   constexpr int kGeneric = kRows * kCodeStride * 2;
   constexpr int kFast = kCode8Bytes + kImgBytes;
@@ -497,14 +535,14 @@ __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, in
   const bool aligned16 = (a.start[pool] & 15) == 0;
   if (pool == 0) {
     if (LH != 0 && aligned16)
-      quantize_tile_fast<LH == 0 ? 6 : LH>(a, 0, t, smem, smem + kCode8Bytes);
+      quantize_tile_fast<LH == 0 ? 6 : LH, kRot>(a, 0, t, smem, smem + kCode8Bytes);
     else
-      quantize_tile<LH>(a, 0, t, reinterpret_cast<uint16_t*>(smem));
+      quantize_tile<LH, kRot>(a, 0, t, reinterpret_cast<uint16_t*>(smem));
   } else {
     if (LL != 0 && aligned16)
-      quantize_tile_fast<LL == 0 ? 5 : LL>(a, 1, t, smem, smem + kCode8Bytes);
+      quantize_tile_fast<LL == 0 ? 5 : LL, kRot>(a, 1, t, smem, smem + kCode8Bytes);
     else
-      quantize_tile<LL>(a, 1, t, reinterpret_cast<uint16_t*>(smem));
+      quantize_tile<LL, kRot>(a, 1, t, reinterpret_cast<uint16_t*>(smem));
   }
 }
 
@@ -517,7 +555,10 @@ hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream) {
   const int tiles = tiles_high + tiles_low;
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, a.layers * a.kv_heads * 2, a.batch);
-  if (a.fmt[0].L == 6 && a.fmt[1].L == 5 && !a.rotate)
+  if (a.fmt[0].L == 6 && a.fmt[1].L == 5 && a.rotate)
+    hipLaunchKernelGGL((quantize_pack_kernel<6, 5, true>), grid, dim3(kThreads), 0, stream, a,
+                       tiles_high);
+  else if (a.fmt[0].L == 6 && a.fmt[1].L == 5)
     hipLaunchKernelGGL((quantize_pack_kernel<6, 5>), grid, dim3(kThreads), 0, stream, a,
                        tiles_high);
   else
