@@ -404,12 +404,16 @@ def decode_attention(q: np.ndarray, pools: Pools, sm_scale: float, layer0: int =
             the not-yet-quantized newest tokens, read exactly
     returns float64 [B][nl][Hq][128]
 
-    With rotated pools the attention runs in the rotated domain: the query
-    and the tail rows are rotated exactly (H q, H k, H v; logits are
-    unchanged since H is orthogonal) and the output is rotated back, H o.
+    With rotated pools the attention runs in the rotated domain (logits are
+    unchanged since H is orthogonal): the query is rotated as the cache rows
+    are (float32 butterflies) and kept at the query's own precision, fp16;
+    the tail rows are rotated exactly (H k, H v); the output is rotated
+    back, H o.
     """
-    q = np.asarray(q, dtype=np.float16).astype(np.float64)
     H = hadamard128() if pools.rotate else None
+    if H is not None:
+        q = rotate_rows_f32(np.asarray(q, dtype=np.float16)).astype(np.float16)
+    q = np.asarray(q, dtype=np.float16).astype(np.float64)
     B, nl, Hq, _ = q.shape
     Hkv = pools.codes_high.shape[2]
     group = Hq // Hkv
@@ -438,7 +442,7 @@ def decode_attention(q: np.ndarray, pools: Pools, sm_scale: float, layer0: int =
                 if H is None:
                     out[b, li, h] = attention(q[b, li, h], keys[g], vals[g], sm_scale)
                 else:
-                    out[b, li, h] = H @ attention(H @ q[b, li, h], keys[g], vals[g], sm_scale)
+                    out[b, li, h] = H @ attention(q[b, li, h], keys[g], vals[g], sm_scale)
     return out
 
 

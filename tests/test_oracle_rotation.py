@@ -112,8 +112,9 @@ def test_rotation_lowers_error_on_outlier_rows():
 
 def test_rotated_decode_near_lossless_at_65536_levels():
     """With 65536 levels the rotated cache holds the rotated rows to about
-    2^-16 of their range, so decode over it (query rotated, output rotated
-    back) must agree with attention on the raw fp16 rows."""
+    2^-16 of their range, so decode over it (query rotated and held in fp16,
+    output rotated back) must agree with attention on the raw fp16 rows for
+    the query that fp16 rotated query stands for, H fp16(H q)."""
     rng = np.random.default_rng(4)
     B, layers, kv, n, Hq = 1, 2, 2, 90, 8
     K = rng.standard_normal((B, layers, kv, n, 128)).astype(np.float16)
@@ -123,10 +124,12 @@ def test_rotated_decode_near_lossless_at_65536_levels():
     assert pools.rotate
     q = (rng.standard_normal((B, layers, Hq, 128)) / 11.3).astype(np.float16)
     got = O.decode_attention(q, pools, 1.0)
+    q_eff = O.rotate_rows_f32(q).astype(np.float16).astype(np.float64) @ sylvester(128) / math.sqrt(128)
+    assert np.max(np.abs(q_eff - q)) <= 2.0 ** -11 * np.max(np.abs(q)) * 4   # fp16 rounding, rotated back
     for b in range(B):
         for layer in range(layers):
             for h in range(Hq):
                 g = h // (Hq // kv)
-                ref = O.attention(q[b, layer, h].astype(np.float64), K[b, layer, g].astype(np.float64),
+                ref = O.attention(q_eff[b, layer, h], K[b, layer, g].astype(np.float64),
                                   V[b, layer, g].astype(np.float64), 1.0)
                 assert np.max(np.abs(got[b, layer, h] - ref)) <= 2e-4 * np.max(np.abs(ref))
