@@ -34,7 +34,9 @@ constexpr int kCodeStride = kHeadDim + 2;   // u16 codes per LDS row (pad)
 
 // Exact round-half-even of (x - m)/s given a candidate c0 within 1 of it.
 __device__ __forceinline__ float exact_code(float x, float m, float s, float c0) {
-  const double d = (double)x - (double)m;           // exact: fp16 operands
+  // exact for fp16 x; a rotated fp32 x rounds only when |x| << |m|, by less
+  // than the spacing of m + (c +/- 1/2) s, so the signs below still hold
+  const double d = (double)x - (double)m;
   const double sd = (double)s;
   const double c = (double)c0;
   const double e_hi = d - (c + 0.5) * sd;           // exact (<= 45 significant bits)
@@ -59,10 +61,17 @@ __device__ __forceinline__ float quad_xor2(float x) {
 // fp32), the lane holding dims 8q + 32i + e as v[8i + e]: butterflies on the
 // index bits 0 .. 6 in order -- bits 0-2 (e) and 5-6 (i) within the lane,
 // bits 3-4 (q) across the quad -- each pair (a, b) -> (a + b, a - b), then
-// one multiply by fp32(1/sqrt(128)).
+// one multiply by fp32(1/sqrt(128)).  kFrom: the first within-lane bit still
+// to do (1 when the caller has done bit 0 already); kScale = false leaves the
+// multiply to the caller.  Across the quad the lane's own value is added with
+// sign +1 (lower lane) or -1 (upper lane) in one fma, which rounds as the add
+// or subtract does.
+constexpr float kRotScale = 0.08838834764831845f;          // fp32(1/sqrt(128))
+
+template <int kFrom = 0, bool kScale = true>
 __device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
 #pragma unroll
-  for (int bit = 0; bit < 3; ++bit)
+  for (int bit = kFrom; bit < 3; ++bit)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -74,11 +83,11 @@ __device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
         }
 #pragma unroll
   for (int m = 1; m <= 2; m <<= 1) {                       // bits 3, 4: lane q ^ m
-    const bool upper = (q & m) != 0;
+    const float sgn = (q & m) ? -1.0f : 1.0f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const float p = m == 1 ? quad_xor1(v[j]) : quad_xor2(v[j]);
-      v[j] = upper ? p - v[j] : v[j] + p;
+      v[j] = fmaf(v[j], sgn, p);
     }
   }
 #pragma unroll
@@ -92,9 +101,10 @@ __device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
           v[8 * i + e] = x0 + x1;
           v[8 * (i + (1 << bit)) + e] = x0 - x1;
         }
-  constexpr float kRot = 0.08838834764831845f;             // fp32(1/sqrt(128))
+  if constexpr (kScale) {
 #pragma unroll
-  for (int j = 0; j < 32; ++j) v[j] *= kRot;
+    for (int j = 0; j < 32; ++j) v[j] *= kRotScale;
+  }
 }
 
 // One 64-slot tile of one pool plane.  LF = level count known at compile
@@ -341,9 +351,20 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
   float yr[kRot ? 32 : 1];
   float lo, hi;
   if constexpr (kRot) {
+    // bit 0 pairs are the two halves of one fp16 pair: a mixed-precision
+    // fma takes them straight from fp16 (exact product, one rounding).  The
+    // multiplier 1 is hidden from the optimizer, which would otherwise turn
+    // the fma into two conversions and an add.
+    float one = 1.0f;
+    asm volatile("" : "+v"(one));
 #pragma unroll
-    for (int k = 0; k < 32; ++k) yr[k] = (float)v[k >> 1][k & 1];
-    rotate_row(yr, q);
+    for (int k = 0; k < 16; ++k) {
+      yr[2 * k & (kRot ? 31 : 0)] = fmaf((float)v[k][1], one, (float)v[k][0]);
+      yr[(2 * k + 1) & (kRot ? 31 : 0)] = fmaf((float)v[k][1], -one, (float)v[k][0]);
+    }
+    // the sums u before the scaling: the rotated value is x = fl(u k), and
+    // as rounding is monotone the extremes are fl(min u k), fl(max u k)
+    rotate_row<1, false>(yr, q);
     lo = yr[0];
     hi = yr[0];
 #pragma unroll
@@ -351,6 +372,8 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
       lo = fminf(lo, yr[k]);
       hi = fmaxf(hi, yr[k]);
     }
+    lo *= kRotScale;
+    hi *= kRotScale;
   } else {
     half2_t mn = v[0], mx = v[0];
 #pragma unroll
@@ -375,7 +398,12 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
   // (within 1 ulp).  |y - (x - m)/s| <= 2^-23 (1.5 (L-1) + |m|/s) (1 + 2^-20);
   // a code whose y lies within 2^-22 ((L-1) + |m| r) of a half-integer is
   // settled exactly.  v_cvt_pk_u8_f32 rounds to nearest even and clamps to
-  // [0, 255], which is the code elsewhere.
+  // [0, 255], which is the code elsewhere.  Rotated rows take y = u fl(r k)
+  // - m r from the unscaled sum u; against x = fl(u k) that adds at most
+  // 2^-23 |x|/s (1 + 2^-22) <= 2^-23 ((L-1) + |m|/s) (1 + 2^-22), so their
+  // window is 2^-22 (1.5 (L-1) + 1.25 |m| r).  The settling itself starts
+  // from round((x - m) r) with x - m rounded once in fp32 (code error
+  // <= 2^-22 (L-1)), which is within 1 of the exact code whatever |m|/s.
   //
   // The fast pass computes y + 10 instead, which lies in [8, 16) where the
   // fraction is the low 20 mantissa bits: the distance of the fraction from
@@ -392,7 +420,9 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
   const float sq = s > 0.0f ? s : 1.0f;
   uint32_t cw[8];
   const float rs = __builtin_amdgcn_rcpf(sq);
-  const float eps = 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
+  const float eps = kRot ? 0x1p-22f * (1.5f * (float)(L - 1) + 1.25f * fabsf(lo) * rs) + 0x1p-30f
+                         : 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
+  const float rsk = kRot ? rs * kRotScale : rs;
   const float nb10 = fmaf(-lo, rs, 10.0f);
   const float win = (2.0f * eps + 0x1p-20f) * 1048576.0f;      // in units of 2^-20
   const bool wide = !(win < 131072.0f);                         // then every code is settled
@@ -402,7 +432,7 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
   uint32_t umin[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};   // per 8 values
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const float y = fmaf(kRot ? yr[k & (kRot ? 31 : 0)] : (float)v[k >> 1][k & 1], rs, nb10);
+    const float y = fmaf(kRot ? yr[k & (kRot ? 31 : 0)] : (float)v[k >> 1][k & 1], rsk, nb10);
     umin[k >> 3] = min(umin[k >> 3], (__builtin_bit_cast(uint32_t, y) << 12) + bias);
     cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(y, k & 3, (k & 3) ? cw[k >> 2] : 0u);
   }
@@ -422,10 +452,11 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
       if (!((flag >> i) & 1u)) continue;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = yr[(8 * i + e) & (kRot ? 31 : 0)];
-        const float y = fmaf(x, rs, nb10);
+        const float u = yr[(8 * i + e) & (kRot ? 31 : 0)];
+        const float y = fmaf(u, rsk, nb10);
         if (wide || (__builtin_bit_cast(uint32_t, y) << 12) + bias <= thr) {
-          const float c = exact_code(x, lo, sq, rintf(y - 10.0f));
+          const float x = u * kRotScale;
+          const float c = exact_code(x, lo, sq, rintf((x - lo) * rs));
           crow[8 * q + 32 * i + e] = (uint8_t)((int)c + 10);
         }
       }
@@ -445,7 +476,7 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
         const float x = h2f((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
         const float y = fmaf(x, rs, nb10);
         if (wide || (__builtin_bit_cast(uint32_t, y) << 12) + bias <= thr) {
-          const float c = exact_code(x, lo, sq, rintf(y - 10.0f));
+          const float c = exact_code(x, lo, sq, rintf((x - lo) * rs));
           crow[8 * q + 32 * i + e] = (uint8_t)((int)c + 10);
         }
       }

@@ -32,6 +32,16 @@ def _rows(rng, B, layers, kv, n, kind):
         K[..., 6, :] = 0.0                                # a zero row
         V[..., 2, :] *= 1e-3
         V[..., 9, 40] = 300.0
+        # rows along e0 rotate to (nearly) constant rows: a range of a few
+        # fp32 ulps above the fp16 floor of the minimum, so |m|/s is large
+        for j, (c, dl) in enumerate([(181.0, 0.0), (1000.0, 2.0 ** -13), (3.0, 2.0 ** -20),
+                                     (-77.5, 2.0 ** -16)]):
+            K[..., 10 + j, :] = 0.0
+            K[..., 10 + j, 0] = c
+            K[..., 10 + j, 1 + j] = dl
+            V[..., 10 + j, :] = 0.0
+            V[..., 10 + j, 0] = -c
+            V[..., 10 + j, 64] = dl
     return K.astype(np.float16), V.astype(np.float16)
 
 
