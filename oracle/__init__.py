@@ -9,4 +9,5 @@ from .semkv_oracle import (GenerationCache, Pools, attention, decode_attention, 
                            group_params, nominal_bits, pack_rows, quantize_pack_cache,
                            quantize_rows, rank_order, rank_topr, rank_topr_batch,
                            row_bytes, scale_fp16_ceil, topr_count, unpack_rows,
-                           hadamard128, rotate_rows_f32, fp16_floor, quantize_rows_rotated)
+                           hadamard128, rotate_rows_f32, fp16_floor, quantize_rows_rotated,
+                           score_keynorm)

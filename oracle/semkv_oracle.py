@@ -49,6 +49,26 @@ import numpy as np
 HEAD_DIM = 128
 
 # --------------------------------------------------------------------------
+# Scoring by key norm (SemKV Fig. 2: one model-internal indicator gives a
+# per-token score; SemKV Table 3 lists the key-norm indicator among the
+# variants; its exact form and layer window are open on the pages).
+# Reading: the score of token t is the sum, over the layers of a window and
+# every KV head, of the Euclidean norm of t's key row.  Only the order of the
+# scores matters to the ranking (SemKV Fig. 2), so no normalisation.
+# --------------------------------------------------------------------------
+
+
+def score_keynorm(K: np.ndarray, layer0: int, nlayers: int) -> np.ndarray:
+    """K fp16 [B][layers][kv][n][128] -> float64 [B][n]:
+    score[b, t] = sum over layers layer0 .. layer0+nlayers-1 and KV heads h
+    of sqrt(sum_d K[b, layer, h, t, d]^2)."""
+    K = np.asarray(K, dtype=np.float16).astype(np.float64)
+    rows = K[:, layer0:layer0 + nlayers]                  # [B][nl][kv][n][128]
+    norms = np.sqrt(np.sum(rows * rows, axis=-1))        # [B][nl][kv][n]
+    return norms.sum(axis=(1, 2))
+
+
+# --------------------------------------------------------------------------
 # Rank (SemKV Fig. 2: ranking within each prompt, no score normalisation;
 #       SemKV Fig. 4: the top-r tokens form the high-precision set H, no
 #       threshold is estimated; SemKV Fig. 5: one assignment per token,
