@@ -249,6 +249,9 @@ def main():
         log(f"per-layer graph: {result['decode_graph_per_layer']['us_per_step']} us/step")
         result["hbm_copy_context"] = copy_leg(torch, stream)
         log(f"copy context: {result['hbm_copy_context']['GB/s']} GB/s")
+        result["score_keynorm"] = score_leg(sk, torch, K, stream)
+        log(f"key-norm score: {result['score_keynorm']['us']} us, "
+            f"{result['score_keynorm']['GB/s']} GB/s")
         del K, V
         torch.cuda.empty_cache()
         result["generation"] = gen_leg(sk, W, torch, dev, stream, args.gen_steps)
@@ -338,6 +341,32 @@ def graph_leg(sk, torch, cache, q, D, layers, B, Hq, decode_bytes, stream):
             "GB/s": round(decode_bytes / (us * 1e-6) / 1e9, 1),
             "pct_hbm_peak": round(100.0 * decode_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "max_rel_diff_vs_one_launch": worst}
+
+
+def score_leg(sk, torch, K, stream, window=4, reps=10):
+    """Key-norm scores of the workload's K over its last `window` layers
+    (semkv_score_keynorm), mean of `reps` launches timed by HIP events on the
+    launch stream.  Algorithmic bytes: the window's key rows read once plus
+    the fp32 scores written."""
+    import numpy as np
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    B, layers, kv, n, D = K.shape
+    layer0 = max(0, layers - window)
+    nl = layers - layer0
+    scores = torch.empty((B, n), dtype=torch.float32, device=K.device)
+    sk.semkv_score_keynorm(K, scores, layer0, nl, stream=stream)
+    stream.synchronize()
+    ev = [(Ev(), Ev()) for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        sk.semkv_score_keynorm(K, scores, layer0, nl, stream=stream)
+        b.record(stream)
+    stream.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    nbytes = B * nl * kv * n * D * 2 + B * n * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"layers": [layer0, layers], "algorithmic_bytes": nbytes, "us": round(ms * 1e3, 2),
+            "GB/s": round(gbs, 1), "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
 
 
 def copy_leg(torch, stream, mib=2048):

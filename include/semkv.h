@@ -133,6 +133,25 @@ int64_t semkv_workspace_bytes(const semkv_geom* g, int32_t nlayers, int64_t max_
 semkv_status semkv_rank_topr(const float* scores, int32_t batch, int64_t n, int64_t ld_scores,
                              int64_t k, int32_t* perm, uint32_t* mask, void* stream);
 
+/* Key-norm token scores (SemKV Fig. 2: a per-token importance score from one
+ * model-internal indicator, ranked within the prompt; SemKV Table 3 lists the
+ * key-norm indicator; its form and layer window are not given there, and
+ * the reading here is the sum of the key rows' Euclidean norms).
+ *   scores[b * ld_scores + t] = sum over layers layer0 .. layer0+nlayers-1
+ *     and KV heads 0 .. kv_heads-1 of sqrt(sum_d k[b,layer,head,t,d]^2)
+ * accumulated in fp32, layer-major.  The result feeds semkv_rank_topr.
+ *  k        fp16 keys; element (b, layer, head, token, d) is at
+ *           k + b*strides[0] + layer*strides[1] + head*strides[2]
+ *             + token*strides[3] + d   (strides in elements, d contiguous;
+ *           every layer of the window must exist)
+ *  scores   fp32 [batch][ld_scores] device memory, first n of each row written
+ * Errors: EINVAL (null or misaligned pointers: k 16-byte, scores 4-byte;
+ * strides negative or not multiples of 8; batch outside [1, 65535];
+ * kv_heads, nlayers < 1; layer0 < 0; n < 1; ld_scores < n). */
+semkv_status semkv_score_keynorm(const uint16_t* k, const int64_t strides[4], int32_t batch,
+                                 int32_t kv_heads, int64_t n, int32_t layer0, int32_t nlayers,
+                                 float* scores, int64_t ld_scores, void* stream);
+
 /* Quantize and pack a prompt (SemKV Fig. 5 and Table 6).
  *  k, v     fp16 rows; element (b, layer, head, token, d) is at
  *           base + b*strides[0] + layer*strides[1] + head*strides[2]

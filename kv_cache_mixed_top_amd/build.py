@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsemkv.so")
 
-SOURCES = ["api.hip", "rank.hip", "quantize.hip", "decode.hip", "decode_mfma.hip", "append.hip"]
+SOURCES = ["api.hip", "score.hip", "rank.hip", "quantize.hip", "decode.hip", "decode_mfma.hip", "append.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -224,6 +224,29 @@ semkv_status semkv_rank_topr(const float* scores, int32_t batch, int64_t n, int6
                               (hipStream_t)stream));
 }
 
+semkv_status semkv_score_keynorm(const uint16_t* k, const int64_t strides[4], int32_t batch,
+                                 int32_t kv_heads, int64_t n, int32_t layer0, int32_t nlayers,
+                                 float* scores, int64_t ld_scores, void* stream) {
+  if (!k || !aligned(k, 16) || !strides_ok(strides)) return SEMKV_EINVAL;
+  if (batch < 1 || batch > 65535 || kv_heads < 1 || layer0 < 0 || nlayers < 1) return SEMKV_EINVAL;
+  if ((int64_t)nlayers * kv_heads > (int64_t)INT32_MAX) return SEMKV_EINVAL;
+  if (n < 1 || n > (int64_t)INT32_MAX || !scores || !aligned(scores, 4) || ld_scores < n)
+    return SEMKV_EINVAL;
+  ScoreArgs a;
+  a.k = k;
+  a.sb = strides[0];
+  a.sl = strides[1];
+  a.sh = strides[2];
+  a.st = strides[3];
+  a.n = n;
+  a.kv_heads = kv_heads;
+  a.layer0 = layer0;
+  a.nlayers = nlayers;
+  a.scores = scores;
+  a.ld = ld_scores;
+  return from_hip(launch_score_keynorm(a, batch, (hipStream_t)stream));
+}
+
 semkv_status semkv_quantize_pack(semkv_cache* c, const uint16_t* k, const uint16_t* v,
                                  const int64_t strides[4], int64_t n, const int32_t* perm,
                                  int64_t k_high, void* stream) {

@@ -1,0 +1,84 @@
+// Key-norm token scores (SemKV Fig. 2: a per-token importance score from one
+// model-internal indicator, ranked within the prompt; SemKV Table 3 lists the
+// key-norm indicator).  score[b][t] = sum over a window of layers and every
+// KV head of the Euclidean norm of token t's key row, accumulated in fp32
+// layer by layer, head by head (the same order for every token).
+//
+// Workgroup = 256 threads = 64 tokens x 4 lanes.  Lane q of a token reads the
+// 16-byte pieces at byte offsets 16q + 64i (i = 0..3) of each of the token's
+// rows, so one load instruction of a quad covers 64 contiguous bytes and the
+// 64 rows of one (layer, head) are one 16 KB run when the tokens are
+// contiguous.  The (layer, head) rows are streamed kAhead at a time: all
+// their loads are issued before the first is used.  Squares are summed by
+// mixed-precision fmas straight from fp16 (the products are exact in fp32).
+#include "semkv_internal.h"
+
+namespace semkv {
+namespace {
+
+constexpr int kTok = 64;
+constexpr int kThreads = 256;
+constexpr int kAhead = 4;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1, 64);
+  x += __shfl_xor(x, 2, 64);
+  return x;   // the same value on the quad's four lanes
+}
+
+__global__ __launch_bounds__(kThreads) void score_keynorm_kernel(ScoreArgs a) {
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, q = tid & 3;
+  const int b = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * kTok + r;
+  const bool valid = t < a.n;
+  const int total = a.nlayers * a.kv_heads;
+  const uint16_t* base = a.k + (int64_t)b * a.sb + t * a.st + 8 * q;
+
+  float acc = 0.0f;
+  for (int j0 = 0; j0 < total; j0 += kAhead) {
+    uint4 w[kAhead][4];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      const int lh = j0 + j;
+      if (valid && lh < total) {
+        const int layer = a.layer0 + lh / a.kv_heads;
+        const int head = lh % a.kv_heads;
+        const uint16_t* src = base + (int64_t)layer * a.sl + (int64_t)head * a.sh;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[j][i] = *reinterpret_cast<const uint4*>(src + 32 * i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[j][i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t ws[4] = {w[j][i].x, w[j][i].y, w[j][i].z, w[j][i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const half2_t h = __builtin_bit_cast(half2_t, ws[e]);
+          ss = fmaf((float)h[0], (float)h[0], ss);
+          ss = fmaf((float)h[1], (float)h[1], ss);
+        }
+      }
+      ss = quad_sum(ss);
+      if (j0 + j < total) acc += __builtin_sqrtf(ss);
+    }
+  }
+  if (valid && q == 0) a.scores[(int64_t)b * a.ld + t] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_score_keynorm(const ScoreArgs& a, int batch, hipStream_t stream) {
+  const dim3 grid((unsigned)((a.n + kTok - 1) / kTok), (unsigned)batch);
+  hipLaunchKernelGGL(score_keynorm_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace semkv

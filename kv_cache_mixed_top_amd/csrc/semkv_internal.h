@@ -5,6 +5,19 @@
 
 namespace semkv {
 
+// ---------------------------------------------------------------- score
+// Key-norm scores: scores[b * ld + t] = sum over layers layer0 ..
+// layer0 + nlayers - 1 and heads 0 .. kv_heads - 1 of |k row|_2.
+struct ScoreArgs {
+  const uint16_t* k;        // layer 0, head 0, token 0 of sequence 0
+  int64_t sb, sl, sh, st;   // element strides: batch, layer, head, token
+  int64_t n;                // tokens per sequence
+  int kv_heads, layer0, nlayers;
+  float* scores;
+  int64_t ld;               // row stride of scores
+};
+hipError_t launch_score_keynorm(const ScoreArgs& a, int batch, hipStream_t stream);
+
 // ---------------------------------------------------------------- rank
 // perm/mask of `batch` sequences of n scores each (row stride ld).
 hipError_t launch_rank(const float* scores, int batch, int n, int64_t ld, int k,

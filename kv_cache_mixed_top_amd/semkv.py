@@ -47,6 +47,8 @@ _SIGS = {
     "semkv_topr_count": (c_i64, [c_i64, c_f64]),
     "semkv_cache_sizes": (c_i32, [ctypes.POINTER(semkv_geom), ctypes.POINTER(c_i64)]),
     "semkv_workspace_bytes": (c_i64, [ctypes.POINTER(semkv_geom), c_i32, c_i64]),
+    "semkv_score_keynorm": (c_i32, [c_p, ctypes.POINTER(c_i64), c_i32, c_i32, c_i64, c_i32, c_i32,
+                                    c_p, c_i64, c_p]),
     "semkv_rank_topr": (c_i32, [c_p, c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p]),
     "semkv_quantize_pack": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_p,
                                     ctypes.POINTER(c_i64), c_i64, c_p, c_i64, c_p]),
@@ -120,6 +122,18 @@ def semkv_workspace_bytes(geom: semkv_geom, nlayers: int, max_tokens: int) -> in
 
 
 # ------------------------------------------------------------------ device calls
+
+def semkv_score_keynorm(K, scores, layer0, nlayers, stream=None):
+    """K fp16 [B][layers][kv][n][128] (any strides with d contiguous); scores fp32 [B][ld] out."""
+    if layer0 < 0 or nlayers < 1 or layer0 + nlayers > K.shape[1]:
+        raise ValueError("layer window outside K")
+    if scores.shape[0] != K.shape[0] or scores.shape[1] < K.shape[3] or scores.stride(1) != 1:
+        raise ValueError("scores must be [B][>= n] with unit stride")
+    _check("semkv_score_keynorm",
+           _lib.semkv_score_keynorm(_ptr(K), _strides(K), K.shape[0], K.shape[2], K.shape[3],
+                                    layer0, nlayers, _ptr(scores), scores.stride(0),
+                                    _stream(stream)))
+
 
 def semkv_rank_topr(scores, k, perm, mask=None, n=None, stream=None):
     """scores fp32 [B][ld]; perm int32 [B][n] out; mask uint32-as-int32 [B][ceil(n/32)] out."""

@@ -107,6 +107,27 @@ def fake_cache(**kw):
                           n_tokens=0)
 
 
+def test_score_keynorm_validation_before_launch():
+    f = sk._lib.semkv_score_keynorm
+    p = ctypes.c_void_p(0x200000)
+    st = (ctypes.c_int64 * 4)(32 * 8 * 1000 * 128, 8 * 1000 * 128, 1000 * 128, 128)
+    bad = (ctypes.c_int64 * 4)(32 * 8 * 1000 * 128, 8 * 1000 * 128, 1000 * 128, 132)
+    E = sk.SEMKV_EINVAL
+    assert f(None, st, 1, 8, 1000, 28, 4, p, 1000, None) == E                 # null K
+    assert f(ctypes.c_void_p(0x200008), st, 1, 8, 1000, 28, 4, p, 1000, None) == E   # K not 16-byte aligned
+    assert f(p, bad, 1, 8, 1000, 28, 4, p, 1000, None) == E                  # stride not a multiple of 8
+    assert f(p, None, 1, 8, 1000, 28, 4, p, 1000, None) == E                 # no strides
+    assert f(p, st, 0, 8, 1000, 28, 4, p, 1000, None) == E                   # batch 0
+    assert f(p, st, 65536, 8, 1000, 28, 4, p, 1000, None) == E               # batch too large
+    assert f(p, st, 1, 0, 1000, 28, 4, p, 1000, None) == E                   # no heads
+    assert f(p, st, 1, 8, 0, 28, 4, p, 1000, None) == E                      # n < 1
+    assert f(p, st, 1, 8, 1000, -1, 4, p, 1000, None) == E                   # layer0 < 0
+    assert f(p, st, 1, 8, 1000, 28, 0, p, 1000, None) == E                   # empty window
+    assert f(p, st, 1, 8, 1000, 28, 4, None, 1000, None) == E                # null scores
+    assert f(p, st, 1, 8, 1000, 28, 4, ctypes.c_void_p(0x200002), 1000, None) == E   # misaligned scores
+    assert f(p, st, 1, 8, 1000, 28, 4, p, 999, None) == E                    # ld < n
+
+
 def test_quantize_pack_validation_before_launch():
     f = sk._lib.semkv_quantize_pack
     c = fake_cache()
