@@ -331,6 +331,54 @@ def test_generation_block_exact(block, steps, r):
     assert_pools_equal(gpu_pools(cache, sk), ref.pools, "after flush")
 
 
+def test_multi_turn():
+    """Two turns of prompt + generation (SemKV Fig. 6; the multi-turn setting
+    uses r = 0.35): each prompt is ranked and quantized as a whole, each
+    turn's generated tokens block by block, the residual block at the turn's
+    end (flush); a prompt is refused while the tail holds tokens."""
+    _print("multi-turn")
+    rng = np.random.default_rng(35)
+    B, layers, kv, Hq, block, r = 2, 2, 2, 8, 128, 0.35
+    turns = [(150, 170), (90, 60)]                 # (prompt tokens, generated tokens)
+    tot = sum(a + b for a, b in turns)
+    cache = sk.SemKVCache(B, layers, kv, Hq, 6, 5, cap16(tot), cap16(tot), block=block,
+                          max_tokens=tot + block)
+    ref = O.GenerationCache(layers=layers, kv_heads=kv, L_high=6, L_low=5, r=r, block=block,
+                            batch=B)
+    out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
+    for t_i, (n_p, n_g) in enumerate(turns):
+        K, V = _kv(rng, B, layers, kv, n_p)
+        s = rng.random((B, n_p)).astype(np.float32)
+        k = O.topr_count(n_p, r)
+        perm = torch.empty((B, n_p), dtype=torch.int32, device="cuda")
+        sk.semkv_rank_topr(to_dev(s), k, perm)
+        sk.semkv_quantize_pack(cache, to_dev(K), to_dev(V), perm, k)
+        ref.prompt(K, V, s)
+        ks = rng.standard_normal((B, layers, kv, n_g, 128)).astype(np.float16)
+        vs = rng.standard_normal((B, layers, kv, n_g, 128)).astype(np.float16)
+        ss = rng.random((B, n_g)).astype(np.float32)
+        sk.semkv_append_block(cache, to_dev(ks), to_dev(vs), to_dev(ss), r)
+        for i in range(n_g):
+            ref.append(ks[:, :, :, i], vs[:, :, :, i], ss[:, i])
+        assert cache.n_tail == ref.n_tail > 0
+        if t_i == 0:                               # a prompt needs an empty tail
+            with pytest.raises(sk.SemKVError):
+                sk.semkv_quantize_pack(cache, to_dev(K), to_dev(V), perm, k)
+        q = (rng.standard_normal((B, layers, Hq, 128)) / math.sqrt(128)).astype(np.float16)
+        sk.semkv_decode_attn(cache, to_dev(q), out)
+        sk.semkv_sync_check()
+        assert_attention_close(out.cpu().numpy(), ref.decode(q, 1.0), f"turn {t_i} before flush")
+        sk.semkv_append_block(cache, None, None, None, r, flush=True)
+        ref.flush()
+        sk.semkv_sync_check()
+        assert cache.n_tail == 0 and cache.n_tokens == ref.n_tokens
+        assert_pools_equal(gpu_pools(cache, sk), ref.pools, f"turn {t_i} after flush")
+    q = (rng.standard_normal((B, layers, Hq, 128)) / math.sqrt(128)).astype(np.float16)
+    sk.semkv_decode_attn(cache, to_dev(q), out)
+    sk.semkv_sync_check()
+    assert_attention_close(out.cpu().numpy(), ref.decode(q, 1.0), "after both turns")
+
+
 def test_append_many_tokens_one_call():
     """t_new larger than a block: the call fills, quantizes and refills."""
     _print("append many")
