@@ -66,6 +66,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="decode steps per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="time every k-th decode partials launch with an event pair (the "
+                         "roofline's average); the other launches carry no event packets")
     ap.add_argument("--rotate", action="store_true",
                     help="Hadamard-rotated cache (the optional quantizer rotation); a variant of "
                          "the workload, not its headline: no extra legs, no CPU baseline")
@@ -145,16 +148,18 @@ def main():
     step_bytes = rank_bytes + quant_bytes + D * decode_bytes
 
     # HIP events on the work stream: quantize-pack and the decode loop of
-    # every timed step, and each decode_partials launch.  An event is a queue
-    # packet between kernels that costs about 1.5 us of the step, so the
-    # merges get one marker each, after them, and the decode time per step is
-    # the loop's.  (With no marker between a merge and the next partials
-    # event, that event pair measured the partials launch about 5 us longer
-    # than rocprofv3's kernel time.)
+    # every timed step, and every `every`-th decode_partials launch (their
+    # mean is the roofline's launch time).  An event is a queue packet
+    # between kernels that costs about 1.5 us of the step, so the other
+    # launches carry none, the merge before each timed launch gets one
+    # marker, and the decode time per step is the loop's.  (With no marker
+    # between a merge and the next partials event, that event pair measured
+    # the partials launch about 5 us longer than rocprofv3's kernel time.)
     Ev = lambda: torch.cuda.Event(enable_timing=True)
     ev_q = [(Ev(), Ev()) for _ in range(args.steps)]
     ev_l = [Ev() for _ in range(args.steps)]                 # decode loop end
-    ev_p = [[(Ev(), Ev()) for _ in range(D)] for _ in range(args.steps)]
+    every = max(1, args.event_every)
+    ev_p = [[(Ev(), Ev()) for _ in range(0, D, every)] for _ in range(args.steps)]
     ev_m = Ev()                                              # marker after a merge
 
     def step(i=None):
@@ -166,14 +171,15 @@ def main():
         if i is not None:
             ev_q[i][1].record(stream)
         for j in range(D):
-            if i is not None:
-                ev_p[i][j][0].record(stream)
+            timed = i is not None and j % every == 0
+            if timed:
+                ev_p[i][j // every][0].record(stream)
             sk.semkv_decode_partials(cache, q[j], stream=stream)
-            if i is not None:
-                ev_p[i][j][1].record(stream)
+            if timed:
+                ev_p[i][j // every][1].record(stream)
             sk.semkv_decode_merge(cache, out, stream=stream)
-            if i is not None:
-                ev_m.record(stream)
+            if i is not None and (j + 1) % every == 0:
+                ev_m.record(stream)                          # before the next timed launch
         if i is not None:
             ev_l[i].record(stream)
 
@@ -238,6 +244,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(part_gbs / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(ms_part * 1e3, 2),
+                     "launches_timed": args.steps * len(range(0, D, every)),
                      "algorithmic_bytes_per_launch": partial_bytes,
                      "traffic": traffic},
         "cpu_baseline": None,
