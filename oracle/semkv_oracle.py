@@ -424,20 +424,23 @@ def decode_attention(q: np.ndarray, pools: Pools, sm_scale: float, layer0: int =
             the not-yet-quantized newest tokens, read exactly
     returns float64 [B][nl][Hq][128]
 
-    With rotated pools the attention runs in the rotated domain (logits are
-    unchanged since H is orthogonal): the query is rotated as the cache rows
-    are (float32 butterflies) and kept at the query's own precision, fp16;
-    the tail rows are rotated exactly (H k, H v); the output is rotated
-    back, H o.
+    One softmax over every cached token.  With rotated pools the rotation
+    belongs to the quantizer: the pool rows hold H k and H v, so their
+    logits take the query rotated as the rows are (float32 butterflies) and
+    kept at the query's own precision, fp16, and their share of the output
+    is rotated back, H (sum p H v).  The fp16 tail holds rows that have not
+    been quantized, hence not rotated: their logits take the query as given
+    and their values enter the output as they are.
     """
     H = hadamard128() if pools.rotate else None
-    if H is not None:
-        q = rotate_rows_f32(np.asarray(q, dtype=np.float16)).astype(np.float16)
-    q = np.asarray(q, dtype=np.float16).astype(np.float64)
-    B, nl, Hq, _ = q.shape
+    q16 = np.asarray(q, dtype=np.float16)
+    q_raw = q16.astype(np.float64)
+    q_pool = (rotate_rows_f32(q16).astype(np.float16).astype(np.float64) if H is not None
+              else q_raw)
+    B, nl, Hq, _ = q_raw.shape
     Hkv = pools.codes_high.shape[2]
     group = Hq // Hkv
-    out = np.zeros(q.shape, dtype=np.float64)
+    out = np.zeros(q_raw.shape, dtype=np.float64)
     for b in range(B):
         for li in range(nl):
             layer = layer0 + li
@@ -449,20 +452,22 @@ def decode_attention(q: np.ndarray, pools: Pools, sm_scale: float, layer0: int =
                 x = dequantize_pool(codes[b, layer], meta[b, layer], L)   # [kv][2][rows][128]
                 parts_k.append(x[:, 0])
                 parts_v.append(x[:, 1])
+            kp = np.concatenate(parts_k, axis=1) if parts_k else np.zeros((Hkv, 0, HEAD_DIM))
+            vp = np.concatenate(parts_v, axis=1) if parts_v else np.zeros((Hkv, 0, HEAD_DIM))
             if tail_kv is not None and n_tail > 0:
                 t = np.asarray(tail_kv[b, layer], dtype=np.float16).astype(np.float64)
-                if H is not None:
-                    t = t @ H                             # each row r -> H r (H symmetric)
-                parts_k.append(t[:, 0, :n_tail])
-                parts_v.append(t[:, 1, :n_tail])
-            keys = np.concatenate(parts_k, axis=1)        # [kv][T][128]
-            vals = np.concatenate(parts_v, axis=1)
+                kt, vt = t[:, 0, :n_tail], t[:, 1, :n_tail]
+            else:
+                kt = vt = np.zeros((Hkv, 0, HEAD_DIM))
+            P = kp.shape[1]
             for h in range(Hq):
                 g = h // group
-                if H is None:
-                    out[b, li, h] = attention(q[b, li, h], keys[g], vals[g], sm_scale)
-                else:
-                    out[b, li, h] = H @ attention(q[b, li, h], keys[g], vals[g], sm_scale)
+                z = sm_scale * np.concatenate([kp[g] @ q_pool[b, li, h], kt[g] @ q_raw[b, li, h]])
+                z = z - z.max()
+                p = np.exp(z)
+                p = p / p.sum()
+                o_pool = p[:P] @ vp[g]
+                out[b, li, h] = (H @ o_pool if H is not None else o_pool) + p[P:] @ vt[g]
     return out
 
 
@@ -489,6 +494,7 @@ class GenerationCache:
     tail_v: list = field(default_factory=list)
     tail_s: list = field(default_factory=list)   # list of [B] fp32
     n_tokens: int = 0
+    rotate: bool = False                         # Hadamard-rotated pools (the tail stays fp16)
 
     def _empty_pools(self) -> Pools:
         B, l, g = self.batch, self.layers, self.kv_heads
@@ -497,7 +503,7 @@ class GenerationCache:
                     np.zeros((B, l, g, 2, 0, 2), np.uint16), np.zeros((B, 0), np.int32))
         ch, mh, th = z(self.L_high)
         cl, ml, tl = z(self.L_low)
-        return Pools(self.L_high, self.L_low, ch, mh, th, cl, ml, tl)
+        return Pools(self.L_high, self.L_low, ch, mh, th, cl, ml, tl, rotate=self.rotate)
 
     def _append_pools(self, new: Pools):
         if self.pools is None:
@@ -510,7 +516,8 @@ class GenerationCache:
             np.concatenate([p.tok_high, new.tok_high], axis=1),
             np.concatenate([p.codes_low, new.codes_low], axis=4),
             np.concatenate([p.meta_low, new.meta_low], axis=4),
-            np.concatenate([p.tok_low, new.tok_low], axis=1))
+            np.concatenate([p.tok_low, new.tok_low], axis=1),
+            rotate=self.rotate)
 
     def prompt(self, K, V, scores):
         """Quantize a whole prompt with one global top-r over its scores."""
@@ -518,7 +525,7 @@ class GenerationCache:
         k = topr_count(n, self.r)
         perm, _ = rank_topr_batch(scores, k)
         self._append_pools(quantize_pack_cache(K, V, perm, k, self.L_high, self.L_low,
-                                               token_base=self.n_tokens))
+                                               token_base=self.n_tokens, rotate=self.rotate))
         self.n_tokens += n
 
     def _quantize_tail(self):
@@ -531,7 +538,7 @@ class GenerationCache:
         k = topr_count(nt, self.r)
         perm, _ = rank_topr_batch(s, k)
         self._append_pools(quantize_pack_cache(K, V, perm, k, self.L_high, self.L_low,
-                                               token_base=self.n_tokens - nt))
+                                               token_base=self.n_tokens - nt, rotate=self.rotate))
         self.tail_k, self.tail_v, self.tail_s = [], [], []
 
     def append(self, k_new, v_new, score_new):

@@ -133,3 +133,56 @@ def test_rotated_decode_near_lossless_at_65536_levels():
                 ref = O.attention(q_eff[b, layer, h], K[b, layer, g].astype(np.float64),
                                   V[b, layer, g].astype(np.float64), 1.0)
                 assert np.max(np.abs(got[b, layer, h] - ref)) <= 2e-4 * np.max(np.abs(ref))
+
+
+def test_rotated_generation_near_lossless_at_65536_levels():
+    """A rotated cache with generated tokens: pool rows (rotated, 65536
+    levels) and fp16 tail rows (not quantized, so not rotated).  Decode must
+    agree with one softmax over the raw rows in which the pool tokens see
+    the query that the fp16 rotated query stands for, H fp16(H q), and the
+    tail tokens see q itself."""
+    rng = np.random.default_rng(8)
+    B, layers, kv, Hq, n0, gen, block = 1, 1, 2, 8, 40, 21, 16
+    g = O.GenerationCache(layers=layers, kv_heads=kv, L_high=65536, L_low=65536, r=0.5,
+                          block=block, batch=B, rotate=True)
+    K0 = rng.standard_normal((B, layers, kv, n0, 128)).astype(np.float16)
+    V0 = rng.standard_normal((B, layers, kv, n0, 128)).astype(np.float16)
+    g.prompt(K0, V0, rng.random((B, n0)).astype(np.float32))
+    ks = rng.standard_normal((gen, B, layers, kv, 128)).astype(np.float16)
+    vs = rng.standard_normal((gen, B, layers, kv, 128)).astype(np.float16)
+    for i in range(gen):
+        g.append(ks[i], vs[i], rng.random(B).astype(np.float32))
+    assert g.pools.rotate and g.n_tail == gen - block
+    q = (rng.standard_normal((B, layers, Hq, 128)) / 11.3).astype(np.float16)
+    got = g.decode(q, 1.0)
+    q_eff = O.rotate_rows_f32(q).astype(np.float16).astype(np.float64) @ sylvester(128) / math.sqrt(128)
+    n_pool = n0 + block                                   # prompt + the one full block
+    Kall = np.concatenate([K0, np.moveaxis(ks, 0, 3)], axis=3).astype(np.float64)
+    Vall = np.concatenate([V0, np.moveaxis(vs, 0, 3)], axis=3).astype(np.float64)
+    for h in range(Hq):
+        gi = h // (Hq // kv)
+        z = np.concatenate([Kall[0, 0, gi, :n_pool] @ q_eff[0, 0, h],
+                            Kall[0, 0, gi, n_pool:] @ q[0, 0, h].astype(np.float64)])
+        p = np.exp(z - z.max())
+        ref = (p / p.sum()) @ Vall[0, 0, gi]
+        assert np.max(np.abs(got[0, 0, h] - ref)) <= 2e-4 * np.max(np.abs(ref))
+
+
+def test_unrotated_decode_unchanged_by_tail_split():
+    """Without rotation, pools and tail are one softmax over every row: the
+    oracle's decode equals attention over the concatenated rows."""
+    rng = np.random.default_rng(12)
+    g = O.GenerationCache(layers=1, kv_heads=1, L_high=65536, L_low=65536, r=0.5, block=8, batch=1)
+    K0 = rng.standard_normal((1, 1, 1, 10, 128)).astype(np.float16)
+    V0 = rng.standard_normal((1, 1, 1, 10, 128)).astype(np.float16)
+    g.prompt(K0, V0, rng.random((1, 10)).astype(np.float32))
+    k1 = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    v1 = rng.standard_normal((1, 1, 1, 128)).astype(np.float16)
+    g.append(k1, v1, np.array([0.5], np.float32))
+    q = (rng.standard_normal((1, 1, 4, 128)) / 11.3).astype(np.float16)
+    got = g.decode(q, 1.0)
+    Kall = np.concatenate([K0[0, 0, 0], k1[0, 0]], axis=0).astype(np.float64)
+    Vall = np.concatenate([V0[0, 0, 0], v1[0, 0]], axis=0).astype(np.float64)
+    for h in range(4):
+        ref = O.attention(q[0, 0, h].astype(np.float64), Kall, Vall, 1.0)
+        assert np.max(np.abs(got[0, 0, h] - ref)) <= 2e-4 * np.max(np.abs(ref))
