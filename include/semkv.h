@@ -66,11 +66,14 @@ typedef struct {
                             * quantization (SemKV Table 2's quantizer; H is the
                             * normalized Sylvester H_128, applied in fp32 by
                             * index-bit butterflies; the row minimum is rounded
-                            * down to fp16).  Decode rotates the queries and
-                            * rotates the outputs back.  With rotate = 1: levels
-                            * (6, 5), 4 query heads per KV head, no generation
-                            * (semkv_append_block returns EUNSUPPORTED); rotated
-                            * rows must stay within the fp16 range. */
+                            * down to fp16).  Decode rotates the queries (held
+                            * in fp16) for the pool rows and rotates their share
+                            * of the output back; the fp16 tail of generation
+                            * is not quantized, hence not rotated, and is read
+                            * with the query as given.  With rotate = 1: levels
+                            * (6, 5) and 4 query heads per KV head, else
+                            * EUNSUPPORTED; rotated rows must stay within the
+                            * fp16 range. */
 } semkv_geom;
 
 /* A mixed-precision cache.  All buffers are caller-owned device memory whose

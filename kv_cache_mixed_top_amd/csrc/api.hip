@@ -273,7 +273,6 @@ semkv_status semkv_append_block(semkv_cache* c, const uint16_t* k_new, const uin
                                 void* stream) {
   semkv_status st = check_cache(c);
   if (st != SEMKV_OK) return st;
-  if (c->g.rotate) return SEMKV_EUNSUPPORTED;   // generation over rotated pools: not built
   if (t_new < 0 || !(r >= 0.0 && r <= 1.0)) return SEMKV_EINVAL;
   if (t_new > 0) {
     if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) || !strides_ok(strides))

@@ -241,6 +241,35 @@ constexpr int kTailGroup = 4;
 constexpr int kTailRows = 128;     // rows per pass over the chunk
 constexpr int kTailMax = 1024;     // rows per chunk, >= block
 
+// The tail chunk's output o[h][d] (the sum of the 4 waves' parts) -> the
+// partial record; wave h stores head h, dimensions 2 lane and 2 lane + 1.
+// With a rotated cache the tail rows are not rotated (only quantized rows
+// are), while the merge rotates the merged output back; the record is then
+// stored as H o (fp32 butterflies over d: bit 0 in the lane, bits 1-6 across
+// lanes), which that rotation returns to o since H H = I.
+static_assert(kThreads == 64 * kTailGroup, "one wave per query head of the group");
+__device__ __forceinline__ void store_tail_output(const DecodeArgs& a, float* wsu,
+                                                  const float (&part)[kThreads / 64][kTailGroup][kHeadDim],
+                                                  int tid) {
+  const int h = tid >> 6, lane = tid & 63;
+  float y0 = part[0][h][2 * lane] + part[1][h][2 * lane] + part[2][h][2 * lane] + part[3][h][2 * lane];
+  float y1 = part[0][h][2 * lane + 1] + part[1][h][2 * lane + 1] + part[2][h][2 * lane + 1] +
+             part[3][h][2 * lane + 1];
+  if (a.rotate) {
+    float s0 = y0 + y1, s1 = y0 - y1;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float p0 = __shfl_xor(s0, m, 64), p1 = __shfl_xor(s1, m, 64);
+      const float sg = (lane & m) ? -1.0f : 1.0f;   // upper lane: partner - own
+      s0 = fmaf(s0, sg, p0);
+      s1 = fmaf(s1, sg, p1);
+    }
+    y0 = s0 * kHadamardScale;
+    y1 = s1 * kHadamardScale;
+  }
+  *reinterpret_cast<float2*>(wsu + h * kPartialStride + 2 + 2 * lane) = make_float2(y0, y1);
+}
+
 __global__ __launch_bounds__(kThreads) void decode_tail_kernel(DecodeArgs a) {
   __shared__ float qs[kTailGroup][kHeadDim];
   __shared__ float z[kTailGroup][kTailMax];
@@ -385,10 +414,7 @@ __global__ __launch_bounds__(kThreads) void decode_tail_kernel(DecodeArgs a) {
 
   const int64_t u = ((((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x);
   float* wsu = a.ws + u * kTailGroup * kPartialStride;
-  for (int i = tid; i < kTailGroup * kHeadDim; i += kThreads) {
-    const int h = i / kHeadDim, d = i - h * kHeadDim;
-    wsu[h * kPartialStride + 2 + d] = part[0][h][d] + part[1][h][d] + part[2][h][d] + part[3][h][d];
-  }
+  store_tail_output(a, wsu, part, tid);
   if (tid < kTailGroup) {
     wsu[tid * kPartialStride + 0] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
     wsu[tid * kPartialStride + 1] = red[0][kTailGroup + tid] + red[1][kTailGroup + tid] +
@@ -536,10 +562,7 @@ __global__ __launch_bounds__(kThreads) void decode_tail128_kernel(DecodeArgs a) 
 
   const int64_t u = ((((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x);
   float* wsu = a.ws + u * kTailGroup * kPartialStride;
-  for (int i = tid; i < kTailGroup * kHeadDim; i += kThreads) {
-    const int h = i / kHeadDim, d = i - h * kHeadDim;
-    wsu[h * kPartialStride + 2 + d] = part[0][h][d] + part[1][h][d] + part[2][h][d] + part[3][h][d];
-  }
+  store_tail_output(a, wsu, part, tid);
   if (tid < kTailGroup) {
     wsu[tid * kPartialStride + 0] = fmaxf(fmaxf(red[0][tid], red[1][tid]), fmaxf(red[2][tid], red[3][tid]));
     wsu[tid * kPartialStride + 1] = red[0][kTailGroup + tid] + red[1][kTailGroup + tid] +

@@ -170,9 +170,21 @@ def semkv_append_block(cache: "SemKVCache", K_new, V_new, score_new, r, flush=Fa
                                    _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def _dense(t, name, dtype, cache):
+    """The kernels read q and write out as dense [B][nl][Hq][128] arrays."""
+    g = cache.geom
+    if (t.dtype != dtype or t.dim() != 4 or t.shape[0] != g.batch or t.shape[2] != g.q_heads
+            or t.shape[3] != 128 or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous {dtype} [batch][nl][q_heads][128] tensor")
+
+
 def semkv_decode_attn(cache: "SemKVCache", q, out, layer0=0, sm_scale=1.0, workspace=None,
                       stream=None):
     """q fp16 [B][nl][Hq][128]; out fp32 [B][nl][Hq][128]."""
+    _dense(q, "q", torch.float16, cache)
+    _dense(out, "out", torch.float32, cache)
+    if out.shape[1] != q.shape[1]:
+        raise ValueError("q and out must cover the same layers")
     ws = cache.workspace if workspace is None else workspace
     _check("semkv_decode_attn",
            _lib.semkv_decode_attn(ctypes.byref(cache.c), _ptr(q), layer0, q.shape[1], sm_scale,
@@ -181,6 +193,7 @@ def semkv_decode_attn(cache: "SemKVCache", q, out, layer0=0, sm_scale=1.0, works
 
 def semkv_decode_partials(cache: "SemKVCache", q, layer0=0, sm_scale=1.0, workspace=None,
                           stream=None):
+    _dense(q, "q", torch.float16, cache)
     ws = cache.workspace if workspace is None else workspace
     _check("semkv_decode_partials",
            _lib.semkv_decode_partials(ctypes.byref(cache.c), _ptr(q), layer0, q.shape[1],
@@ -188,6 +201,7 @@ def semkv_decode_partials(cache: "SemKVCache", q, layer0=0, sm_scale=1.0, worksp
 
 
 def semkv_decode_merge(cache: "SemKVCache", out, workspace=None, stream=None):
+    _dense(out, "out", torch.float32, cache)
     ws = cache.workspace if workspace is None else workspace
     _check("semkv_decode_merge",
            _lib.semkv_decode_merge(ctypes.byref(cache.c), out.shape[1], _ptr(out), _ptr(ws),

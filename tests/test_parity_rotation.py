@@ -96,14 +96,11 @@ def test_rotated_decode(n, r, kind, sm):
     assert_attention_close(out_l.cpu().numpy(), ref, f"rotated per-layer decode n={n}")
 
 
-def test_rotated_cache_refuses_generation_and_other_levels():
-    cache = sk.SemKVCache(1, 1, 2, 8, 6, 5, 64, 64, block=16, rotate=True)
-    k = torch.zeros((1, 1, 2, 1, 128), dtype=torch.float16, device="cuda")
-    sc = torch.zeros((1, 1), dtype=torch.float32, device="cuda")
-    with pytest.raises(sk.SemKVError):
-        sk.semkv_append_block(cache, k, k, sc, 0.5)
+def test_rotated_cache_refuses_other_levels():
     with pytest.raises(sk.SemKVError):
         sk.SemKVCache(1, 1, 2, 8, 8, 6, 64, 64, rotate=True)
+    with pytest.raises(sk.SemKVError):
+        sk.SemKVCache(1, 1, 2, 4, 6, 5, 64, 64, rotate=True)       # 2 query heads per KV head
     # the generic decode kernel reads unrotated queries only
     rng = np.random.default_rng(0)
     K, V = _rows(rng, 1, 1, 2, 40, "normal")
@@ -119,3 +116,55 @@ def test_rotated_cache_refuses_generation_and_other_levels():
     sk.semkv_decode_attn(cache, q, out)
     sk.semkv_sync_check()
     assert_attention_close(out.cpu().numpy(), O.decode_attention(q.cpu().numpy(), op, 1.0), "refuse")
+
+
+@pytest.mark.parametrize("block,n0,steps,r", [(128, 150, 300, 0.25), (16, 70, 53, 0.35),
+                                              (512, 200, 130, 0.5)])
+def test_rotated_generation(block, n0, steps, r):
+    """Generation on a rotated cache (SemKV Fig. 6 with Table 2's rotated
+    quantizer): full blocks are rotated and quantized, the fp16 tail is read
+    unrotated; pools bit-exact and decode (one launch and per layer) within
+    the decode tolerance at steps inside and at the ends of blocks."""
+    _print("rotated generation", block, n0, steps, r)
+    rng = np.random.default_rng(block + steps)
+    B, layers, kv, Hq = 2, 2, 2, 8
+    K0, V0 = _rows(rng, B, layers, kv, n0, "outlier")
+    s0 = rng.random((B, n0)).astype(np.float32)
+    k0 = O.topr_count(n0, r)
+    tot = n0 + steps
+    cache = sk.SemKVCache(B, layers, kv, Hq, 6, 5, cap16(tot), cap16(tot), block=block,
+                          max_tokens=tot + block, rotate=True)
+    perm = torch.empty((B, n0), dtype=torch.int32, device="cuda")
+    sk.semkv_rank_topr(to_dev(s0), k0, perm)
+    sk.semkv_quantize_pack(cache, to_dev(K0), to_dev(V0), perm, k0)
+    ref = O.GenerationCache(layers=layers, kv_heads=kv, L_high=6, L_low=5, r=r, block=block,
+                            batch=B, rotate=True)
+    ref.prompt(K0, V0, s0)
+    ks = rng.standard_normal((steps, B, layers, kv, 128)).astype(np.float16)
+    vs = rng.standard_normal((steps, B, layers, kv, 128)).astype(np.float16)
+    ss = rng.random((steps, B)).astype(np.float32)
+    out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
+    check_at = {0, block - 1, block, steps - 1}
+    for i in range(steps):
+        sk.semkv_append_block(cache, to_dev(ks[i][:, :, :, None, :]), to_dev(vs[i][:, :, :, None, :]),
+                              to_dev(ss[i][:, None]), r)
+        ref.append(ks[i], vs[i], ss[i])
+        assert cache.n_tail == ref.n_tail
+        if i in check_at:
+            q = (rng.standard_normal((B, layers, Hq, 128)) / math.sqrt(128)).astype(np.float16)
+            want = ref.decode(q, 1.0)
+            sk.semkv_decode_attn(cache, to_dev(q), out)
+            sk.semkv_sync_check()
+            assert_attention_close(out.cpu().numpy(), want, f"rotated gen step {i}")
+            for layer in range(layers):
+                o1 = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device="cuda")
+                sk.semkv_decode_partials(cache, to_dev(q[:, layer:layer + 1]), layer0=layer)
+                sk.semkv_decode_merge(cache, o1)
+                sk.semkv_sync_check()
+                assert_attention_close(o1.cpu().numpy(), want[:, layer:layer + 1],
+                                       f"rotated gen step {i} layer {layer}")
+    sk.semkv_append_block(cache, None, None, None, r, flush=True)
+    ref.flush()
+    sk.semkv_sync_check()
+    assert cache.n_tail == 0
+    assert_pools_equal(gpu_pools(cache, sk), ref.pools, "rotated generation after flush")
