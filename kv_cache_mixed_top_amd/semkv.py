@@ -139,6 +139,13 @@ def semkv_rank_topr(scores, k, perm, mask=None, n=None, stream=None):
     """scores fp32 [B][ld]; perm int32 [B][n] out; mask uint32-as-int32 [B][ceil(n/32)] out."""
     batch = scores.shape[0]
     n = scores.shape[1] if n is None else n
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1 or n > scores.shape[1]:
+        raise ValueError("scores must be fp32 [B][>= n] with unit stride")
+    if (perm.dtype != torch.int32 or tuple(perm.shape) != (batch, n) or not perm.is_contiguous()):
+        raise ValueError("perm must be a contiguous int32 [B][n] tensor")
+    if mask is not None and (mask.dtype != torch.int32 or tuple(mask.shape) != (batch, (n + 31) // 32)
+                             or not mask.is_contiguous()):
+        raise ValueError("mask must be a contiguous int32 [B][ceil(n/32)] tensor")
     _check("semkv_rank_topr", _lib.semkv_rank_topr(_ptr(scores), batch, n, scores.stride(0), k,
                                                    _ptr(perm), _ptr(mask), _stream(stream)))
 

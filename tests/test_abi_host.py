@@ -177,3 +177,25 @@ def test_decode_and_append_validation_before_launch():
 def test_status_strings():
     for s in range(-5, 1):
         assert sk.semkv_status_str(s)
+
+
+def test_binding_rejects_layouts_the_kernels_cannot_read():
+    """The binding checks shapes, dtypes and density before any call: the
+    kernels read dense arrays (CPU tensors suffice, nothing is launched)."""
+    import types
+    import torch
+    cache = types.SimpleNamespace(geom=types.SimpleNamespace(batch=2, q_heads=8))
+    out = torch.zeros((2, 2, 8, 128), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        sk.semkv_decode_merge(cache, out[:, 1:2])                        # strided view over batch
+    with pytest.raises(ValueError):
+        sk.semkv_decode_partials(cache, torch.zeros((2, 1, 8, 128), dtype=torch.float32))  # not fp16
+    with pytest.raises(ValueError):
+        sk.semkv_decode_attn(cache, torch.zeros((2, 1, 4, 128), dtype=torch.float16), out[:, :1])
+    s = torch.zeros((2, 100), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        sk.semkv_rank_topr(s[:, ::2], 10, torch.zeros((2, 50), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sk.semkv_rank_topr(s, 10, torch.zeros((2, 99), dtype=torch.int32))
+    with pytest.raises(ValueError):
+        sk.semkv_rank_topr(s, 10, torch.zeros((2, 100), dtype=torch.int64))
