@@ -66,6 +66,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="decode steps per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--keynorm-score", action="store_true",
+                    help="score the tokens in the step by key norm over the last 4 layers "
+                         "(semkv_score_keynorm) instead of the workload's precomputed score; "
+                         "a variant of the workload, not its headline")
     ap.add_argument("--event-every", type=int, default=8,
                     help="time every k-th decode partials launch with an event pair (the "
                          "roofline's average); the other launches carry no event packets")
@@ -145,7 +149,9 @@ def main():
     q_bytes = B * layers * Hq * 128 * 2
     decode_bytes = kv_packed + q_bytes + B * layers * Hq * 128 * 4
     partial_bytes = kv_packed + q_bytes                       # per decode_partials launch
-    step_bytes = rank_bytes + quant_bytes + D * decode_bytes
+    kn_layer0 = max(0, layers - 4)
+    score_bytes = (B * (layers - kn_layer0) * kv * n * 256 + B * n * 4) if args.keynorm_score else 0
+    step_bytes = score_bytes + rank_bytes + quant_bytes + D * decode_bytes
 
     # HIP events on the work stream: quantize-pack and the decode loop of
     # every timed step, and every `every`-th decode_partials launch (their
@@ -164,6 +170,8 @@ def main():
 
     def step(i=None):
         cache.reset()
+        if args.keynorm_score:
+            sk.semkv_score_keynorm(K, scores, kn_layer0, layers - kn_layer0, stream=stream)
         sk.semkv_rank_topr(scores, k, perm, mask, stream=stream)
         if i is not None:
             ev_q[i][0].record(stream)
@@ -230,7 +238,9 @@ def main():
         "config": {"workload": args.workload, "batch": B, "layers": layers, "kv_heads": kv,
                    "q_heads": Hq, "head_dim": 128, "tokens": n, "r": w.r,
                    "levels": [w.L_high, w.L_low], "decode_steps": D,
-                   "v_dist": w.v_dist, "score": w.score, "rotate": bool(args.rotate)},
+                   "v_dist": w.v_dist,
+                   "score": "keynorm_last4" if args.keynorm_score else w.score,
+                   "rotate": bool(args.rotate)},
         "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "quantize_pack": {"ms": round(ms_quant, 4), "GB/s": round(quant_gbs, 1),
                           "pct_hbm_peak": round(100.0 * quant_gbs / HBM_PEAK_GBS, 2),
@@ -250,7 +260,7 @@ def main():
         "cpu_baseline": None,
     }
 
-    if not args.no_extra and not args.rotate:
+    if not args.no_extra and not args.rotate and not args.keynorm_score:
         result["decode_graph_per_layer"] = graph_leg(sk, torch, cache, q, D, layers, B, Hq,
                                                      decode_bytes, stream)
         log(f"per-layer graph: {result['decode_graph_per_layer']['us_per_step']} us/step")
@@ -267,7 +277,7 @@ def main():
             f"{g['decode_tokens/s']} tok/s; block quantize {g['block_quantize_us']} us")
         K = V = None
 
-    if not args.no_cpu_baseline and not args.rotate:
+    if not args.no_cpu_baseline and not args.rotate and not args.keynorm_score:
         import cpu_baseline
         import oracle as O
         ls = max(1, min(args.cpu_layers, layers))
