@@ -71,7 +71,8 @@ typedef struct {
                             * of the output back; the fp16 tail of generation
                             * is not quantized, hence not rotated, and is read
                             * with the query as given.  With rotate = 1: levels
-                            * (6, 5) and 4 query heads per KV head, else
+                            * (6, 5), (6, 6) or (5, 5) and 4 query heads per KV
+                            * head, else
                             * EUNSUPPORTED; rotated rows must stay within the
                             * fp16 range. */
 } semkv_geom;

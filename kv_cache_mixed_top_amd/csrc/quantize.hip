@@ -592,6 +592,9 @@ hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream) {
   else if (a.fmt[0].L == 6 && a.fmt[1].L == 5)
     hipLaunchKernelGGL((quantize_pack_kernel<6, 5>), grid, dim3(kThreads), 0, stream, a,
                        tiles_high);
+  else if (a.rotate)
+    hipLaunchKernelGGL((quantize_pack_kernel<0, 0, true>), grid, dim3(kThreads), 0, stream, a,
+                       tiles_high);
   else
     hipLaunchKernelGGL((quantize_pack_kernel<0, 0>), grid, dim3(kThreads), 0, stream, a,
                        tiles_high);

@@ -53,6 +53,8 @@ def geom(**kw):
 def test_rotated_geometry_accepted():
     out = (ctypes.c_int64 * 8)()
     assert sk._lib.semkv_cache_sizes(ctypes.byref(geom(rotate=1)), out) == sk.SEMKV_OK
+    for lh, ll in ((6, 6), (5, 5)):
+        assert sk._lib.semkv_cache_sizes(ctypes.byref(geom(rotate=1, L_high=lh, L_low=ll)), out) == sk.SEMKV_OK
 
 
 def test_cache_sizes():
@@ -74,6 +76,7 @@ def test_cache_sizes():
     (dict(batch=0), sk.SEMKV_EINVAL),
     (dict(rotate=2), sk.SEMKV_EINVAL),
     (dict(rotate=1, L_high=8, L_low=6), sk.SEMKV_EUNSUPPORTED),
+    (dict(rotate=1, L_high=6, L_low=4), sk.SEMKV_EUNSUPPORTED),
     (dict(rotate=1, q_heads=16), sk.SEMKV_EUNSUPPORTED),
 ])
 def test_geometry_validation(bad, status):

@@ -168,3 +168,30 @@ def test_rotated_generation(block, n0, steps, r):
     sk.semkv_sync_check()
     assert cache.n_tail == 0
     assert_pools_equal(gpu_pools(cache, sk), ref.pools, "rotated generation after flush")
+
+
+@pytest.mark.parametrize("Lh,Ll", [(6, 6), (5, 5)])
+def test_rotated_uniform_levels(Lh, Ll):
+    """Rotation on caches of one level count (the generic quantize tile with
+    the rotation, the matrix-core decode): bit-exact pools, decode within
+    the tolerance."""
+    _print("rotated uniform", Lh, Ll)
+    rng = np.random.default_rng(Lh * 10 + Ll)
+    B, layers, kv, Hq, n = 1, 2, 2, 8, 900
+    K, V = _rows(rng, B, layers, kv, n, "outlier")
+    s = rng.random((B, n)).astype(np.float32)
+    k = O.topr_count(n, 0.5)
+    cache = sk.SemKVCache(B, layers, kv, Hq, Lh, Ll, cap16(k), cap16(n - k), rotate=True)
+    perm = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    sk.semkv_rank_topr(to_dev(s), k, perm)
+    sk.semkv_quantize_pack(cache, to_dev(K), to_dev(V), perm, k)
+    sk.semkv_sync_check()
+    wp, _ = O.rank_topr_batch(s, k)
+    op = O.quantize_pack_cache(K, V, wp, k, Lh, Ll, rotate=True)
+    assert_pools_equal(gpu_pools(cache, sk), op, f"rotated ({Lh},{Ll})")
+    q = (rng.standard_normal((B, layers, Hq, 128)) / math.sqrt(128)).astype(np.float16)
+    out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
+    sk.semkv_decode_attn(cache, to_dev(q), out)
+    sk.semkv_sync_check()
+    assert_attention_close(out.cpu().numpy(), O.decode_attention(q, op, 1.0), f"rotated ({Lh},{Ll}) decode")
+
