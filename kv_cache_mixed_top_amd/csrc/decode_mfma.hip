@@ -136,14 +136,28 @@ __device__ __forceinline__ void features(uint32_t x, uint32_t& g0, uint32_t& g1,
   g2 = __builtin_bit_cast(uint32_t, F2 - (h2){a2, a2});
 }
 
-template <int S>
-__device__ __forceinline__ f4 qk_mfma(const h4 (&qf)[3], uint32_t lo, uint32_t hi, f4 acc) {
-  return __builtin_amdgcn_mfma_f32_4x4x4f16(qf[S / 16], as_h4(lo, hi), acc, 4, S % 16, 0);
+// Query fragments of the QK^T product (ABID-packed 4x4x4 A operands).  With
+// kLo (a rotated cache) the query is the fp32 rotation H q, carried as its
+// nearest fp16 `hi` plus the fp16 remainder `lo` (about 22 bits), so that the
+// logits do not inherit an fp16 rounding of H q; each product then takes one
+// more MFMA into the same accumulator.
+template <bool kLo>
+struct QFrag {
+  h4 hi[3];
+  h4 lo[kLo ? 3 : 1];
+};
+
+template <int S, bool kLo>
+__device__ __forceinline__ f4 qk_mfma(const QFrag<kLo>& qf, uint32_t lo, uint32_t hi, f4 acc) {
+  acc = __builtin_amdgcn_mfma_f32_4x4x4f16(qf.hi[S / 16], as_h4(lo, hi), acc, 4, S % 16, 0);
+  if constexpr (kLo)
+    acc = __builtin_amdgcn_mfma_f32_4x4x4f16(qf.lo[S / 16], as_h4(lo, hi), acc, 4, S % 16, 0);
+  return acc;
 }
 
 // ---- 6 levels: one K row = 43 bytes = 11 dwords (the 44th byte masked)
-template <int W, int NC>
-__device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const h4 (&qf)[3],
+template <int W, int NC, bool kLo>
+__device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const QFrag<kLo>& qf,
                                           f4 (&acc)[3]) {
   const uint32_t X = d[W];
   const uint32_t xe = perm(kBias, X, 0x04020400u);   // bytes 4W, 4W+2 -> biased slots
@@ -151,14 +165,14 @@ __device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const h4 (&qf
   uint32_t e0, e1, e2, o0, o1, o2;
   digits<6>(xe, e0, e1, e2);
   digits<6>(xo, o0, o1, o2);
-  acc[0 % NC] = qk_mfma<3 * W + 0>(qf, e0, o0, acc[0 % NC]);
-  acc[1 % NC] = qk_mfma<3 * W + 1>(qf, e1, o1, acc[1 % NC]);
-  acc[2 % NC] = qk_mfma<3 * W + 2>(qf, e2, o2, acc[2 % NC]);
+  acc[0 % NC] = qk_mfma<3 * W + 0, kLo>(qf, e0, o0, acc[0 % NC]);
+  acc[1 % NC] = qk_mfma<3 * W + 1, kLo>(qf, e1, o1, acc[1 % NC]);
+  acc[2 % NC] = qk_mfma<3 * W + 2, kLo>(qf, e2, o2, acc[2 % NC]);
 }
-template <int NC, int... Ws>
-__device__ __forceinline__ void qk6(const uint32_t (&d)[12], const h4 (&qf)[3], f4 (&acc)[3],
+template <int NC, bool kLo, int... Ws>
+__device__ __forceinline__ void qk6(const uint32_t (&d)[12], const QFrag<kLo>& qf, f4 (&acc)[3],
                                     std::integer_sequence<int, Ws...>) {
-  (qk6_dword<Ws, NC>(d, qf, acc), ...);
+  (qk6_dword<Ws, NC, kLo>(d, qf, acc), ...);
 }
 
 // ---- 5 levels: one K row = 38 bytes; 7-byte units hold 8 fields of 7 bits.
@@ -180,19 +194,19 @@ __device__ __forceinline__ uint32_t bias_register() {
   asm volatile("v_mov_b32 %0, 0x66006600" : "=v"(b));
   return b;
 }
-template <int Q, int NC>   // Q = 2u + quad
-__device__ __forceinline__ void qk5_quad(uint32_t W, const h4 (&qf)[3], f4 (&acc)[3],
+template <int Q, int NC, bool kLo>   // Q = 2u + quad
+__device__ __forceinline__ void qk5_quad(uint32_t W, const QFrag<kLo>& qf, f4 (&acc)[3],
                                          uint32_t bias) {
   uint32_t pa, pb, a0, a1, a2, b0, b1, b2;
   field_pairs(W, pa, pb, bias);
   digits<5>(pa, a0, a1, a2);
   digits<5>(pb, b0, b1, b2);
-  acc[0 % NC] = qk_mfma<3 * Q + 0>(qf, a0, b0, acc[0 % NC]);
-  acc[1 % NC] = qk_mfma<3 * Q + 1>(qf, a1, b1, acc[1 % NC]);
-  acc[2 % NC] = qk_mfma<3 * Q + 2>(qf, a2, b2, acc[2 % NC]);
+  acc[0 % NC] = qk_mfma<3 * Q + 0, kLo>(qf, a0, b0, acc[0 % NC]);
+  acc[1 % NC] = qk_mfma<3 * Q + 1, kLo>(qf, a1, b1, acc[1 % NC]);
+  acc[2 % NC] = qk_mfma<3 * Q + 2, kLo>(qf, a2, b2, acc[2 % NC]);
 }
-template <int U, int NC>
-__device__ __forceinline__ void qk5_unit(const uint32_t (&d)[12], const h4 (&qf)[3],
+template <int U, int NC, bool kLo>
+__device__ __forceinline__ void qk5_unit(const uint32_t (&d)[12], const QFrag<kLo>& qf,
                                          f4 (&acc)[3], uint32_t bias) {
   constexpr int b0 = 7 * U;
   const uint32_t lo = __builtin_amdgcn_alignbyte(d[b0 / 4 + 1], d[b0 / 4], b0 % 4);
@@ -200,16 +214,16 @@ __device__ __forceinline__ void qk5_unit(const uint32_t (&d)[12], const h4 (&qf)
     constexpr int b1 = 7 * U + 4;
     const uint32_t hi = __builtin_amdgcn_alignbyte(d[b1 / 4 + 1], d[b1 / 4], b1 % 4);
     const uint32_t m = __builtin_amdgcn_alignbit(hi, lo, 28);
-    qk5_quad<2 * U, NC>(lo, qf, acc, bias);
-    qk5_quad<2 * U + 1, NC>(m, qf, acc, bias);
+    qk5_quad<2 * U, NC, kLo>(lo, qf, acc, bias);
+    qk5_quad<2 * U + 1, NC, kLo>(m, qf, acc, bias);
   } else {
-    qk5_quad<2 * U, NC>(lo, qf, acc, bias);   // fields 40..42 and one zero pad field
+    qk5_quad<2 * U, NC, kLo>(lo, qf, acc, bias);   // fields 40..42 and one zero pad field
   }
 }
-template <int NC, int... Us>
-__device__ __forceinline__ void qk5(const uint32_t (&d)[12], const h4 (&qf)[3], f4 (&acc)[3],
+template <int NC, bool kLo, int... Us>
+__device__ __forceinline__ void qk5(const uint32_t (&d)[12], const QFrag<kLo>& qf, f4 (&acc)[3],
                                     uint32_t bias, std::integer_sequence<int, Us...>) {
-  (qk5_unit<Us, NC>(d, qf, acc, bias), ...);
+  (qk5_unit<Us, NC, kLo>(d, qf, acc, bias), ...);
 }
 
 // d index of slot `i` (0..3) of QK instruction s, or -1 for a zero slot.
@@ -358,7 +372,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
   // ---- queries: ABID-packed 4x4x4 A fragments and per-head sums
   const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
                        (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
-  h4 qf[3];
+  QFrag<false> qf;
   {
     const int head = lane & 3, blk = lane >> 2;
 #pragma unroll
@@ -372,7 +386,7 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
           v[i] = d >= 0 ? qg[head * kHeadDim + d] : (_Float16)0.0f;
         }
       }
-      qf[P] = v;
+      qf.hi[P] = v;
     }
   }
   float sumq[4];
@@ -494,11 +508,11 @@ __device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64
       d[11] = 0;
       if (L == 6) {
         d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
-        qk6<3>(d, qf, sacc, std::make_integer_sequence<int, 11>{});
+        qk6<3, false>(d, qf, sacc, std::make_integer_sequence<int, 11>{});
       } else {
         d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
         d[10] = 0;
-        qk5<3>(d, qf, sacc, bias5, std::make_integer_sequence<int, 6>{});
+        qk5<3, false>(d, qf, sacc, bias5, std::make_integer_sequence<int, 6>{});
       }
     }
     const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
@@ -608,7 +622,8 @@ struct Stage2 {
   uint8_t *v0, *v1;            // wave 1 staging
   float *z0, *z1;              // logits of the last two tiles, [4][kTile] + maxima [4]
   _Float16* w;                 // wave 1: weights hi, lo, [2 * 4 * kTile]
-  _Float16* qr;                // wave 0: the rotated queries of a rotated cache, [4][128]
+  _Float16* qr;                // wave 0: the rotated queries of a rotated cache, hi and
+                               // lo, [2][4][128]
   __device__ uint8_t* k(int b) const { return b ? k1 : k0; }
   __device__ uint8_t* v(int b) const { return b ? v1 : v0; }
   __device__ float* z(int b) const { return b ? z1 : z0; }
@@ -639,7 +654,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* base, i
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-template <int L>
+template <int L, bool kRot>
 __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0, int64_t r1, int b, int li,
                         int g, Stage2& st) {
   constexpr int R = (L == 6) ? 43 : 38;
@@ -655,7 +670,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
 
   // queries: ABID-packed 4x4x4 A fragments and per-head sums (loaded once
   // the first K tile is in flight)
-  h4 qf[3];
+  QFrag<kRot> qf;
   float sumq[4];
   // The 3 KB of K bytes from row t0 on -> buffer `buf` (16 bytes per lane per
   // instruction), and the lane's K meta word -> register.  The plane from
@@ -694,11 +709,11 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
       d[11] = 0;
       if (L == 6) {
         d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
-        qk6<1>(d, qf, sacc, std::make_integer_sequence<int, 11>{});
+        qk6<1, kRot>(d, qf, sacc, std::make_integer_sequence<int, 11>{});
       } else {
         d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
         d[10] = 0;
-        qk5<1>(d, qf, sacc, bias5, std::make_integer_sequence<int, 6>{});
+        qk5<1, kRot>(d, qf, sacc, bias5, std::make_integer_sequence<int, 6>{});
       }
     }
     const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
@@ -728,8 +743,8 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   if (ir0 < ir1) issue(0, ir0);
   const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
                        (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
-  // A fragments and per-head sums from the 4 heads' queries at `qs`
-  auto load_queries = [&](const _Float16* qs) {
+  // A fragments of the 4 heads' query values at `qs`
+  auto fragments = [&](const _Float16* qs, h4 (&out)[3]) {
     const int head = lane & 3, blk = lane >> 2;
 #pragma unroll
     for (int P = 0; P < 3; ++P) {
@@ -742,16 +757,15 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
           v[i] = d >= 0 ? qs[head * kHeadDim + d] : (_Float16)0.0f;
         }
       }
-      qf[P] = v;
+      out[P] = v;
     }
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      sumq[h] = wave_sum((float)qs[h * kHeadDim + 2 * lane] + (float)qs[h * kHeadDim + 2 * lane + 1]);
   };
-  if (a.rotate) {
+  if constexpr (kRot) {
     // rotated cache: q -> H q in fp32 (lane holds dimensions 2 lane, 2 lane + 1:
-    // index bit 0 within the lane, bits 1-6 across lanes), rounded to fp16
-    constexpr float kRot = 0.08838834764831845f;   // 1/sqrt(128)
+    // index bit 0 within the lane, bits 1-6 across lanes), carried as the
+    // nearest fp16 plus the fp16 remainder; sum(H q) for the min term is
+    // taken from the fp32 values
+    constexpr float kNorm = 0.08838834764831845f;   // 1/sqrt(128)
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       const float x0 = (float)qg[h * kHeadDim + 2 * lane], x1 = (float)qg[h * kHeadDim + 2 * lane + 1];
@@ -763,13 +777,23 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
         y0 = upper ? p0 - y0 : y0 + p0;
         y1 = upper ? p1 - y1 : y1 + p1;
       }
-      st.qr[h * kHeadDim + 2 * lane] = (_Float16)(y0 * kRot);
-      st.qr[h * kHeadDim + 2 * lane + 1] = (_Float16)(y1 * kRot);
+      y0 *= kNorm;
+      y1 *= kNorm;
+      const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+      st.qr[h * kHeadDim + 2 * lane] = h0;
+      st.qr[h * kHeadDim + 2 * lane + 1] = h1;
+      st.qr[(4 + h) * kHeadDim + 2 * lane] = (_Float16)(y0 - (float)h0);
+      st.qr[(4 + h) * kHeadDim + 2 * lane + 1] = (_Float16)(y1 - (float)h1);
+      sumq[h] = wave_sum(y0 + y1);
     }
     wait_lgkm0();   // the wave's LDS writes have landed
-    load_queries(st.qr);
+    fragments(st.qr, qf.hi);
+    fragments(st.qr + 4 * kHeadDim, qf.lo);
   } else {
-    load_queries(qg);
+    fragments(qg, qf.hi);
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
   }
 
   for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 1
@@ -954,11 +978,12 @@ void decode_mfma_kernel(DecodeArgs a) {
     decode_chunk<5>(a, seg, r0, r1, b, li, g, u, st);
 }
 
+template <bool kRot>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_mfma2_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t k0[kBuf], k1[kBuf], v0[kBuf], v1[kBuf];
   __shared__ __attribute__((aligned(16))) float z0[4 * kTile + 4], z1[4 * kTile + 4];
   __shared__ __attribute__((aligned(16))) _Float16 w[2 * 4 * kTile];
-  __shared__ __attribute__((aligned(16))) _Float16 qr[4 * kHeadDim];
+  __shared__ __attribute__((aligned(16))) _Float16 qr[kRot ? 2 * 4 * kHeadDim : 8];
   Stage2 st;
   st.qr = qr;
   st.k0 = k0;
@@ -980,10 +1005,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const int64_t u = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (a.fmt[seg].L == 6) {
-    if (wave == 0) qk_wave<6>(a, seg, r0, r1, b, li, g, st);
+    if (wave == 0) qk_wave<6, kRot>(a, seg, r0, r1, b, li, g, st);
     else pv_wave<6>(a, seg, r0, r1, b, li, g, u, st);
   } else {
-    if (wave == 0) qk_wave<5>(a, seg, r0, r1, b, li, g, st);
+    if (wave == 0) qk_wave<5, kRot>(a, seg, r0, r1, b, li, g, st);
     else pv_wave<5>(a, seg, r0, r1, b, li, g, u, st);
   }
 }
@@ -1009,7 +1034,7 @@ int64_t decode_mfma_resident_waves() {
     int dev = 0, cus = 0, per_cu = 0;
     const hipError_t e =
         w == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel, 64, 0)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma2_kernel, 128, 0);
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma2_kernel<false>, 128, 0);
     if (e != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0 || per_cu <= 0)
@@ -1034,8 +1059,10 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   dim3 grid(pool_chunks, a.nl * a.kv_heads, a.batch);
   if (single_wave() && !a.rotate)   // the single-wave form reads unrotated queries only
     hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(64), 0, stream, a);
+  else if (a.rotate)
+    hipLaunchKernelGGL(decode_mfma2_kernel<true>, grid, dim3(128), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_mfma2_kernel, grid, dim3(128), 0, stream, a);
+    hipLaunchKernelGGL(decode_mfma2_kernel<false>, grid, dim3(128), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -36,8 +36,13 @@ the reading used here is the plainest one that the rest supports, marked
     of a rotated row is rounded down to fp16.  Decode rotates the query and
     rotates the output back (H is symmetric and orthogonal).
 
-Parity pins for every function live in tests/test_oracle_pins.py and
-tests/test_oracle_props.py; no function here is "parity unpinned".
+Parity pins for every function live in tests/test_oracle_pins.py,
+tests/test_oracle_props.py and the other tests/test_oracle_*.py files.  One
+reading is "parity unpinned" beyond a bound: the float32 butterfly order of
+rotate_rows_f32 (and hence the exact bits of the rotated codes that
+quantize_rows_rotated derives from it) is a convention of ours; the pages fix
+no order or precision, so it is pinned only to within its rounding bound of
+the exact float64 rotation, not bit for bit.
 """
 from __future__ import annotations
 
@@ -210,7 +215,8 @@ def rotate_rows_f32(x: np.ndarray) -> np.ndarray:
     y = x as float32; for bit = 0 .. 6, every index pair (i, i + 2^bit) with
     that bit clear in i becomes (y_i + y_j, y_i - y_j), each sum and
     difference rounded to float32; finally y * float32(1/sqrt(128)).  Up to
-    those roundings this is hadamard128() @ x.
+    those roundings this is hadamard128() @ x.  The order of the stages is a
+    convention (parity unpinned beyond the rounding bound; see the header).
     """
     y = np.asarray(x, dtype=np.float16).astype(np.float32).copy()
     if y.shape[-1] != HEAD_DIM:
@@ -425,18 +431,17 @@ def decode_attention(q: np.ndarray, pools: Pools, sm_scale: float, layer0: int =
     returns float64 [B][nl][Hq][128]
 
     One softmax over every cached token.  With rotated pools the rotation
-    belongs to the quantizer: the pool rows hold H k and H v, so their
-    logits take the query rotated as the rows are (float32 butterflies) and
-    kept at the query's own precision, fp16, and their share of the output
-    is rotated back, H (sum p H v).  The fp16 tail holds rows that have not
+    belongs to the quantizer: the pool rows hold the quantized H k and H v,
+    and as H is orthogonal and symmetric, q . k = (H q) . (H k) and
+    sum p v = H (sum p H v).  So their logits take the exactly rotated query
+    H q (float64, no rounding: the pages define none) and their share of the
+    output is rotated back exactly.  The fp16 tail holds rows that have not
     been quantized, hence not rotated: their logits take the query as given
     and their values enter the output as they are.
     """
     H = hadamard128() if pools.rotate else None
-    q16 = np.asarray(q, dtype=np.float16)
-    q_raw = q16.astype(np.float64)
-    q_pool = (rotate_rows_f32(q16).astype(np.float16).astype(np.float64) if H is not None
-              else q_raw)
+    q_raw = np.asarray(q, dtype=np.float16).astype(np.float64)
+    q_pool = q_raw @ H if H is not None else q_raw       # H symmetric: rows -> H q
     B, nl, Hq, _ = q_raw.shape
     Hkv = pools.codes_high.shape[2]
     group = Hq // Hkv
