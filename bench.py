@@ -425,9 +425,9 @@ def gen_leg(sk, W, torch, dev, stream, gen_steps=None):
     kb = sk.semkv_topr_count(w.block, w.r)
     Ev = lambda: torch.cuda.Event(enable_timing=True)
     with torch.cuda.stream(stream):
-        K, V, _ = W.make_kv_torch(w, dev)
+        K, V, chans = W.make_kv_torch(w, dev)
         scores = W.attention_mass_torch(K, w, dev)
-        Kg, Vg, Sg = W.make_gen_tokens_torch(w, T, dev)
+        Kg, Vg, Sg = W.make_gen_tokens_torch(w, T, dev, chans=chans)
         Qg = W.make_q_torch(w, T, dev)
         cache = sk.SemKVCache(B, w.layers, w.kv_heads, w.q_heads, w.L_high, w.L_low,
                               cap16(k + (T // w.block + 1) * kb),

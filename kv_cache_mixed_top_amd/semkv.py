@@ -98,6 +98,32 @@ def _strides(t):
     return (c_i64 * 4)(*[t.stride(i) for i in range(4)])
 
 
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _on_device(*ts):
+    """The C entry points take device pointers: host tensors are refused here,
+    after the layout checks (which need no device)."""
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors passed to the library must live on the GPU")
+
+
+def _kv_rows(cache, K, V, what):
+    """K and V: fp16 [batch][layers][kv_heads][tokens][128] views with unit-
+    stride d that share shape and strides, covering the cache's geometry."""
+    g = cache.geom
+    for t in (K, V):
+        if t.dtype != torch.float16:
+            raise ValueError(f"{what} must be fp16")
+        if t.dim() != 5 or tuple(t.shape[:3]) != (g.batch, g.layers, g.kv_heads):
+            raise ValueError(f"{what} must be [{g.batch}][{g.layers}][{g.kv_heads}][tokens][128]")
+    if V.shape != K.shape or tuple(V.stride()) != tuple(K.stride()):
+        raise ValueError(f"{what}: K and V must share shape and strides")
+    return _strides(K)
+
+
 # ------------------------------------------------------------------ host-only
 
 def semkv_row_bytes(L: int) -> int:
@@ -127,10 +153,15 @@ def semkv_score_keynorm(K, scores, layer0, nlayers, stream=None):
     """K fp16 [B][layers][kv][n][128] (any strides with d contiguous); scores fp32 [B][ld] out."""
     if layer0 < 0 or nlayers < 1 or layer0 + nlayers > K.shape[1]:
         raise ValueError("layer window outside K")
-    if scores.shape[0] != K.shape[0] or scores.shape[1] < K.shape[3] or scores.stride(1) != 1:
-        raise ValueError("scores must be [B][>= n] with unit stride")
+    if K.dtype != torch.float16:
+        raise ValueError("K must be fp16")
+    if (scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != K.shape[0]
+            or scores.shape[1] < K.shape[3] or scores.stride(1) != 1):
+        raise ValueError("scores must be fp32 [B][>= n] with unit stride")
+    strides = _strides(K)
+    _on_device(K, scores)
     _check("semkv_score_keynorm",
-           _lib.semkv_score_keynorm(_ptr(K), _strides(K), K.shape[0], K.shape[2], K.shape[3],
+           _lib.semkv_score_keynorm(_ptr(K), strides, K.shape[0], K.shape[2], K.shape[3],
                                     layer0, nlayers, _ptr(scores), scores.stride(0),
                                     _stream(stream)))
 
@@ -146,16 +177,21 @@ def semkv_rank_topr(scores, k, perm, mask=None, n=None, stream=None):
     if mask is not None and (mask.dtype != torch.int32 or tuple(mask.shape) != (batch, (n + 31) // 32)
                              or not mask.is_contiguous()):
         raise ValueError("mask must be a contiguous int32 [B][ceil(n/32)] tensor")
+    _on_device(scores, perm, mask)
     _check("semkv_rank_topr", _lib.semkv_rank_topr(_ptr(scores), batch, n, scores.stride(0), k,
                                                    _ptr(perm), _ptr(mask), _stream(stream)))
 
 
 def semkv_quantize_pack(cache: "SemKVCache", K, V, perm, k_high, stream=None):
+    """K, V fp16 [batch][layers][kv][n][128] (d contiguous); perm int32 [batch][n]."""
+    strides = _kv_rows(cache, K, V, "K/V")
     n = K.shape[3]
-    if V.shape != K.shape or tuple(V.stride()) != tuple(K.stride()):
-        raise ValueError("K and V must share shape and strides")
+    if (perm.dtype != torch.int32 or tuple(perm.shape) != (cache.geom.batch, n)
+            or not perm.is_contiguous()):
+        raise ValueError("perm must be a contiguous int32 [batch][n] tensor")
+    _on_device(K, V, perm)
     _check("semkv_quantize_pack",
-           _lib.semkv_quantize_pack(ctypes.byref(cache.c), _ptr(K), _ptr(V), _strides(K), n,
+           _lib.semkv_quantize_pack(ctypes.byref(cache.c), _ptr(K), _ptr(V), strides, n,
                                     _ptr(perm), k_high, _stream(stream)))
 
 
@@ -164,17 +200,21 @@ def semkv_append_block(cache: "SemKVCache", K_new, V_new, score_new, r, flush=Fa
     """K_new/V_new fp16 [B][layers][kv][t_new][128] (or None with flush); score_new [B][t_new]."""
     ws = cache.workspace if workspace is None else workspace
     if K_new is None:
+        _on_device(ws)
         _check("semkv_append_block",
                _lib.semkv_append_block(ctypes.byref(cache.c), None, None, None, None, 0, r,
-                                       int(bool(flush)), _ptr(ws), ws.numel(), _stream(stream)))
+                                       int(bool(flush)), _ptr(ws), _nbytes(ws), _stream(stream)))
         return
+    strides = _kv_rows(cache, K_new, V_new, "K_new/V_new")
     t_new = K_new.shape[3]
-    if V_new.shape != K_new.shape or tuple(V_new.stride()) != tuple(K_new.stride()):
-        raise ValueError("K_new and V_new must share shape and strides")
+    if (score_new.dtype != torch.float32 or tuple(score_new.shape) != (cache.geom.batch, t_new)
+            or not score_new.is_contiguous()):
+        raise ValueError("score_new must be a contiguous fp32 [batch][t_new] tensor")
+    _on_device(K_new, V_new, score_new, ws)
     _check("semkv_append_block",
            _lib.semkv_append_block(ctypes.byref(cache.c), _ptr(K_new), _ptr(V_new),
-                                   _strides(K_new), _ptr(score_new), t_new, r, int(bool(flush)),
-                                   _ptr(ws), ws.numel(), _stream(stream)))
+                                   strides, _ptr(score_new), t_new, r, int(bool(flush)),
+                                   _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def _dense(t, name, dtype, cache):
@@ -183,6 +223,7 @@ def _dense(t, name, dtype, cache):
     if (t.dtype != dtype or t.dim() != 4 or t.shape[0] != g.batch or t.shape[2] != g.q_heads
             or t.shape[3] != 128 or not t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous {dtype} [batch][nl][q_heads][128] tensor")
+    _on_device(t)
 
 
 def semkv_decode_attn(cache: "SemKVCache", q, out, layer0=0, sm_scale=1.0, workspace=None,
@@ -193,26 +234,29 @@ def semkv_decode_attn(cache: "SemKVCache", q, out, layer0=0, sm_scale=1.0, works
     if out.shape[1] != q.shape[1]:
         raise ValueError("q and out must cover the same layers")
     ws = cache.workspace if workspace is None else workspace
+    _on_device(ws)
     _check("semkv_decode_attn",
            _lib.semkv_decode_attn(ctypes.byref(cache.c), _ptr(q), layer0, q.shape[1], sm_scale,
-                                  _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+                                  _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def semkv_decode_partials(cache: "SemKVCache", q, layer0=0, sm_scale=1.0, workspace=None,
                           stream=None):
     _dense(q, "q", torch.float16, cache)
     ws = cache.workspace if workspace is None else workspace
+    _on_device(ws)
     _check("semkv_decode_partials",
            _lib.semkv_decode_partials(ctypes.byref(cache.c), _ptr(q), layer0, q.shape[1],
-                                      sm_scale, _ptr(ws), ws.numel(), _stream(stream)))
+                                      sm_scale, _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def semkv_decode_merge(cache: "SemKVCache", out, workspace=None, stream=None):
     _dense(out, "out", torch.float32, cache)
     ws = cache.workspace if workspace is None else workspace
+    _on_device(ws)
     _check("semkv_decode_merge",
            _lib.semkv_decode_merge(ctypes.byref(cache.c), out.shape[1], _ptr(out), _ptr(ws),
-                                   ws.numel(), _stream(stream)))
+                                   _nbytes(ws), _stream(stream)))
 
 
 def semkv_sync_check(stream=None):

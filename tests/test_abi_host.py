@@ -51,10 +51,13 @@ def geom(**kw):
 
 
 def test_rotated_geometry_accepted():
+    """Rotation is a quantizer option for every level pair and query group."""
     out = (ctypes.c_int64 * 8)()
     assert sk._lib.semkv_cache_sizes(ctypes.byref(geom(rotate=1)), out) == sk.SEMKV_OK
-    for lh, ll in ((6, 6), (5, 5)):
-        assert sk._lib.semkv_cache_sizes(ctypes.byref(geom(rotate=1, L_high=lh, L_low=ll)), out) == sk.SEMKV_OK
+    for lh, ll, hq in ((6, 6, 32), (5, 5, 32), (8, 6, 32), (6, 4, 32), (16, 3, 32), (6, 5, 16),
+                       (6, 5, 8), (6, 5, 64), (65536, 65536, 32)):
+        g = geom(rotate=1, L_high=lh, L_low=ll, q_heads=hq)
+        assert sk._lib.semkv_cache_sizes(ctypes.byref(g), out) == sk.SEMKV_OK
 
 
 def test_cache_sizes():
@@ -75,9 +78,7 @@ def test_cache_sizes():
     (dict(block=0), sk.SEMKV_EINVAL),
     (dict(batch=0), sk.SEMKV_EINVAL),
     (dict(rotate=2), sk.SEMKV_EINVAL),
-    (dict(rotate=1, L_high=8, L_low=6), sk.SEMKV_EUNSUPPORTED),
-    (dict(rotate=1, L_high=6, L_low=4), sk.SEMKV_EUNSUPPORTED),
-    (dict(rotate=1, q_heads=16), sk.SEMKV_EUNSUPPORTED),
+    (dict(rotate=1, q_heads=8 * 16), sk.SEMKV_EUNSUPPORTED),
 ])
 def test_geometry_validation(bad, status):
     out = (ctypes.c_int64 * 8)()
@@ -202,3 +203,42 @@ def test_binding_rejects_layouts_the_kernels_cannot_read():
         sk.semkv_rank_topr(s, 10, torch.zeros((2, 99), dtype=torch.int32))
     with pytest.raises(ValueError):
         sk.semkv_rank_topr(s, 10, torch.zeros((2, 100), dtype=torch.int64))
+
+
+def test_binding_rejects_bad_quantize_and_append_inputs():
+    """quantize_pack and append_block check dtype, geometry coverage and the
+    perm / score layout before any call (CPU tensors: nothing is launched),
+    and refuse host tensors even when their layout is right."""
+    import types
+    import torch
+    geom = types.SimpleNamespace(batch=2, layers=3, kv_heads=2, q_heads=8)
+    cache = types.SimpleNamespace(geom=geom, workspace=torch.zeros(256, dtype=torch.uint8))
+    n = 40
+    K = torch.zeros((2, 3, 2, n, 128), dtype=torch.float16)
+    perm = torch.zeros((2, n), dtype=torch.int32)
+    bad_inputs = [
+        (K.float(), K.float(), perm),                                    # fp32 rows
+        (K[:, :2], K[:, :2], perm),                                      # fewer layers than the cache
+        (torch.zeros((2, 3, 4, n, 128), dtype=torch.float16),) * 2 + (perm,),   # more heads
+        (K, K[..., :64], perm),                                          # V shape differs
+        (K, K, perm.long()),                                             # int64 perm
+        (K, K, perm[:, :n - 1]),                                         # perm too short
+        (K, K, torch.zeros((2, 2 * n), dtype=torch.int32)[:, ::2]),      # strided perm
+        (K, K, perm),                                                    # host tensors
+    ]
+    for k_, v_, p_ in bad_inputs:
+        with pytest.raises(ValueError):
+            sk.semkv_quantize_pack(cache, k_, v_, p_, 10)
+    Kn = torch.zeros((2, 3, 2, 1, 128), dtype=torch.float16)
+    s = torch.zeros((2, 1), dtype=torch.float32)
+    bad_app = [
+        (Kn, Kn, s.double()),                                            # fp64 scores
+        (Kn, Kn, torch.zeros((2, 2), dtype=torch.float32)),              # wrong t_new
+        (Kn, Kn, torch.zeros((1, 1), dtype=torch.float32)),              # wrong batch
+        (Kn.float(), Kn.float(), s),                                     # fp32 rows
+        (Kn[:, :1], Kn[:, :1], s),                                       # too few layers
+        (Kn, Kn, s),                                                     # host tensors
+    ]
+    for k_, v_, s_ in bad_app:
+        with pytest.raises(ValueError):
+            sk.semkv_append_block(cache, k_, v_, s_, 0.25)

@@ -28,15 +28,15 @@ def _print(*a):
     print(*a, flush=True)
 
 
-def _inputs(w, seed=0):
-    K, V, _ = W.make_kv_torch(w, DEV, seed=seed)
+def _inputs(w, seed=0, with_chans=False):
+    K, V, chans = W.make_kv_torch(w, DEV, seed=seed)
     if w.score == "attn_mass":
         scores = W.attention_mass_torch(K, w, DEV, seed=seed)
     else:
         g = torch.Generator(device=DEV)
         g.manual_seed(seed + 3)
         scores = torch.rand((w.batch, w.n), generator=g, device=DEV)
-    return K, V, scores
+    return (K, V, scores, chans) if with_chans else (K, V, scores)
 
 
 def _rank_full(scores, k):
@@ -150,7 +150,7 @@ def test_gen_16x8k_sampled():
     appended one per step and quantized in 128-token blocks."""
     w = W.WORKLOADS["gen_16x8k"]
     _print("gen_16x8k: inputs")
-    K, V, scores = _inputs(w)
+    K, V, scores, chans = _inputs(w, with_chans=True)
     B, n, k = w.batch, w.n, sk.semkv_topr_count(w.n, w.r)
     perm, wp = _rank_full(scores, k)
     T = w.gen_tokens
@@ -160,14 +160,9 @@ def test_gen_16x8k_sampled():
     cache = sk.SemKVCache(B, w.layers, w.kv_heads, w.q_heads, 6, 5, cap_h, cap_l, block=w.block,
                           max_tokens=n + T)
     sk.semkv_quantize_pack(cache, K, V, perm, k)
-    g = torch.Generator(device=DEV)
-    g.manual_seed(1)
-    shape = (T, B, w.layers, w.kv_heads, 128)
-    Kg = torch.randn(shape, generator=g, device=DEV).half()
-    Vg = torch.randn(shape, generator=g, device=DEV).half()
-    Sg = torch.rand((T, B), generator=g, device=DEV)
-    Qg = (torch.randn((2, B, w.layers, w.q_heads, 128), generator=g, device=DEV)
-          / math.sqrt(128)).half()
+    # generated tokens with the prompt's distributions (outlier channels too)
+    Kg, Vg, Sg = W.make_gen_tokens_torch(w, T, DEV, chans=chans)
+    Qg = W.make_q_torch(w, 2, DEV, seed=5)
     layers_s = (0, 31)
     ref = O.GenerationCache(layers=len(layers_s), kv_heads=w.kv_heads, L_high=6, L_low=5,
                             r=w.r, block=w.block, batch=1)

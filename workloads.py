@@ -127,12 +127,19 @@ def attention_mass_np(K16, rng, w: Workload, nq: int = 32):
     return score
 
 
-def make_gen_tokens_np(w: Workload, steps: int, seed: int = 1):
-    """Generated-token K/V [steps][B][layers][kv][128] fp16 and scores U(0,1)."""
+def make_gen_tokens_np(w: Workload, steps: int, seed: int = 1, chans=None):
+    """Generated-token K/V [steps][B][layers][kv][128] fp16 and scores U(0,1).
+
+    `chans` [layers][outliers] are the prompt's outlier channels: generated
+    keys take the same per-layer channels x10, so that they follow the
+    prompt's distribution."""
     rng = np.random.default_rng(seed)
     shape = (steps, w.batch, w.layers, w.kv_heads, HEAD_DIM)
     K = rng.standard_normal(shape, dtype=np.float32)
     V = rng.standard_normal(shape, dtype=np.float32)
+    if chans is not None:
+        for layer in range(w.layers):
+            K[:, :, layer, :, np.asarray(chans[layer])] *= 10.0
     s = rng.random((steps, w.batch), dtype=np.float32)
     q = (rng.standard_normal((steps, w.batch, w.layers, w.q_heads, HEAD_DIM), dtype=np.float32)
          / math.sqrt(HEAD_DIM)).astype(np.float16)
@@ -209,13 +216,20 @@ def make_q_torch(w: Workload, steps: int, device, seed: int = 0):
     return q.half()
 
 
-def make_gen_tokens_torch(w: Workload, steps: int, device, seed: int = 1):
-    """Generated-token K/V [steps][B][layers][kv][128] fp16 and U(0,1) scores."""
+def make_gen_tokens_torch(w: Workload, steps: int, device, seed: int = 1, chans=None):
+    """Generated-token K/V [steps][B][layers][kv][128] fp16 and U(0,1) scores;
+    `chans` as in make_gen_tokens_np (the prompt's per-layer outlier channels,
+    as make_kv_torch returns them)."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     shape = (steps, w.batch, w.layers, w.kv_heads, HEAD_DIM)
-    K = torch.randn(shape, generator=g, device=device).half()
+    K = torch.randn(shape, generator=g, device=device)
+    if chans is not None:
+        for layer in range(w.layers):
+            idx = torch.as_tensor(chans[layer], device=device)
+            K[:, :, layer].index_copy_(-1, idx, K[:, :, layer].index_select(-1, idx) * 10.0)
+    K = K.half()
     V = torch.randn(shape, generator=g, device=device).half()
     s = torch.rand((steps, w.batch), generator=g, device=device)
     return K, V, s
