@@ -66,14 +66,13 @@ typedef struct {
                             * quantization (SemKV Table 2's quantizer; H is the
                             * normalized Sylvester H_128, applied in fp32 by
                             * index-bit butterflies; the row minimum is rounded
-                            * down to fp16).  Decode rotates the queries (held
-                            * in fp16) for the pool rows and rotates their share
+                            * down to fp16).  Decode rotates the queries in fp32
+                            * (carried as an fp16 hi + lo pair on the matrix
+                            * cores) for the pool rows and rotates their share
                             * of the output back; the fp16 tail of generation
                             * is not quantized, hence not rotated, and is read
-                            * with the query as given.  With rotate = 1: levels
-                            * (6, 5), (6, 6) or (5, 5) and 4 query heads per KV
-                            * head, else
-                            * EUNSUPPORTED; rotated rows must stay within the
+                            * with the query as given.  Any level pair and
+                            * query group; rotated rows must stay within the
                             * fp16 range. */
 } semkv_geom;
 

@@ -25,11 +25,6 @@ semkv_status check_geom(const semkv_geom* g) {
     return SEMKV_EINVAL;
   if (g->cap_high > (int64_t)INT32_MAX || g->cap_low > (int64_t)INT32_MAX) return SEMKV_EINVAL;
   if (g->rotate != 0 && g->rotate != 1) return SEMKV_EINVAL;
-  // rotated caches decode on the matrix-core path: levels (6, 5), (6, 6) or
-  // (5, 5) with 4 query heads per KV head
-  const bool mfma_levels = (g->L_high == 6 && (g->L_low == 5 || g->L_low == 6)) ||
-                           (g->L_high == 5 && g->L_low == 5);
-  if (g->rotate && (!mfma_levels || g->q_heads != 4 * g->kv_heads)) return SEMKV_EUNSUPPORTED;
   return SEMKV_OK;
 }
 
@@ -166,8 +161,6 @@ semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0
   }
   a->ws = reinterpret_cast<float*>(ws);
   a->rotate = g.rotate;
-  // rotated caches decode on the matrix-core path only (levels 6/5, group 4)
-  if (a->rotate && !decode_use_mfma(*a)) return SEMKV_EUNSUPPORTED;
   const int64_t need = units * a->nchunks * per_chunk_bytes;
   if (!ws || !aligned(ws, 256) || ws_bytes < need) return SEMKV_EWORKSPACE;
   return SEMKV_OK;

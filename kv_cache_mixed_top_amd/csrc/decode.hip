@@ -13,8 +13,6 @@
 //
 // This is the generic kernel: any level count, any group size <= 8, VALU
 // arithmetic.
-#include <cstdlib>
-
 #include "semkv_internal.h"
 
 namespace semkv {
@@ -144,6 +142,28 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
     const int h = i / kHeadDim, d = i - h * kHeadDim;
     qs[h][d] = h2f(a.q[(((int64_t)b * a.nl + li) * a.q_heads + g * G + h) * kHeadDim + d]);
   }
+  // Rotated cache: the pool rows hold H k and H v, so their logits take the
+  // fp32 rotation H q (the fp16 tail rows are not rotated and take q as
+  // given).  Wave w rotates heads w, w + 4: dimensions 2 lane, 2 lane + 1 in
+  // the lane (index bit 0), bits 1-6 across lanes.
+  const bool rot_rows = a.rotate && sg.seg < 2;
+  if (rot_rows) {
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int h = wave; h < G; h += kThreads / 64) {
+      float y0 = qs[h][2 * lane] + qs[h][2 * lane + 1];
+      float y1 = qs[h][2 * lane] - qs[h][2 * lane + 1];
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
+        const bool upper = (lane & m) != 0;
+        y0 = upper ? p0 - y0 : y0 + p0;
+        y1 = upper ? p1 - y1 : y1 + p1;
+      }
+      qs[h][2 * lane] = y0 * kHadamardScale;
+      qs[h][2 * lane + 1] = y1 * kHadamardScale;
+    }
+  }
 
   // ---- pass 1: logits
   const int r = tid >> 2, qq = tid & 3;
@@ -220,6 +240,29 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
 
   const int64_t u = ((((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x);
   float* wsu = a.ws + u * G * kPartialStride;
+  if (a.rotate && sg.seg == 2) {
+    // Tail rows of a rotated cache are not rotated, while the merge rotates
+    // the merged output back: store this chunk's output as H o, so that the
+    // merge's rotation returns it to o (H H = I).  o goes through LDS (the
+    // logit rows are free now); H o is summed with the signs of H.
+    float* ob = &sc[0][0];                       // [G][128]
+#pragma unroll
+    for (int k = 0; k < kMaxGroup / 2; ++k) {
+      const int h = hh + 2 * k;
+      if (h < G) ob[h * kHeadDim + d] = acc[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxGroup / 2; ++k) {
+      const int h = hh + 2 * k;
+      if (h < G) {
+        float y = 0.f;
+        for (int j = 0; j < kHeadDim; ++j)
+          y += (__popc(d & j) & 1) ? -ob[h * kHeadDim + j] : ob[h * kHeadDim + j];
+        acc[k] = y * kHadamardScale;
+      }
+    }
+  }
 #pragma unroll
   for (int k = 0; k < kMaxGroup / 2; ++k) {
     const int h = hh + 2 * k;
@@ -770,14 +813,7 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int count, hipStream_t str
   return hipGetLastError();
 }
 
-// SEMKV_DECODE=generic forces the generic kernel (diagnostics and tests that
-// compare the two kernels on identical inputs); read at every launch.
-static bool force_generic() {
-  const char* e = getenv("SEMKV_DECODE");
-  return e && e[0] == 'g';
-}
-
-bool decode_use_mfma(const DecodeArgs& a) { return !force_generic() && decode_mfma_supported(a); }
+bool decode_use_mfma(const DecodeArgs& a) { return decode_mfma_supported(a); }
 
 hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream) {
   DecodeArgs g = a;

@@ -5,11 +5,9 @@
 // and KV head) for the 4 query heads of the KV head, writing (m, l, o[128])
 // partials per head.
 //
-// decode_mfma2_kernel (the one launched): two waves per chunk.  Wave 0
-// streams K and computes the logits, wave 1 streams V, keeps the softmax and
-// the PV accumulators; the logits of a tile pass through LDS with one
-// barrier per tile.  decode_mfma_kernel is the single-wave form, kept for
-// comparison (SEMKV_DECODE=mfma1).
+// decode_mfma2_kernel: two waves per chunk.  Wave 0 streams K and computes
+// the logits, wave 1 streams V, keeps the softmax and the PV accumulators;
+// the logits of a tile pass through LDS with one barrier per tile.
 //
 // Per 64-row tile:
 //  * Staging: direct global->LDS loads of the next tile through a buffer
@@ -43,6 +41,7 @@
 //    sums grow with the chunk and the recovery amplifies their rounding)
 //    adds coef_k * sum(w) to each digit sum, read from a B column that holds
 //    no field.  sum_t p_t * min_V(t) is accumulated on the VALU.
+#include <atomic>
 #include <utility>
 
 #include "semkv_internal.h"
@@ -288,15 +287,6 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // LDS address space, so the DMA target stays visibly inside its buffer.
 __device__ __forceinline__ lds_void* lds_at(uint8_t* p, int off) { return (lds_void*)((lds_u8*)p + off); }
 
-// LDS of one wave (a workgroup is one wave): two staging buffers of K rows
-// and V tiles filled by direct global->LDS loads, plus the softmax weights.
-// 13312 bytes, so that twelve workgroups fit in the 160 KB of one CU.
-struct Stage {
-  uint8_t k[2][kBuf];
-  uint8_t v[2][kBuf];
-  _Float16 w[2 * 4 * kTile];   // hi, lo
-};
-
 // Partial record of a chunk: per-head sums, digit sums from the feature
 // sums, (m, l, o[128]) per query head.
 template <int L>
@@ -351,260 +341,6 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t u, in
       wsu[h * kPartialStride + 0] = mref[h] * m_unit;   // natural-log units
       wsu[h * kPartialStride + 1] = lsum[h];
     }
-}
-
-template <int L>
-__device__ __forceinline__ void decode_chunk(const DecodeArgs& a, int seg, int64_t r0, int64_t r1,
-                                             int b, int li, int g, int64_t u, Stage& st) {
-  constexpr int R = (L == 6) ? 43 : 38;
-  const int lane = threadIdx.x;
-  _Float16* wbuf = st.w;
-  const int layer = a.layer0 + li;
-  const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
-  const int64_t cap = a.cap[seg];
-  const uint8_t* kcodes = a.codes[seg] + plane_k * cap * R;
-  const uint8_t* vcodes = kcodes + cap * R;
-  const uint32_t* kmg = a.meta[seg] + plane_k * cap;
-  const uint32_t* vmg = kmg + cap;
-  const float sm = a.sm_scale;
-  const uint32_t bias5 = L == 5 ? bias_register() : 0u;   // 5-level field bias
-
-  // ---- queries: ABID-packed 4x4x4 A fragments and per-head sums
-  const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
-                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
-  QFrag<false> qf;
-  {
-    const int head = lane & 3, blk = lane >> 2;
-#pragma unroll
-    for (int P = 0; P < 3; ++P) {
-      const int s = 16 * P + blk;
-      h4 v = {0, 0, 0, 0};
-      if (s < kQkInstr) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = qk_slot_dim<L>(s, i);
-          v[i] = d >= 0 ? qg[head * kHeadDim + d] : (_Float16)0.0f;
-        }
-      }
-      qf.hi[P] = v;
-    }
-  }
-  float sumq[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h)
-    sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
-
-  // ---- per-chunk exponent E: w = p * scale_V * 2^E stays below 2^14
-  const uint32_t smax = chunk_scale_max(vmg, r0, r1, lane);
-  int E = 0;
-  if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
-  const float two_e = ldexpf(1.0f, E);
-
-  float mref[4], lsum[4], msum[4];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    mref[h] = -INFINITY;
-    lsum[h] = 0.f;
-    msum[h] = 0.f;
-  }
-  f4 acc[3][3];
-#pragma unroll
-  for (int s = 0; s < 3; ++s)
-#pragma unroll
-    for (int k = 0; k < 3; ++k) acc[s][k] = (f4){0.f, 0.f, 0.f, 0.f};
-
-  // Direct global->LDS loads of rows [t0, t0 + nt) into buffer `buf`: each
-  // instruction moves 16 bytes per lane (1 KB); chunks past the valid range
-  // re-read the last valid chunk so that no load leaves the plane.  The
-  // lane's own K and V meta words go to registers.
-  uint32_t km_next = 0, vm_next = 0;
-  auto issue = [&](int buf, int64_t t0, int nt) {
-    const int nk = (nt * R + 15) >> 4;
-    const uint8_t* ks = kcodes + t0 * R;
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      if (64 * i < nk)
-        __builtin_amdgcn_global_load_lds(ks + 16 * min(64 * i + lane, nk - 1),
-                                         (lds_void*)(st.k[buf] + 1024 * i), 16, 0, 0);
-    const int nv = ((nt + 15) >> 4) * R;          // whole 16-row byte-planar tiles
-    const uint8_t* vs = vcodes + t0 * R;
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      if (64 * i < nv)
-        __builtin_amdgcn_global_load_lds(vs + 16 * min(64 * i + lane, nv - 1),
-                                         (lds_void*)(st.v[buf] + 1024 * i), 16, 0, 0);
-    const int mi = min(lane, nt - 1);
-    km_next = kmg[t0 + mi];
-    vm_next = vmg[t0 + mi];
-  };
-
-  // The tile loop keeps one tile's loads in flight while computing the
-  // previous one.  Only the loop head waits for outstanding loads; inside a
-  // tile, LDS hand-offs between lanes of the (single) wave only wait for the
-  // LDS queue (a workgroup barrier would also wait for the prefetch).
-  // The weights are taken against a per-head frame mref kept kFrameMargin
-  // above the running maximum logit.  A tile with a logit above the frame
-  // (in practice only the first tile) raises the frame, rescales what was
-  // accumulated and runs again from the loop head: the matrix-core
-  // accumulation is reached only when no rescale is pending.
-  int buf = 0;
-  uint32_t km = 0, vm = 0;   // meta words of the tile at t0
-  bool fresh = true;         // the tile at t0 has not been started yet
-  if (r0 < r1) issue(0, r0, (int)min((int64_t)kTile, r1 - r0));
-  for (int64_t t0 = r0; t0 < r1;) {
-    const int nt = (int)min((int64_t)kTile, r1 - t0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile's loads have landed
-    __syncthreads();                                     // every lane is past tile - 1
-    const uint8_t* kbuf = st.k[buf];
-    const uint8_t* vbuf = st.v[buf];
-    const int col = lane & 15;
-    const int quad = lane >> 4;
-
-    // This lane's V code bytes of the tile (8 tokens x one byte per group and
-    // set; two bytes for 5 levels) are read into registers before the next
-    // tile's loads are issued: LDS reads that follow an in-flight
-    // global->LDS load of the same array would wait for it.
-    uint2 vr[2][3][L == 6 ? 1 : 2];
-#pragma unroll
-    for (int G = 0; G < 2; ++G) {
-      const int tok0 = 32 * G + 8 * quad;
-      const int vo = (tok0 >> 4) * (16 * R) + (tok0 & 15);
-#pragma unroll
-      for (int set = 0; set < 3; ++set) {
-        const int j = 16 * set + col;
-        if (L == 6) {
-          vr[G][set][0] = (32 * G < nt && j < R) ? *reinterpret_cast<const uint2*>(vbuf + (vo + j * 16))
-                                                : make_uint2(0u, 0u);
-        } else {
-          const int j0 = (7 * j) >> 3;
-          const bool ok = 32 * G < nt && j < 43;
-          vr[G][set][0] = ok ? *reinterpret_cast<const uint2*>(vbuf + (vo + j0 * 16)) : make_uint2(0u, 0u);
-          vr[G][set][L == 6 ? 0 : 1] =
-              ok ? *reinterpret_cast<const uint2*>(vbuf + (vo + (j0 + 1) * 16)) : make_uint2(0u, 0u);
-        }
-      }
-    }
-    if (fresh) {
-      km = km_next;
-      vm = vm_next;
-    }
-
-    // ---- QK^T: lane = token
-    f4 sacc[3];
-#pragma unroll
-    for (int k = 0; k < 3; ++k) sacc[k] = (f4){0.f, 0.f, 0.f, 0.f};
-    {
-      const int off = lane * R;
-      const uint32_t* kb32 = reinterpret_cast<const uint32_t*>(kbuf + (off & ~3));
-      const int sh = off & 3;
-      uint32_t raw[12];
-#pragma unroll
-      for (int i = 0; i < 12; ++i) raw[i] = kb32[i];
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // staging reads done
-      if (t0 + kTile < r1) issue(buf ^ 1, t0 + kTile, (int)min((int64_t)kTile, r1 - t0 - kTile));
-      uint32_t d[12];
-#pragma unroll
-      for (int i = 0; i < 11; ++i) d[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
-      d[11] = 0;
-      if (L == 6) {
-        d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
-        qk6<3, false>(d, qf, sacc, std::make_integer_sequence<int, 11>{});
-      } else {
-        d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
-        d[10] = 0;
-        qk5<3, false>(d, qf, sacc, bias5, std::make_integer_sequence<int, 6>{});
-      }
-    }
-    const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
-    const float kbias = sm * h2f((uint16_t)(km >> 16));
-    float z[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float s = sacc[0][h] + sacc[1][h] + sacc[2][h];
-      z[h] = lane < nt ? fmaf(kfac, s, kbias * sumq[h]) : -INFINITY;
-    }
-
-    // ---- frame check (all weights <= 1)
-    const bool up = z[0] > mref[0] || z[1] > mref[1] || z[2] > mref[2] || z[3] > mref[3];
-    if (__ballot(up) != 0ull) {
-      float fac[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float nm = fmaxf(mref[h], wave_max(z[h]) + kFrameMargin);
-        fac[h] = __expf(mref[h] - nm);              // exp(-inf) = 0 on the first tile
-        mref[h] = nm;
-        lsum[h] *= fac[h];
-        msum[h] *= fac[h];
-      }
-#pragma unroll
-      for (int s = 0; s < 3; ++s)
-#pragma unroll
-        for (int k = 0; k < 3; ++k)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[s][k][r] *= fac[r];
-      fresh = false;
-      continue;                                     // run this tile again in the new frame
-    }
-    const float vs = h2f((uint16_t)(vm & 0xFFFFu)) * two_e;
-    const float vmin = h2f((uint16_t)(vm >> 16));
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float p = __expf(z[h] - mref[h]);
-      lsum[h] += p;
-      msum[h] = fmaf(p, vmin, msum[h]);
-      const float w = p * vs;
-      const _Float16 whi = (_Float16)w;
-      wbuf[h * kTile + lane] = whi;
-      wbuf[4 * kTile + h * kTile + lane] = (_Float16)(w - (float)whi);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // weights visible to the wave
-
-    // ---- PV: 32 tokens per MFMA
-#pragma unroll
-    for (int G = 0; G < 2; ++G) {
-      if (32 * G >= nt) break;
-      // A rows 0-3: w_hi of the 4 heads, rows 4-7: w_lo; rows 8-15 repeat
-      // them and only feed C rows 8-15, which are never read.
-      const h8 aw = *reinterpret_cast<const h8*>(wbuf + (col & 7) * kTile + 32 * G + 8 * quad);
-#pragma unroll
-      for (int set = 0; set < 3; ++set) {
-        const int j = 16 * set + col;                     // byte (L=6) or field (L=5)
-        uint32_t p0, p1, p2, p3;
-        if (L == 6) {
-          const uint2 w8 = vr[G][set][0];
-          p0 = perm(kBias, w8.x, 0x04010400u);
-          p1 = perm(kBias, w8.x, 0x04030402u);
-          p2 = perm(kBias, w8.y, 0x04010400u);
-          p3 = perm(kBias, w8.y, 0x04030402u);
-        } else {
-          const int bit = 7 * j;
-          const uint2 b0 = vr[G][set][0];
-          const uint2 b1 = vr[G][set][L == 6 ? 0 : 1];
-          const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
-          p0 = (u32(v2(perm(b1.x, b0.x, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
-          p1 = (u32(v2(perm(b1.x, b0.x, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
-          p2 = (u32(v2(perm(b1.y, b0.y, 0x05010400u)) >> shv) & 0x007F007Fu) | 0x66006600u;
-          p3 = (u32(v2(perm(b1.y, b0.y, 0x07030602u)) >> shv) & 0x007F007Fu) | 0x66006600u;
-        }
-        uint32_t g0[4], g1[4], g2[4];
-        features<L>(p0, g0[0], g1[0], g2[0]);
-        features<L>(p1, g0[1], g1[1], g2[1]);
-        features<L>(p2, g0[2], g1[2], g2[2]);
-        features<L>(p3, g0[3], g1[3], g2[3]);
-        const h8 B0 = as_h8(g0[0], g0[1], g0[2], g0[3]);
-        const h8 B1 = as_h8(g1[0], g1[1], g1[2], g1[3]);
-        const h8 B2 = as_h8(g2[0], g2[1], g2[2], g2[3]);
-        acc[set][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B0, acc[set][0], 0, 0, 0);
-        acc[set][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B1, acc[set][1], 0, 0, 0);
-        acc[set][2] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw, B2, acc[set][2], 0, 0, 0);
-      }
-    }
-    t0 += kTile;
-    buf ^= 1;
-    fresh = true;
-  }
-
-  write_partial<L>(a, u, lane, E, acc, mref, lsum, msum);
 }
 
 // ---- two-wave form: one workgroup of two waves per chunk.  Wave 0 streams
@@ -959,25 +695,6 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   write_partial<L>(a, u, lane, E, acc, mref, lsum, msum, kLn2);
 }
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8)))
-void decode_mfma_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) Stage st;
-
-  const int x = blockIdx.x;
-  const int seg = x < a.nch[0] ? 0 : 1;
-  const int ch = seg == 0 ? x : x - a.nch[0];
-  const int64_t r0 = (int64_t)ch * a.chunk;
-  const int64_t r1 = min(r0 + (int64_t)a.chunk, a.rows[seg]);
-  const int li = blockIdx.y / a.kv_heads;
-  const int g = blockIdx.y % a.kv_heads;
-  const int b = blockIdx.z;
-  const int64_t u = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x;
-  if (a.fmt[seg].L == 6)
-    decode_chunk<6>(a, seg, r0, r1, b, li, g, u, st);
-  else
-    decode_chunk<5>(a, seg, r0, r1, b, li, g, u, st);
-}
-
 template <bool kRot>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_mfma2_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t k0[kBuf], k1[kBuf], v0[kBuf], v1[kBuf];
@@ -1013,35 +730,29 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   }
 }
 
-// SEMKV_DECODE=mfma1 selects the single-wave kernel (for comparison).
-bool single_wave() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("SEMKV_DECODE");
-    v = (e && e[0] == 'm' && e[4] == '1') ? 1 : 0;
-  }
-  return v == 1;
-}
-
 }  // namespace
 
-// Workgroups of the matrix-core kernel resident on the device at once
-// (registers and LDS both limit it); the pool chunking fills them once.
+// Workgroups of the matrix-core kernel resident on the current device at
+// once (registers and LDS both limit it); the pool chunking fills them once.
+// Cached per device ordinal; concurrent first calls compute the same value.
 int64_t decode_mfma_resident_waves() {
-  static int64_t slots[2] = {0, 0};
-  const int w = single_wave() ? 0 : 1;
-  if (slots[w] <= 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    const hipError_t e =
-        w == 0 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel, 64, 0)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma2_kernel<false>, 128, 0);
-    if (e != hipSuccess || hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-      return 2048;
-    slots[w] = (int64_t)cus * per_cu;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int64_t> slots[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 2048;
+  if (dev < kMaxDevices) {
+    const int64_t v = slots[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
   }
-  return slots[w];
+  int cus = 0, per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma2_kernel<false>, 128, 0) !=
+          hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0 || per_cu <= 0)
+    return 2048;
+  const int64_t v = (int64_t)cus * per_cu;
+  if (dev < kMaxDevices) slots[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 bool decode_mfma_supported(const DecodeArgs& a) {
@@ -1057,9 +768,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   const int pool_chunks = a.nch[0] + a.nch[1];
   if (pool_chunks == 0) return hipSuccess;
   dim3 grid(pool_chunks, a.nl * a.kv_heads, a.batch);
-  if (single_wave() && !a.rotate)   // the single-wave form reads unrotated queries only
-    hipLaunchKernelGGL(decode_mfma_kernel, grid, dim3(64), 0, stream, a);
-  else if (a.rotate)
+  if (a.rotate)
     hipLaunchKernelGGL(decode_mfma2_kernel<true>, grid, dim3(128), 0, stream, a);
   else
     hipLaunchKernelGGL(decode_mfma2_kernel<false>, grid, dim3(128), 0, stream, a);

@@ -84,8 +84,7 @@ hipError_t launch_decode_generic(const DecodeArgs& a, int count, hipStream_t str
 // Matrix-core kernel for the pool chunks [0, nch[0] + nch[1]) when both pool
 // formats are 6- or 5-level and the query group is 4.
 bool decode_mfma_supported(const DecodeArgs& a);
-// The matrix-core kernel will run for these arguments (supported and not
-// disabled with SEMKV_DECODE=generic).
+// The matrix-core kernel will run for these arguments.
 bool decode_use_mfma(const DecodeArgs& a);
 // Pool chunk rows for the matrix-core kernel: enough chunks per (sequence,
 // layer, KV head) to fill the device's resident wave slots once.

@@ -3,7 +3,6 @@ with its rotation; the matrix and precision as read in the oracle):
 rotated quantize-pack bit-exact against the oracle, decode over rotated pools
 within the decode tolerance, and the unsupported combinations refused."""
 import math
-import os
 
 import numpy as np
 import pytest
@@ -96,48 +95,72 @@ def test_rotated_decode(n, r, kind, sm):
     assert_attention_close(out_l.cpu().numpy(), ref, f"rotated per-layer decode n={n}")
 
 
-def test_rotated_cache_refuses_other_levels():
-    with pytest.raises(sk.SemKVError):
-        sk.SemKVCache(1, 1, 2, 8, 8, 6, 64, 64, rotate=True)
-    with pytest.raises(sk.SemKVError):
-        sk.SemKVCache(1, 1, 2, 4, 6, 5, 64, 64, rotate=True)       # 2 query heads per KV head
-    # the generic decode kernel reads unrotated queries only
-    rng = np.random.default_rng(0)
-    K, V = _rows(rng, 1, 1, 2, 40, "normal")
-    cache, op = _rotated_case(K, V, rng.random((1, 40)).astype(np.float32), 0.5, "refuse")
-    q = to_dev((rng.standard_normal((1, 1, 8, 128)) / 11.3).astype(np.float16))
-    out = torch.empty((1, 1, 8, 128), dtype=torch.float32, device="cuda")
-    os.environ["SEMKV_DECODE"] = "generic"
-    try:
-        with pytest.raises(sk.SemKVError):
-            sk.semkv_decode_attn(cache, q, out)
-    finally:
-        del os.environ["SEMKV_DECODE"]
-    sk.semkv_decode_attn(cache, q, out)
+@pytest.mark.parametrize("Lh,Ll,Hq,n,r,kind", [
+    (5, 4, 8, 700, 0.5, "outlier"),         # 5/4 pair, group 4: generic decode
+    (8, 6, 8, 333, 0.25, "mixed"),          # 8/6 pair
+    (6, 5, 2, 500, 0.5, "outlier"),         # group 1
+    (6, 5, 4, 257, 0.75, "mixed"),          # group 2
+    (6, 5, 16, 300, 0.5, "normal"),         # group 8
+    (16, 4, 8, 200, 0.1, "outlier"),
+    (65536, 65536, 8, 90, 0.5, "normal"),
+])
+def test_rotated_any_levels_and_groups(Lh, Ll, Hq, n, r, kind):
+    """Rotation on every level pair and query group: the rotated quantizer
+    (generic tile) bit-exact, decode over the generic kernel within the
+    tolerance (one launch, and per layer)."""
+    _print("rotated any", Lh, Ll, Hq, n, r, kind)
+    rng = np.random.default_rng(Lh + Ll + Hq + n)
+    B, layers, kv = 2, 2, 2
+    K, V = _rows(rng, B, layers, kv, n, kind)
+    s = rng.random((B, n)).astype(np.float32)
+    k = O.topr_count(n, r)
+    cache = sk.SemKVCache(B, layers, kv, Hq, Lh, Ll, cap16(k), cap16(n - k), rotate=True)
+    perm = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    sk.semkv_rank_topr(to_dev(s), k, perm)
+    sk.semkv_quantize_pack(cache, to_dev(K), to_dev(V), perm, k)
     sk.semkv_sync_check()
-    assert_attention_close(out.cpu().numpy(), O.decode_attention(q.cpu().numpy(), op, 1.0), "refuse")
+    wp, _ = O.rank_topr_batch(s, k)
+    op = O.quantize_pack_cache(K, V, wp, k, Lh, Ll, rotate=True)
+    assert_pools_equal(gpu_pools(cache, sk), op, f"rotated ({Lh},{Ll}) Hq={Hq}")
+    q = (rng.standard_normal((B, layers, Hq, 128)) / math.sqrt(128)).astype(np.float16)
+    ref = O.decode_attention(q, op, 1.0)
+    out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
+    sk.semkv_decode_attn(cache, to_dev(q), out)
+    sk.semkv_sync_check()
+    e = assert_attention_close(out.cpu().numpy(), ref, f"rotated ({Lh},{Ll}) Hq={Hq} decode")
+    for layer in range(layers):
+        o1 = torch.empty((B, 1, Hq, 128), dtype=torch.float32, device="cuda")
+        sk.semkv_decode_attn(cache, to_dev(q[:, layer:layer + 1]), o1, layer0=layer)
+        sk.semkv_sync_check()
+        assert_attention_close(o1.cpu().numpy(), ref[:, layer:layer + 1],
+                               f"rotated ({Lh},{Ll}) Hq={Hq} layer {layer}")
+    _print(f"   decode error {e:.3e}")
 
 
-@pytest.mark.parametrize("block,n0,steps,r", [(128, 150, 300, 0.25), (16, 70, 53, 0.35),
-                                              (512, 200, 130, 0.5)])
-def test_rotated_generation(block, n0, steps, r):
+@pytest.mark.parametrize("block,n0,steps,r,Lh,Ll,Hq", [
+    (128, 150, 300, 0.25, 6, 5, 8), (16, 70, 53, 0.35, 6, 5, 8), (512, 200, 130, 0.5, 6, 5, 8),
+    (64, 50, 100, 0.5, 6, 6, 8),            # uniform levels, matrix-core decode
+    (16, 40, 45, 0.25, 8, 6, 4),            # generic decode with a tail, group 2
+    (32, 33, 70, 0.5, 5, 4, 16),            # group 8
+])
+def test_rotated_generation(block, n0, steps, r, Lh, Ll, Hq):
     """Generation on a rotated cache (SemKV Fig. 6 with Table 2's rotated
     quantizer): full blocks are rotated and quantized, the fp16 tail is read
     unrotated; pools bit-exact and decode (one launch and per layer) within
     the decode tolerance at steps inside and at the ends of blocks."""
-    _print("rotated generation", block, n0, steps, r)
+    _print("rotated generation", block, n0, steps, r, Lh, Ll, Hq)
     rng = np.random.default_rng(block + steps)
-    B, layers, kv, Hq = 2, 2, 2, 8
+    B, layers, kv = 2, 2, 2
     K0, V0 = _rows(rng, B, layers, kv, n0, "outlier")
     s0 = rng.random((B, n0)).astype(np.float32)
     k0 = O.topr_count(n0, r)
     tot = n0 + steps
-    cache = sk.SemKVCache(B, layers, kv, Hq, 6, 5, cap16(tot), cap16(tot), block=block,
+    cache = sk.SemKVCache(B, layers, kv, Hq, Lh, Ll, cap16(tot), cap16(tot), block=block,
                           max_tokens=tot + block, rotate=True)
     perm = torch.empty((B, n0), dtype=torch.int32, device="cuda")
     sk.semkv_rank_topr(to_dev(s0), k0, perm)
     sk.semkv_quantize_pack(cache, to_dev(K0), to_dev(V0), perm, k0)
-    ref = O.GenerationCache(layers=layers, kv_heads=kv, L_high=6, L_low=5, r=r, block=block,
+    ref = O.GenerationCache(layers=layers, kv_heads=kv, L_high=Lh, L_low=Ll, r=r, block=block,
                             batch=B, rotate=True)
     ref.prompt(K0, V0, s0)
     ks = rng.standard_normal((steps, B, layers, kv, 128)).astype(np.float16)
@@ -170,15 +193,16 @@ def test_rotated_generation(block, n0, steps, r):
     assert_pools_equal(gpu_pools(cache, sk), ref.pools, "rotated generation after flush")
 
 
-@pytest.mark.parametrize("Lh,Ll", [(6, 6), (5, 5)])
-def test_rotated_uniform_levels(Lh, Ll):
+@pytest.mark.parametrize("Lh,Ll,kind", [(6, 6, "outlier"), (5, 5, "outlier"), (6, 6, "mixed"),
+                                         (5, 5, "mixed")])
+def test_rotated_uniform_levels(Lh, Ll, kind):
     """Rotation on caches of one level count (the generic quantize tile with
     the rotation, the matrix-core decode): bit-exact pools, decode within
     the tolerance."""
-    _print("rotated uniform", Lh, Ll)
+    _print("rotated uniform", Lh, Ll, kind)
     rng = np.random.default_rng(Lh * 10 + Ll)
     B, layers, kv, Hq, n = 1, 2, 2, 8, 900
-    K, V = _rows(rng, B, layers, kv, n, "outlier")
+    K, V = _rows(rng, B, layers, kv, n, kind)
     s = rng.random((B, n)).astype(np.float32)
     k = O.topr_count(n, 0.5)
     cache = sk.SemKVCache(B, layers, kv, Hq, Lh, Ll, cap16(k), cap16(n - k), rotate=True)
