@@ -217,6 +217,22 @@ semkv_status semkv_decode_partials(const semkv_cache* c, const uint16_t* q, int3
 semkv_status semkv_decode_merge(const semkv_cache* c, int32_t nlayers, float* out,
                                 void* workspace, int64_t ws_bytes, void* stream);
 
+/* semkv_decode_attn without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The split-K partials live in a static device array
+ * of semkv_decode_noalloc_scratch_bytes() = 64 MiB that the library holds on
+ * each device it runs on until the process ends; no call allocates or frees.
+ * Same arguments, output and errors as semkv_decode_attn, except: EWORKSPACE
+ * when this call's partials (2080 bytes per (sequence, layer, KV head, chunk)
+ * with 4 query heads per KV head; about 16k such records) exceed that array;
+ * EHIP if the array's device address cannot be looked up.  Every call on one
+ * device shares that device's array and nothing in it needs to start at
+ * zero; calls that overlap on one device (concurrent streams, or threads)
+ * race on it and must be serialised by the caller. */
+semkv_status semkv_decode_attn_noalloc(const semkv_cache* c, const uint16_t* q, int32_t layer0,
+                                       int32_t nlayers, float sm_scale, float* out, void* stream);
+int64_t semkv_decode_noalloc_scratch_bytes(void);
+
 /* Synchronise `stream` and map a sticky HIP error to SEMKV_EHIP. */
 semkv_status semkv_sync_check(void* stream);
 

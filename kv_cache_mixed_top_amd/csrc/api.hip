@@ -1,5 +1,6 @@
 // C ABI of the SemKV hot path: host-side validation and kernel launches.
 // Declarations and the contract of every entry point are in include/semkv.h.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -164,6 +165,32 @@ semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0
   const int64_t need = units * a->nchunks * per_chunk_bytes;
   if (!ws || !aligned(ws, 256) || ws_bytes < need) return SEMKV_EWORKSPACE;
   return SEMKV_OK;
+}
+
+// ---- scratch of the no-allocation decode entry point (semkv_decode_attn_noalloc)
+// A file-scope device array holds that entry point's split-K partials, so it
+// needs no caller workspace and never allocates.  Each device that runs the
+// library holds its own copy until the process ends.  In host code the
+// array's name is only a stand-in: its device address is looked up once per
+// device with hipGetSymbolAddress, with that device current, and only that
+// address is ever handed to kernels.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxScratchDevices];
+
+// Device address of the current device's scratch, or null on failure.
+// Concurrent first calls look up the same address.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
 }
 
 }  // namespace
@@ -392,6 +419,25 @@ semkv_status semkv_decode_attn(const semkv_cache* c, const uint16_t* q, int32_t 
   if (st != SEMKV_OK) return st;
   return from_hip(launch_decode_merge(a, (hipStream_t)stream));
 }
+
+semkv_status semkv_decode_attn_noalloc(const semkv_cache* c, const uint16_t* q, int32_t layer0,
+                                       int32_t nlayers, float sm_scale, float* out, void* stream) {
+  if (!q || !aligned(q, 16) || !out || !aligned(out, 16)) return SEMKV_EINVAL;
+  void* ws = device_scratch();
+  if (!ws) return SEMKV_EHIP;
+  DecodeArgs a;
+  // the partials must fit the static scratch: decode_args picks the chunking
+  // for kScratchBytes of workspace and reports EWORKSPACE if even the
+  // coarsest chunking does not fit
+  semkv_status st =
+      decode_args(c, q, layer0, nlayers, sm_scale, out, ws, kScratchBytes, &a);
+  if (st != SEMKV_OK) return st;
+  st = from_hip(launch_decode_partials(a, (hipStream_t)stream));
+  if (st != SEMKV_OK) return st;
+  return from_hip(launch_decode_merge(a, (hipStream_t)stream));
+}
+
+int64_t semkv_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 semkv_status semkv_sync_check(void* stream) {
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);

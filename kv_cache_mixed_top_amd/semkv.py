@@ -59,6 +59,9 @@ _SIGS = {
     "semkv_decode_partials": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_i32, c_i32, c_f32,
                                       c_p, c_i64, c_p]),
     "semkv_decode_merge": (c_i32, [ctypes.POINTER(semkv_cache), c_i32, c_p, c_p, c_i64, c_p]),
+    "semkv_decode_attn_noalloc": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_i32, c_i32, c_f32,
+                                          c_p, c_p]),
+    "semkv_decode_noalloc_scratch_bytes": (c_i64, []),
     "semkv_sync_check": (c_i32, [c_p]),
     "semkv_status_str": (ctypes.c_char_p, [c_i32]),
 }
@@ -238,6 +241,22 @@ def semkv_decode_attn(cache: "SemKVCache", q, out, layer0=0, sm_scale=1.0, works
     _check("semkv_decode_attn",
            _lib.semkv_decode_attn(ctypes.byref(cache.c), _ptr(q), layer0, q.shape[1], sm_scale,
                                   _ptr(out), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def semkv_decode_attn_noalloc(cache: "SemKVCache", q, out, layer0=0, sm_scale=1.0, stream=None):
+    """semkv_decode_attn with the partials in the library's static device
+    scratch (no workspace argument, nothing allocated)."""
+    _dense(q, "q", torch.float16, cache)
+    _dense(out, "out", torch.float32, cache)
+    if out.shape[1] != q.shape[1]:
+        raise ValueError("q and out must cover the same layers")
+    _check("semkv_decode_attn_noalloc",
+           _lib.semkv_decode_attn_noalloc(ctypes.byref(cache.c), _ptr(q), layer0, q.shape[1],
+                                          sm_scale, _ptr(out), _stream(stream)))
+
+
+def semkv_decode_noalloc_scratch_bytes() -> int:
+    return _lib.semkv_decode_noalloc_scratch_bytes()
 
 
 def semkv_decode_partials(cache: "SemKVCache", q, layer0=0, sm_scale=1.0, workspace=None,
