@@ -12,16 +12,13 @@
 // Per 64-row tile:
 //  * Staging: direct global->LDS loads of the next tile through a buffer
 //    resource over the plane (range-checked, no per-lane address math).
-//  * Digits: a field value x enters as the fp16 value 1536 + x (one v_perm
+//  * Floors: a field value x enters as the fp16 value 1536 + x (one v_perm
 //    puts the byte under a 0x66 high byte); one packed fp16 FMA with the
-//    constants below gives 1536 + floor(x / L) exactly, and the digits
-//    follow with exact fp16 subtracts and FMAs.  All MFMA operands are
-//    normal fp16 values (a chain with subnormal operands measured ~100x
-//    larger rounding on gfx950).
-//  * QK^T on the 4x4x4 (16-block) f16 MFMA.  Lane t owns token row t of the
-//    row-major K plane.  The 4 query heads are the A operand; cbsz = 4
-//    broadcasts block `abid`'s A to all 16 blocks, so the q fragments of 16
-//    consecutive instructions share one VGPR pair.
+//    constants below gives 1536 + floor(x / L) exactly, applied twice for
+//    floor(x / L^2).
+//  * QK^T on the int8 matrix cores (16x16x64): the features x, floor(x/L),
+//    floor(x/L^2) of every field against a transformed fixed-point query in
+//    four signed limbs, products and sums exact in int32 (see qk_wave_i8).
 //  * logit z = sm_scale * log2(e) * (scale_K * (q . c) + min_K * sum(q)), in
 //    log2 units; the weights are taken against a per-head frame a margin
 //    above the running maximum, which rises (and rescales the accumulators)
@@ -29,10 +26,13 @@
 //  * PV on the 16x16x32 f16 MFMA with K = 32 tokens.  V planes are stored
 //    byte-planar in 16-row tiles (byte j of 16 consecutive rows is
 //    contiguous), so one 8-byte LDS read gives one code byte of 8 tokens.
-//    The A operand is w = p * scale_V * 2^E (E per chunk keeps w below 2^14)
-//    split into two fp16 terms w_hi (A rows 0-3) + w_lo (rows 4-7), so the
-//    weights keep ~22 bits: with heavy-tailed V the min_V and scale_V * code
-//    terms nearly cancel and a single fp16 weight (11 bits) is not enough.
+//    The A operand is w = p * scale_V * 2^E (E per chunk, from the first
+//    tile's largest scale and lowered if a later tile needs it, keeps w
+//    below 2^15) split into two fp16 terms w_hi (A rows 0-3) + w_lo (rows
+//    4-7), so the weights keep ~22 bits: with heavy-tailed V the min_V and
+//    scale_V * code terms nearly cancel and a single fp16 weight (11 bits)
+//    is not enough.  All f16 MFMA operands are normal fp16 values (a chain
+//    with subnormal operands measured ~100x larger rounding on gfx950).
 //    The B operand holds the linear features of each packed field f: f,
 //    floor(f/L), floor(f/L^2), centred on integer midpoints of their ranges.
 //    The digits are linear in them (c0 = f - L*f1, c1 = f1 - L*f2, c2 = f2),
@@ -49,7 +49,6 @@
 namespace semkv {
 namespace {
 
-typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -58,7 +57,6 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 constexpr int kTile = 64;
 constexpr int kBuf = 3072;          // 3 x 1 KB load blocks (>= 64 * 43 + 48 read slack)
 constexpr int kPartialStride = 2 + kHeadDim;
-constexpr int kQkInstr = 33;        // 4x4x4 MFMAs per row (132 digit slots)
 constexpr float kFrameMargin = 8.0f; // softmax frame above the running max (natural log)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -67,9 +65,6 @@ __device__ __forceinline__ uint32_t u32(u16x2 v) { return __builtin_bit_cast(uin
 __device__ __forceinline__ u16x2 v2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
 __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
   return __builtin_amdgcn_perm(s0, s1, sel);
-}
-__device__ __forceinline__ h4 as_h4(uint32_t lo, uint32_t hi) {
-  return __builtin_bit_cast(h4, make_uint2(lo, hi));
 }
 __device__ __forceinline__ h8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return __builtin_bit_cast(h8, make_uint4(a, b, c, d));
@@ -89,22 +84,6 @@ template <int L>
 __device__ __forceinline__ h2 floor_div(h2 v) {   // 1536 + x -> 1536 + floor(x / L)
   constexpr _Float16 m = (_Float16)floor_m<L>(), k = (_Float16)floor_k<L>();
   return __builtin_elementwise_fma(v, (h2){m, m}, (h2){k, k});
-}
-
-// Two biased field values -> their three base-L digits as exact fp16 integers.
-template <int L>
-__device__ __forceinline__ void digits(uint32_t x, uint32_t& c0, uint32_t& c1, uint32_t& c2) {
-  constexpr _Float16 B = (_Float16)kBase, nL = (_Float16)(-L);
-  const h2 X = __builtin_bit_cast(h2, x);
-  const h2 F1 = floor_div<L>(X);
-  const h2 F2 = floor_div<L>(F1);
-  const h2 d2 = F2 - (h2){B, B};
-  const h2 f1 = F1 - (h2){B, B};
-  const h2 d1 = __builtin_elementwise_fma(d2, (h2){nL, nL}, f1);
-  const h2 d0 = __builtin_elementwise_fma(f1, (h2){nL, nL}, X - (h2){B, B});
-  c0 = __builtin_bit_cast(uint32_t, d0);
-  c1 = __builtin_bit_cast(uint32_t, d1);
-  c2 = __builtin_bit_cast(uint32_t, d2);
 }
 
 // Integer centres of the PV features f, floor(f/L), floor(f/L^2) near the
@@ -135,45 +114,6 @@ __device__ __forceinline__ void features(uint32_t x, uint32_t& g0, uint32_t& g1,
   g2 = __builtin_bit_cast(uint32_t, F2 - (h2){a2, a2});
 }
 
-// Query fragments of the QK^T product (ABID-packed 4x4x4 A operands).  With
-// kLo (a rotated cache) the query is the fp32 rotation H q, carried as its
-// nearest fp16 `hi` plus the fp16 remainder `lo` (about 22 bits), so that the
-// logits do not inherit an fp16 rounding of H q; each product then takes one
-// more MFMA into the same accumulator.
-template <bool kLo>
-struct QFrag {
-  h4 hi[3];
-  h4 lo[kLo ? 3 : 1];
-};
-
-template <int S, bool kLo>
-__device__ __forceinline__ f4 qk_mfma(const QFrag<kLo>& qf, uint32_t lo, uint32_t hi, f4 acc) {
-  acc = __builtin_amdgcn_mfma_f32_4x4x4f16(qf.hi[S / 16], as_h4(lo, hi), acc, 4, S % 16, 0);
-  if constexpr (kLo)
-    acc = __builtin_amdgcn_mfma_f32_4x4x4f16(qf.lo[S / 16], as_h4(lo, hi), acc, 4, S % 16, 0);
-  return acc;
-}
-
-// ---- 6 levels: one K row = 43 bytes = 11 dwords (the 44th byte masked)
-template <int W, int NC, bool kLo>
-__device__ __forceinline__ void qk6_dword(const uint32_t (&d)[12], const QFrag<kLo>& qf,
-                                          f4 (&acc)[3]) {
-  const uint32_t X = d[W];
-  const uint32_t xe = perm(kBias, X, 0x04020400u);   // bytes 4W, 4W+2 -> biased slots
-  const uint32_t xo = perm(kBias, X, 0x04030401u);   // bytes 4W+1, 4W+3
-  uint32_t e0, e1, e2, o0, o1, o2;
-  digits<6>(xe, e0, e1, e2);
-  digits<6>(xo, o0, o1, o2);
-  acc[0 % NC] = qk_mfma<3 * W + 0, kLo>(qf, e0, o0, acc[0 % NC]);
-  acc[1 % NC] = qk_mfma<3 * W + 1, kLo>(qf, e1, o1, acc[1 % NC]);
-  acc[2 % NC] = qk_mfma<3 * W + 2, kLo>(qf, e2, o2, acc[2 % NC]);
-}
-template <int NC, bool kLo, int... Ws>
-__device__ __forceinline__ void qk6(const uint32_t (&d)[12], const QFrag<kLo>& qf, f4 (&acc)[3],
-                                    std::integer_sequence<int, Ws...>) {
-  (qk6_dword<Ws, NC, kLo>(d, qf, acc), ...);
-}
-
 // ---- 5 levels: one K row = 38 bytes; 7-byte units hold 8 fields of 7 bits.
 // From a word W with fields at bits 0, 7, 14, 21: slots (F0, F2) and (F1, F3).
 // `bias` is 0x66006600 held in a register, so that each mask and OR is one
@@ -193,55 +133,6 @@ __device__ __forceinline__ uint32_t bias_register() {
   asm volatile("v_mov_b32 %0, 0x66006600" : "=v"(b));
   return b;
 }
-template <int Q, int NC, bool kLo>   // Q = 2u + quad
-__device__ __forceinline__ void qk5_quad(uint32_t W, const QFrag<kLo>& qf, f4 (&acc)[3],
-                                         uint32_t bias) {
-  uint32_t pa, pb, a0, a1, a2, b0, b1, b2;
-  field_pairs(W, pa, pb, bias);
-  digits<5>(pa, a0, a1, a2);
-  digits<5>(pb, b0, b1, b2);
-  acc[0 % NC] = qk_mfma<3 * Q + 0, kLo>(qf, a0, b0, acc[0 % NC]);
-  acc[1 % NC] = qk_mfma<3 * Q + 1, kLo>(qf, a1, b1, acc[1 % NC]);
-  acc[2 % NC] = qk_mfma<3 * Q + 2, kLo>(qf, a2, b2, acc[2 % NC]);
-}
-template <int U, int NC, bool kLo>
-__device__ __forceinline__ void qk5_unit(const uint32_t (&d)[12], const QFrag<kLo>& qf,
-                                         f4 (&acc)[3], uint32_t bias) {
-  constexpr int b0 = 7 * U;
-  const uint32_t lo = __builtin_amdgcn_alignbyte(d[b0 / 4 + 1], d[b0 / 4], b0 % 4);
-  if (U < 5) {
-    constexpr int b1 = 7 * U + 4;
-    const uint32_t hi = __builtin_amdgcn_alignbyte(d[b1 / 4 + 1], d[b1 / 4], b1 % 4);
-    const uint32_t m = __builtin_amdgcn_alignbit(hi, lo, 28);
-    qk5_quad<2 * U, NC, kLo>(lo, qf, acc, bias);
-    qk5_quad<2 * U + 1, NC, kLo>(m, qf, acc, bias);
-  } else {
-    qk5_quad<2 * U, NC, kLo>(lo, qf, acc, bias);   // fields 40..42 and one zero pad field
-  }
-}
-template <int NC, bool kLo, int... Us>
-__device__ __forceinline__ void qk5(const uint32_t (&d)[12], const QFrag<kLo>& qf, f4 (&acc)[3],
-                                    uint32_t bias, std::integer_sequence<int, Us...>) {
-  (qk5_unit<Us, NC, kLo>(d, qf, acc, bias), ...);
-}
-
-// d index of slot `i` (0..3) of QK instruction s, or -1 for a zero slot.
-template <int L>
-__device__ __forceinline__ int qk_slot_dim(int s, int i) {
-  const int order[4] = {0, 2, 1, 3};
-  if (L == 6) {
-    const int w = s / 3, k = s % 3;
-    const int byte = 4 * w + order[i];
-    const int d = 3 * byte + k;
-    return (byte < 43 && d < kHeadDim) ? d : -1;
-  } else {
-    const int q = s / 3, k = s % 3;           // q = 2u + quad
-    const int f = 4 * q + order[i];           // fields 8u + 4quad + {0,2,1,3}
-    const int d = 3 * f + k;
-    return (f < 43 && d < kHeadDim) ? d : -1;
-  }
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -256,29 +147,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
   return v;
-}
-
-// Largest V scale (the low half of the meta word) over rows [r0, r1), as
-// fp16 bits, in every lane.  r0 is a multiple of 4 and the meta plane is
-// 16-byte aligned, so the rows are read four to a 16-byte load, sixteen loads
-// per lane in flight: a chunk of up to 4096 rows costs one memory latency.
-__device__ __forceinline__ uint32_t chunk_scale_max(const uint32_t* vmg, int64_t r0, int64_t r1,
-                                                    int lane) {
-  constexpr int kDepth = 16;
-  uint32_t smax = 0;
-  const int64_t n4 = (r1 - r0) >> 2;
-  const uint4* g4 = reinterpret_cast<const uint4*>(vmg + r0);
-  for (int64_t i = lane; i < n4; i += 64 * kDepth) {
-    uint4 v[kDepth];
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k) v[k] = g4[min(i + 64 * k, n4 - 1)];   // repeats are harmless
-#pragma unroll
-    for (int k = 0; k < kDepth; ++k)
-      smax = max(smax, max(max(v[k].x & 0xFFFFu, v[k].y & 0xFFFFu), max(v[k].z & 0xFFFFu, v[k].w & 0xFFFFu)));
-  }
-  const int64_t rr = r0 + 4 * n4 + lane;           // the last (r1 - r0) % 4 rows
-  if (rr < r1) smax = max(smax, vmg[rr] & 0xFFFFu);
-  return wave_max_u32(smax);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -358,8 +226,6 @@ struct Stage2 {
   uint8_t *v0, *v1;            // wave 1 staging
   float *z0, *z1;              // logits of the last two tiles, [4][kTile] + maxima [4]
   _Float16* w;                 // wave 1: weights hi, lo, [2 * 4 * kTile]
-  _Float16* qr;                // wave 0: the rotated queries of a rotated cache, hi and
-                               // lo, [2][4][128]
   __device__ uint8_t* k(int b) const { return b ? k1 : k0; }
   __device__ uint8_t* v(int b) const { return b ? v1 : v0; }
   __device__ float* z(int b) const { return b ? z1 : z0; }
@@ -390,148 +256,286 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const void* base, i
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// ---- QK^T on the int8 matrix cores (wave 0 of the two-wave kernel).
+//
+// A field value f of L-level codes (f = c0 + L c1 + L^2 c2) gives the
+// features f, F1 = floor(f / L), F2 = floor(f / L^2), and the digits are
+// linear in them: c0 = f - L F1, c1 = F1 - L F2, c2 = F2.  So the query's part
+// of a field, q_a c0 + q_b c1 + q_c c2, equals
+//   q_a f + (q_b - L q_a) F1 + (q_c - L q_b) F2,
+// a dot product of small non-negative integers (the features) with a
+// transformed query.  The query of each head is first put on a fixed-point
+// grid, qint = rint(q 2^S) with |qint| < 2^27 (S from the head's largest
+// component; the grid step is 2^-27 of it), so the transformed coefficients
+// are exact integers below 2^30.  Each coefficient is split into four signed
+// base-256 digits (limbs), and v_mfma_i32_16x16x64_i8 multiplies them with
+// the features exactly: A rows are (head, limb) = 16 rows, B columns are 16
+// tokens, K runs over 64 feature bytes; the four limb sums of a head are
+// recombined per token in fp32.  Integer products need no centring of the
+// features, so a feature costs one packed fp16 FMA (the floor trick below) and
+// no subtraction.
+//
+// Layout of one 16-token set: lane (n, kg) = (lane & 15, lane >> 4) holds
+// token 4n + s of the tile (s = set) and k-group kg: bytes 12kg .. 12kg+11 of
+// a 6-level row (fields 12kg + 0..11), or fields 11kg + 0..10 of a 5-level
+// row (a 77-bit window).  Its B bytes per set are, in order:
+//   6 levels: F0 of its 12 fields (raw bytes XOR 0x80: f - 128 as int8),
+//             then F1 and F2 as fp16 slots 1536 + F (low byte F, high byte
+//             0x66), two fields per dword: 15 dwords + 1 zero = 4 MFMAs;
+//   5 levels: per group of 4 fields, the slots of f (low byte f < 128), F1
+//             and F2: 18 dwords + 2 zeros = 5 MFMAs.
+// The A bytes facing a slot's 0x66 byte, a field past the row or a zero dword
+// are 0.  The constant -128 of the XORed bytes is added back through the
+// MFMA's C input: 128 * sum of the F0 coefficients, in limbs.  The C output
+// of lane (n, g) is the four limb sums of head g for token 4n + s.
+
+typedef int i4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i4 mfma_i8(i4 a, i4 b, i4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ i4 as_i4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return __builtin_bit_cast(i4, make_uint4(a, b, c, d));
+}
+// Signed base-256 digits of x in [-0x80808080, 0x7F7F7F7F] as four int8
+// bytes (lowest digit first): sum_k digit_k 256^k = x.
+__device__ __forceinline__ uint32_t limb_bytes(int32_t x) {
+  return ((uint32_t)x + 0x80808080u) ^ 0x80808080u;
+}
+__device__ __forceinline__ uint32_t floor_slots(uint32_t x, int L) {   // see floor_div
+  return L == 6 ? __builtin_bit_cast(uint32_t, floor_div<6>(__builtin_bit_cast(h2, x)))
+                : __builtin_bit_cast(uint32_t, floor_div<5>(__builtin_bit_cast(h2, x)));
+}
+
+constexpr int kCoefSlots = 48;   // per (head, feature): 4 k-groups x 12
+
+// LDS of the query preparation of wave 0 (once per chunk).
+struct QPrep {
+  int32_t qint[4][kHeadDim + 4];                 // fixed-point queries, 4 zero pads
+  uint32_t coef[4][3][kCoefSlots];               // limb bytes of the coefficients
+};
+
 template <int L, bool kRot>
-__device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0, int64_t r1, int b, int li,
-                        int g, Stage2& st) {
+__device__ __forceinline__ void qk_wave_i8(const DecodeArgs& a, int seg, int64_t r0, int64_t r1,
+                                           int b, int li, int g, Stage2& st, QPrep& qp) {
   constexpr int R = (L == 6) ? 43 : 38;
+  constexpr int NM = (L == 6) ? 4 : 5;          // MFMAs per 16-token set
   const int lane = threadIdx.x & 63;
+  const int n = lane & 15, kg = lane >> 4;
   const int layer = a.layer0 + li;
   const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
   const int cap = (int)a.cap[seg];            // cap * R < 2^31 (checked by the launcher)
   const int ir0 = (int)r0, ir1 = (int)r1;
   const uint8_t* kcodes = a.codes[seg] + plane_k * cap * R;
   const uint32_t* kmg = a.meta[seg] + plane_k * cap;
-  const float sm = a.sm_scale * kLog2e;   // logits in log2 units
   const uint32_t bias5 = L == 5 ? bias_register() : 0u;   // 5-level field bias
 
-  // queries: ABID-packed 4x4x4 A fragments and per-head sums (loaded once
-  // the first K tile is in flight)
-  QFrag<kRot> qf;
-  float sumq[4];
-  // The 3 KB of K bytes from row t0 on -> buffer `buf` (16 bytes per lane per
-  // instruction), and the lane's K meta word -> register.  The plane from
-  // row t0 is a buffer resource built on the scalar unit: the loads need no
-  // per-lane address arithmetic, and bytes past the plane read as zeros (the
-  // rows past the tile are not used).
-  uint32_t km_next = 0;
+  // The 3 KB of K bytes from row t0 on -> buffer `buf`, and the K meta words
+  // of tokens 4n .. 4n+3 -> registers (bytes past the plane read as zeros).
+  uint4 km_next = make_uint4(0u, 0u, 0u, 0u);
   const uint32_t lane16 = 16u * (uint32_t)lane;
   auto issue = [&](int buf, int t0) {
     const __amdgpu_buffer_rsrc_t rk = plane_rsrc(kcodes + t0 * R, (cap - t0) * R);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 1024, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 2048, 0);
-    km_next = __builtin_amdgcn_raw_buffer_load_b32(plane_rsrc(kmg + t0, (cap - t0) * 4), 4 * lane, 0, 0);
+    km_next = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(plane_rsrc(kmg + t0, (cap - t0) * 4), 16 * n, 0, 0));
   };
+  if (ir0 < ir1) issue(0, ir0);
 
-  float frame[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  // One tile in staging buffer B (a compile-time constant, so that reads of
-  // buffer B are known not to overlap the loads in flight into 1 - B).
+  // ---- queries (once per chunk, while the first K tile is in flight)
+  const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
+                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
+  float cA, cB;                       // this lane's head (kg): logit = cA s_K z + cB m_K
+  {
+    const float sm = a.sm_scale * kLog2e;   // logits in log2 units
+    float cA4[4], cB4[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float y0 = (float)qg[h * kHeadDim + 2 * lane], y1 = (float)qg[h * kHeadDim + 2 * lane + 1];
+      if constexpr (kRot) {
+        // rotated cache: q -> H q in fp32 (index bit 0 within the lane,
+        // bits 1-6 across lanes)
+        constexpr float kNorm = 0.08838834764831845f;   // 1/sqrt(128)
+        float u0 = y0 + y1, u1 = y0 - y1;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          const float p0 = __shfl_xor(u0, m, 64), p1 = __shfl_xor(u1, m, 64);
+          const bool upper = (lane & m) != 0;
+          u0 = upper ? p0 - u0 : u0 + p0;
+          u1 = upper ? p1 - u1 : u1 + p1;
+        }
+        y0 = u0 * kNorm;
+        y1 = u1 * kNorm;
+      }
+      const float mx = wave_max(fmaxf(fabsf(y0), fabsf(y1)));
+      const int S = mx > 0.0f ? 26 - ilogbf(mx) : 0;
+      qp.qint[h][2 * lane] = (int32_t)rintf(ldexpf(y0, S));
+      qp.qint[h][2 * lane + 1] = (int32_t)rintf(ldexpf(y1, S));
+      if (lane < 4) qp.qint[h][kHeadDim + lane] = 0;
+      cA4[h] = sm * ldexpf(1.0f, -S);
+      cB4[h] = sm * wave_sum(y0 + y1);
+    }
+    cA = kg == 0 ? cA4[0] : kg == 1 ? cA4[1] : kg == 2 ? cA4[2] : cA4[3];
+    cB = kg == 0 ? cB4[0] : kg == 1 ? cB4[1] : kg == 2 ? cB4[2] : cB4[3];
+  }
+  wait_lgkm0();   // the wave's qint writes have landed
+  // coefficient limbs: slot kgs * 12 + j of (head, feature) is field 12 kgs + j
+  // (6 levels) or 11 kgs + j for j < 11 (5 levels); fields past 42 are 0
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const int idx = lane + 64 * p;                 // (head, slot), 192 of them
+    const int h = idx / kCoefSlots, slot = idx - h * kCoefSlots;
+    const int kgs = slot / 12, j = slot - kgs * 12;
+    const int f = L == 6 ? slot : (j < 11 ? 11 * kgs + j : 99);
+    uint32_t c0 = 0, c1 = 0, c2 = 0;
+    if (f < 43) {
+      const int qa = qp.qint[h][3 * f], qb = qp.qint[h][3 * f + 1], qc = qp.qint[h][3 * f + 2];
+      c0 = limb_bytes(qa);
+      c1 = limb_bytes(qb - L * qa);
+      c2 = limb_bytes(qc - L * qb);
+    }
+    qp.coef[h][0][slot] = c0;
+    qp.coef[h][1][slot] = c1;
+    qp.coef[h][2][slot] = c2;
+  }
+  wait_lgkm0();
+  // A operands: lane (row r = 4 h + k, kg) holds limb k of head h's
+  // coefficients for the B bytes of k-group kg, in the same order
+  i4 A[NM];
+  i4 cinit = {0, 0, 0, 0};
+  {
+    const int h = n >> 2, k = n & 3;
+    const uint32_t kk = (uint32_t)k;
+    const uint32_t sel_pair = kk | 0x0C00u | ((4u + kk) << 16) | 0x0C000000u;   // [x.k, 0, y.k, 0]
+    const uint32_t sel_lo = kk | ((4u + kk) << 8) | 0x0C0C0000u;                // [x.k, y.k, 0, 0]
+    const uint32_t sel_hi = 0x0C0Cu | (kk << 16) | ((4u + kk) << 24);           // [0, 0, x.k, y.k]
+    uint32_t w[4 * NM];
+    auto row = [&](int type, int j0) {
+      return *reinterpret_cast<const uint4*>(&qp.coef[h][type][kg * 12 + j0]);
+    };
+    if constexpr (L == 6) {
+      int f0sum = 0;
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const uint4 c0 = row(0, 4 * q), c1 = row(1, 4 * q), c2 = row(2, 4 * q);
+        w[q] = perm(c0.y, c0.x, sel_lo) | perm(c0.w, c0.z, sel_hi);
+        f0sum = __builtin_amdgcn_sdot4((int)w[q], 0x01010101, f0sum, false);
+        w[3 + 2 * q] = perm(c1.z, c1.x, sel_pair);
+        w[4 + 2 * q] = perm(c1.w, c1.y, sel_pair);
+        w[9 + 2 * q] = perm(c2.z, c2.x, sel_pair);
+        w[10 + 2 * q] = perm(c2.w, c2.y, sel_pair);
+      }
+      w[15] = 0;
+      // the XORed bytes are f - 128: add 128 * sum of the F0 coefficients,
+      // limb by limb, through the C input (rows 4 g .. 4 g + 3 of lane (n, g))
+      f0sum += __shfl_xor(f0sum, 16, 64);
+      f0sum += __shfl_xor(f0sum, 32, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) cinit[i] = 128 * __shfl(f0sum, 4 * kg + i, 64);
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < 3; ++gi) {
+        const uint4 c0 = row(0, 4 * gi), c1 = row(1, 4 * gi), c2 = row(2, 4 * gi);
+        w[6 * gi + 0] = perm(c0.z, c0.x, sel_pair);
+        w[6 * gi + 1] = perm(c0.w, c0.y, sel_pair);
+        w[6 * gi + 2] = perm(c1.z, c1.x, sel_pair);
+        w[6 * gi + 3] = perm(c1.w, c1.y, sel_pair);
+        w[6 * gi + 4] = perm(c2.z, c2.x, sel_pair);
+        w[6 * gi + 5] = perm(c2.w, c2.y, sel_pair);
+      }
+      w[18] = w[19] = 0;
+    }
+#pragma unroll
+    for (int m = 0; m < NM; ++m) A[m] = as_i4(w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]);
+  }
+
+  // byte offset and bit shift of this lane's window within a row
+  const int kbyte = L == 6 ? 12 * kg : (77 * kg) >> 3;
+  const int kbit = L == 6 ? 0 : (77 * kg) & 7;
+
+  float frame = -INFINITY;   // this lane's head (kg): kFrameMargin above its running maximum
   auto tile = [&](int t0, auto Bc) {
     constexpr int B = decltype(Bc)::value;
     const int nt = min(kTile, ir1 - t0);
-    wait_vm0();   // this tile's rows have landed
-    const uint32_t km = km_next;
+    wait_vm0();   // this tile's rows and meta have landed
+    const uint4 km4 = km_next;
     if (t0 + kTile < ir1) issue(1 - B, t0 + kTile);
-    f4 sacc[3];
+    const uint32_t kmw[4] = {km4.x, km4.y, km4.z, km4.w};
+    float zz[4];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) sacc[k] = (f4){0.f, 0.f, 0.f, 0.f};
-    {
-      const int off = lane * R;
-      const uint32_t* kb32 = reinterpret_cast<const uint32_t*>(st.k(B) + (off & ~3));
-      const int sh = off & 3;
-      uint32_t d[12];
+    for (int s = 0; s < 4; ++s) {
+      const int t = 4 * n + s;
+      const int off = t * R + kbyte;
+      const uint32_t* k32 = reinterpret_cast<const uint32_t*>(st.k(B) + (off & ~3));
+      const uint32_t x0 = k32[0], x1 = k32[1], x2 = k32[2], x3 = k32[3];
+      uint32_t w[4 * NM];
+      if constexpr (L == 6) {
+        const int sh = off & 3;
+        const uint32_t d[3] = {__builtin_amdgcn_alignbyte(x1, x0, sh),
+                               __builtin_amdgcn_alignbyte(x2, x1, sh),
+                               __builtin_amdgcn_alignbyte(x3, x2, sh)};
 #pragma unroll
-      for (int i = 0; i < 11; ++i) d[i] = __builtin_amdgcn_alignbyte(kb32[i + 1], kb32[i], sh);
-      d[11] = 0;
-      if (L == 6) {
-        d[10] &= 0x00FFFFFFu;                       // byte 43 belongs to the next row
-        qk6<1, kRot>(d, qf, sacc, std::make_integer_sequence<int, 11>{});
+        for (int q = 0; q < 3; ++q) {
+          w[q] = d[q] ^ 0x80808080u;
+          const uint32_t e = perm(kBias, d[q], 0x04020400u);   // fields 4q, 4q+2 -> slots
+          const uint32_t o = perm(kBias, d[q], 0x04030401u);   // fields 4q+1, 4q+3
+          const uint32_t e1 = floor_slots(e, 6), o1 = floor_slots(o, 6);
+          w[3 + 2 * q] = e1;
+          w[4 + 2 * q] = o1;
+          w[9 + 2 * q] = floor_slots(e1, 6);
+          w[10 + 2 * q] = floor_slots(o1, 6);
+        }
+        w[15] = 0;
       } else {
-        d[9] &= 0x0000FFFFu;                        // bytes 38, 39 belong to the next row
-        d[10] = 0;
-        qk5<1, kRot>(d, qf, sacc, bias5, std::make_integer_sequence<int, 6>{});
+        const int bs = 8 * (off & 3) + kbit;                     // < 32
+        const uint32_t w0 = __builtin_amdgcn_alignbit(x1, x0, bs);
+        const uint32_t w1 = __builtin_amdgcn_alignbit(x2, x1, bs);
+        const uint32_t w2 = __builtin_amdgcn_alignbit(x3, x2, bs);
+        const uint32_t G[3] = {w0, __builtin_amdgcn_alignbit(w1, w0, 28),
+                               __builtin_amdgcn_alignbit(w2, w1, 24)};
+#pragma unroll
+        for (int gi = 0; gi < 3; ++gi) {
+          uint32_t pa, pb;
+          field_pairs(G[gi], pa, pb, bias5);
+          const uint32_t a1 = floor_slots(pa, 5), b1 = floor_slots(pb, 5);
+          w[6 * gi + 0] = pa;
+          w[6 * gi + 1] = pb;
+          w[6 * gi + 2] = a1;
+          w[6 * gi + 3] = b1;
+          w[6 * gi + 4] = floor_slots(a1, 5);
+          w[6 * gi + 5] = floor_slots(b1, 5);
+        }
+        w[18] = w[19] = 0;
       }
+      i4 acc = cinit;
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        acc = mfma_i8(A[m], as_i4(w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]), acc);
+      // limb sums of head kg -> the integer dot product in fp32
+      const int32_t tlo = (acc[1] << 8) + acc[0];
+      const int32_t thi = (acc[3] << 8) + acc[2];
+      const float zf = fmaf((float)thi, 65536.0f, (float)tlo);
+      const float sK = h2f((uint16_t)(kmw[s] & 0xFFFFu));
+      const float mK = h2f((uint16_t)(kmw[s] >> 16));
+      zz[s] = t < nt ? fmaf(sK * cA, zf, mK * cB) : -INFINITY;   // rows past the chunk: no weight
+      __builtin_amdgcn_sched_barrier(0);   // one set's temporaries live at a time
     }
-    const float kfac = sm * h2f((uint16_t)(km & 0xFFFFu));
-    const float kbias = sm * h2f((uint16_t)(km >> 16));
-    float z[4];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) z[h] = fmaf(kfac, sacc[0][h], kbias * sumq[h]);   // one accumulator chain
-    if (nt < kTile) {                          // rows past the chunk end take no weight
-#pragma unroll
-      for (int h = 0; h < 4; ++h) z[h] = lane < nt ? z[h] : -INFINITY;
-    }
-#pragma unroll
-    for (int h = 0; h < 4; ++h) st.z(B)[h * kTile + lane] = z[h];
-    // softmax frame per head, kFrameMargin above the running maximum; it is
+    *reinterpret_cast<float4*>(st.z(B) + kg * kTile + 4 * n) = make_float4(zz[0], zz[1], zz[2], zz[3]);
+    // softmax frame of head kg, kFrameMargin above the running maximum; it is
     // raised only when a logit exceeds it (in practice on the first tile)
-    const bool up = z[0] > frame[0] || z[1] > frame[1] || z[2] > frame[2] || z[3] > frame[3];
-    if (__ballot(up) != 0ull) {
+    const float zmax = fmaxf(fmaxf(zz[0], zz[1]), fmaxf(zz[2], zz[3]));
+    if (__ballot(zmax > frame) != 0ull) {
+      float m = zmax;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) frame[h] = fmaxf(frame[h], wave_max(z[h]) + kFrameMargin * kLog2e);
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      frame = fmaxf(frame, m + kFrameMargin * kLog2e);
     }
-    if (lane == 0)
-      *reinterpret_cast<float4*>(st.z(B) + 4 * kTile) =
-          make_float4(frame[0], frame[1], frame[2], frame[3]);
+    if (n == 0) st.z(B)[4 * kTile + kg] = frame;
     wait_lgkm0();  // logits written
     tile_barrier();
   };
-  if (ir0 < ir1) issue(0, ir0);
-  const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
-                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
-  // A fragments of the 4 heads' query values at `qs`
-  auto fragments = [&](const _Float16* qs, h4 (&out)[3]) {
-    const int head = lane & 3, blk = lane >> 2;
-#pragma unroll
-    for (int P = 0; P < 3; ++P) {
-      const int s = 16 * P + blk;
-      h4 v = {0, 0, 0, 0};
-      if (s < kQkInstr) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = qk_slot_dim<L>(s, i);
-          v[i] = d >= 0 ? qs[head * kHeadDim + d] : (_Float16)0.0f;
-        }
-      }
-      out[P] = v;
-    }
-  };
-  if constexpr (kRot) {
-    // rotated cache: q -> H q in fp32 (lane holds dimensions 2 lane, 2 lane + 1:
-    // index bit 0 within the lane, bits 1-6 across lanes), carried as the
-    // nearest fp16 plus the fp16 remainder; sum(H q) for the min term is
-    // taken from the fp32 values
-    constexpr float kNorm = 0.08838834764831845f;   // 1/sqrt(128)
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float x0 = (float)qg[h * kHeadDim + 2 * lane], x1 = (float)qg[h * kHeadDim + 2 * lane + 1];
-      float y0 = x0 + x1, y1 = x0 - x1;
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const float p0 = __shfl_xor(y0, m, 64), p1 = __shfl_xor(y1, m, 64);
-        const bool upper = (lane & m) != 0;
-        y0 = upper ? p0 - y0 : y0 + p0;
-        y1 = upper ? p1 - y1 : y1 + p1;
-      }
-      y0 *= kNorm;
-      y1 *= kNorm;
-      const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
-      st.qr[h * kHeadDim + 2 * lane] = h0;
-      st.qr[h * kHeadDim + 2 * lane + 1] = h1;
-      st.qr[(4 + h) * kHeadDim + 2 * lane] = (_Float16)(y0 - (float)h0);
-      st.qr[(4 + h) * kHeadDim + 2 * lane + 1] = (_Float16)(y1 - (float)h1);
-      sumq[h] = wave_sum(y0 + y1);
-    }
-    wait_lgkm0();   // the wave's LDS writes have landed
-    fragments(st.qr, qf.hi);
-    fragments(st.qr + 4 * kHeadDim, qf.lo);
-  } else {
-    fragments(qg, qf.hi);
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-      sumq[h] = wave_sum((float)qg[h * kHeadDim + 2 * lane] + (float)qg[h * kHeadDim + 2 * lane + 1]);
-  }
-
   for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 1
     tile(t0, std::integral_constant<int, 0>{});
     if (t0 + kTile < ir1) tile(t0 + kTile, std::integral_constant<int, 1>{});
@@ -551,10 +555,14 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   const uint8_t* vcodes = a.codes[seg] + (plane_k + 1) * cap * R;
   const uint32_t* vmg = a.meta[seg] + (plane_k + 1) * cap;
 
-  // per-chunk exponent E: w = p * scale_V * 2^E stays below 2^14 (set
-  // below, once the first V tile is in flight)
+  // Chunk exponent E: w = p * scale_V * 2^E (p <= 1) stays below 2^15, so
+  // that the fp16 hi/lo split of w neither overflows nor goes subnormal
+  // for the largest weights.  It is set from the first tile's largest V
+  // scale and lowered (rescaling what was accumulated) when a later tile
+  // holds a scale it cannot take.
   int E = 0;
   float two_e = 1.0f;
+  uint32_t slim = 0;        // fp16 bits of the first scale E cannot take (0: E not set yet)
 
   float mref[4], lsum[4], msum[4];
 #pragma unroll
@@ -596,6 +604,19 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
     wait_vm0();   // this tile's V has landed
     const uint32_t vm = vm_next;
     if (t0 + kTile < ir1) issue(1 - B, t0 + kTile);
+    // E from the first tile; lowered when a tile holds a scale it cannot
+    // take (then the accumulators are rescaled with the frame below)
+    const uint32_t sbits = vm & 0xFFFFu;                 // non-negative fp16: ordered as integers
+    float efac = 1.0f;
+    if (__ballot(sbits >= slim) != 0ull) {
+      const uint32_t smax = wave_max_u32(sbits);
+      const int E0 = E;
+      E = smax != 0 ? 13 - ilogbf(h2f((uint16_t)smax)) : 0;
+      two_e = ldexpf(1.0f, E);
+      efac = ldexpf(1.0f, E - E0);                       // the sums so far are 0 on the first tile
+      const int e = 15 - E;                              // scales must stay below 2^e
+      slim = e >= 16 ? 0x7C00u : e >= -14 ? (uint32_t)(e + 15) << 10 : e >= -24 ? 1u << (e + 24) : 1u;
+    }
     tile_barrier();                                      // logits of this tile are in LDS
     float z[4];
 #pragma unroll
@@ -604,15 +625,16 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
 
     // the weights are taken against the frame of wave 0; when it was raised
     // (in practice only on the first tile) what was accumulated is rescaled
-    if (fr.x != mref[0] || fr.y != mref[1] || fr.z != mref[2] || fr.w != mref[3]) {
+    if (fr.x != mref[0] || fr.y != mref[1] || fr.z != mref[2] || fr.w != mref[3] || efac != 1.0f) {
       const float nf[4] = {fr.x, fr.y, fr.z, fr.w};
       float fac[4];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
-        fac[h] = __builtin_amdgcn_exp2f(mref[h] - nf[h]);   // 2^-inf = 0 on the first tile
+        const float ff = mref[h] == nf[h] ? 1.0f : __builtin_amdgcn_exp2f(mref[h] - nf[h]);   // 2^-inf = 0 on the first tile
         mref[h] = nf[h];
-        lsum[h] *= fac[h];
-        msum[h] *= fac[h];
+        lsum[h] *= ff;
+        msum[h] *= ff;
+        fac[h] = ff * efac;
       }
 #pragma unroll
       for (int s = 0; s < 3; ++s)
@@ -683,11 +705,6 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
     }
   };
   if (ir0 < ir1) issue(0, ir0);
-  {
-    const uint32_t smax = chunk_scale_max(vmg, r0, r1, lane);
-    if (smax != 0) E = 13 - ilogbf(h2f((uint16_t)smax));
-    two_e = ldexpf(1.0f, E);
-  }
   for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 0
     tile(t0, std::integral_constant<int, 0>{});
     if (t0 + kTile < ir1) tile(t0 + kTile, std::integral_constant<int, 1>{});
@@ -700,9 +717,8 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   __shared__ __attribute__((aligned(16))) uint8_t k0[kBuf], k1[kBuf], v0[kBuf], v1[kBuf];
   __shared__ __attribute__((aligned(16))) float z0[4 * kTile + 4], z1[4 * kTile + 4];
   __shared__ __attribute__((aligned(16))) _Float16 w[2 * 4 * kTile];
-  __shared__ __attribute__((aligned(16))) _Float16 qr[kRot ? 2 * 4 * kHeadDim : 8];
+  __shared__ __attribute__((aligned(16))) QPrep qp;
   Stage2 st;
-  st.qr = qr;
   st.k0 = k0;
   st.k1 = k1;
   st.v0 = v0;
@@ -722,10 +738,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const int64_t u = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (a.fmt[seg].L == 6) {
-    if (wave == 0) qk_wave<6, kRot>(a, seg, r0, r1, b, li, g, st);
+    if (wave == 0) qk_wave_i8<6, kRot>(a, seg, r0, r1, b, li, g, st, qp);
     else pv_wave<6>(a, seg, r0, r1, b, li, g, u, st);
   } else {
-    if (wave == 0) qk_wave<5, kRot>(a, seg, r0, r1, b, li, g, st);
+    if (wave == 0) qk_wave_i8<5, kRot>(a, seg, r0, r1, b, li, g, st, qp);
     else pv_wave<5>(a, seg, r0, r1, b, li, g, u, st);
   }
 }
