@@ -211,25 +211,51 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, int64_t u, in
     }
 }
 
-// ---- two-wave form: one workgroup of two waves per chunk.  Wave 0 streams
-// the K rows and computes the logits; wave 1 streams the V tiles, keeps the
-// softmax and the PV accumulators and writes the partial record.  The
-// logits of a tile pass through LDS (double-buffered) with one workgroup
-// barrier per tile, so wave 0 computes tile t+1 while wave 1 finishes tile
-// t, and each wave holds only its own half of the state.
-// The buffers are separate LDS arrays (pointers into them are selected by
-// tile parity), so that an LDS access can be told apart from an in-flight
-// global->LDS load into another buffer; otherwise the compiler waits for the
-// loads before it.
-struct Stage2 {
-  uint8_t *k0, *k1;            // wave 0 staging, kBuf bytes each
-  uint8_t *v0, *v1;            // wave 1 staging
-  float *z0, *z1;              // logits of the last two tiles, [4][kTile] + maxima [4]
+// ---- two-wave form: one workgroup of two waves per chunk.  Wave 0 loads
+// the tiles and computes the logits; wave 1 keeps the softmax and the PV
+// accumulators and writes the partial record.  Per 64-row tile there is one
+// workgroup barrier: before it wave 0 has written the tile's logits to LDS
+// and its V bytes have landed in LDS; after it wave 1 consumes both while
+// wave 0 goes on with the next tile.
+//
+// Staging, two tiles ahead, all issued by wave 0 in this order per tile:
+// the V bytes go global->LDS into one of three buffers (read only by wave
+// 1), then the K rows and K meta go straight into registers (three register
+// slots).  Loads complete in issue order, so once wave 0 has its K rows of
+// tile t (the compiler waits for those registers before it uses them), the
+// V bytes of tile t are in LDS too; the barrier after the logits hands them
+// to wave 1.  The V buffer of tile t + 2 is the one wave 1 finished before
+// it reached the barrier of tile t, so wave 0 refills it after that barrier.
+// Wave 1 issues only its V meta loads (registers, two tiles ahead) and so
+// needs no wait for global->LDS loads before its LDS reads.  Tile slots are
+// compile-time constants (the loop is unrolled by three), and the loads of a
+// tile past the chunk go through an empty buffer range: they read nothing,
+// and every tile issues the same instructions.
+struct Stage3 {
+  uint8_t *v0, *v1, *v2;       // V tiles, kBuf bytes each
+  float *z0, *z1, *z2;         // logits [4][kTile] + frames [4]
   _Float16* w;                 // wave 1: weights hi, lo, [2 * 4 * kTile]
-  __device__ uint8_t* k(int b) const { return b ? k1 : k0; }
-  __device__ uint8_t* v(int b) const { return b ? v1 : v0; }
-  __device__ float* z(int b) const { return b ? z1 : z0; }
 };
+template <int S> __device__ __forceinline__ uint8_t* vbuf_of(const Stage3& st) {
+  return S == 0 ? st.v0 : S == 1 ? st.v1 : st.v2;
+}
+template <int S> __device__ __forceinline__ float* zbuf_of(const Stage3& st) {
+  return S == 0 ? st.z0 : S == 1 ? st.z1 : st.z2;
+}
+template <int S> using Slot = std::integral_constant<int, S>;
+
+// Tiles 0 .. n-1 in slots 0, 1, 2, 0, ...: step(Slot<S>, tile) for each.
+template <typename F>
+__device__ __forceinline__ void for_tiles(int n, F&& step) {
+  int v = 0;
+  for (; v + 3 <= n; v += 3) {
+    step(Slot<0>{}, v);
+    step(Slot<1>{}, v + 1);
+    step(Slot<2>{}, v + 2);
+  }
+  if (v < n) step(Slot<0>{}, v);
+  if (v + 1 < n) step(Slot<1>{}, v + 1);
+}
 
 // One workgroup barrier with no memory fence: the LDS writes before it are
 // waited for by the caller; outstanding global->LDS prefetches stay in flight.
@@ -317,7 +343,7 @@ struct QPrep {
 
 template <int L, bool kRot>
 __device__ __forceinline__ void qk_wave_i8(const DecodeArgs& a, int seg, int64_t r0, int64_t r1,
-                                           int b, int li, int g, Stage2& st, QPrep& qp) {
+                                           int b, int li, int g, const Stage3& st, QPrep& qp) {
   constexpr int R = (L == 6) ? 43 : 38;
   constexpr int NM = (L == 6) ? 4 : 5;          // MFMAs per 16-token set
   const int lane = threadIdx.x & 63;
@@ -327,33 +353,65 @@ __device__ __forceinline__ void qk_wave_i8(const DecodeArgs& a, int seg, int64_t
   const int cap = (int)a.cap[seg];            // cap * R < 2^31 (checked by the launcher)
   const int ir0 = (int)r0, ir1 = (int)r1;
   const uint8_t* kcodes = a.codes[seg] + plane_k * cap * R;
+  const uint8_t* vcodes = kcodes + cap * R;
   const uint32_t* kmg = a.meta[seg] + plane_k * cap;
   const uint32_t bias5 = L == 5 ? bias_register() : 0u;   // 5-level field bias
+  const int ntiles = (ir1 - ir0 + kTile - 1) / kTile;
 
-  // The 3 KB of K bytes from row t0 on -> buffer `buf`, and the K meta words
-  // of tokens 4n .. 4n+3 -> registers (bytes past the plane read as zeros).
-  uint4 km_next = make_uint4(0u, 0u, 0u, 0u);
+  // byte offset and bit shift of this lane's window within a row, and the
+  // dword-aligned offset of set s's window within a tile
+  const int kbyte = L == 6 ? 12 * kg : (77 * kg) >> 3;
+  const int kbit = L == 6 ? 0 : (77 * kg) & 7;
+  int koff[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) koff[s] = (4 * n + s) * R + kbyte;
+
+  // Tile v: its V bytes (3 KB from its first row; 16-row byte-planar tiles)
+  // -> V buffer S, then this lane's 16-byte windows of its 4 K rows and the
+  // K meta of tokens 4n .. 4n+3 -> register slot S.  Past the chunk the
+  // buffer ranges are empty (zeros, no memory traffic).
+  uint4 kx[3][4], km[3];
   const uint32_t lane16 = 16u * (uint32_t)lane;
-  auto issue = [&](int buf, int t0) {
-    const __amdgpu_buffer_rsrc_t rk = plane_rsrc(kcodes + t0 * R, (cap - t0) * R);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_at(st.k(buf), 0), 16, (int)lane16, 0, 2048, 0);
-    km_next = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(plane_rsrc(kmg + t0, (cap - t0) * 4), 16 * n, 0, 0));
+  auto issue_v = [&](lds_void* dst, int v) {
+    const bool live = v < ntiles;
+    const int t0 = ir0 + kTile * v;
+    const __amdgpu_buffer_rsrc_t rv = plane_rsrc(vcodes + (live ? t0 * R : 0), live ? (cap - t0) * R : 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, (int)lane16, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, (int)lane16, 0, 1024, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, (int)lane16, 0, 2048, 0);
   };
-  if (ir0 < ir1) issue(0, ir0);
+  auto issue = [&](auto Sc, int v) {
+    constexpr int S = decltype(Sc)::value;
+    issue_v(lds_at(vbuf_of<S>(st), 0), v);
+    const bool live = v < ntiles;
+    const int t0 = ir0 + kTile * v;
+    const int rows = live ? cap - t0 : 0;
+    const int tb = live ? t0 * R : 0;
+    const __amdgpu_buffer_rsrc_t rk = plane_rsrc(kcodes + tb, rows * R);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      kx[S][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[s] & ~3, 0, 0));
+    km[S] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(plane_rsrc(kmg + (live ? t0 : 0), rows * 4), 16 * n, 0, 0));
+  };
+  // the queries (dimensions 2 lane, 2 lane + 1 of the 4 heads) are loaded
+  // before the first tiles, so that waiting for them drains nothing else
+  const uint32_t* qg = reinterpret_cast<const uint32_t*>(a.q) +
+                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * (kHeadDim / 2);
+  uint32_t qw[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) qw[h] = qg[h * (kHeadDim / 2) + lane];
+  issue(Slot<0>{}, 0);
+  issue(Slot<1>{}, 1);
 
-  // ---- queries (once per chunk, while the first K tile is in flight)
-  const _Float16* qg = reinterpret_cast<const _Float16*>(a.q) +
-                       (((int64_t)b * a.nl + li) * a.q_heads + g * 4) * kHeadDim;
+  // ---- queries (once per chunk, while the first tiles are in flight)
   float cA, cB;                       // this lane's head (kg): logit = cA s_K z + cB m_K
   {
     const float sm = a.sm_scale * kLog2e;   // logits in log2 units
     float cA4[4], cB4[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      float y0 = (float)qg[h * kHeadDim + 2 * lane], y1 = (float)qg[h * kHeadDim + 2 * lane + 1];
+      float y0 = h2f((uint16_t)(qw[h] & 0xFFFFu)), y1 = h2f((uint16_t)(qw[h] >> 16));
       if constexpr (kRot) {
         // rotated cache: q -> H q in fp32 (index bit 0 within the lane,
         // bits 1-6 across lanes)
@@ -451,28 +509,19 @@ __device__ __forceinline__ void qk_wave_i8(const DecodeArgs& a, int seg, int64_t
     for (int m = 0; m < NM; ++m) A[m] = as_i4(w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]);
   }
 
-  // byte offset and bit shift of this lane's window within a row
-  const int kbyte = L == 6 ? 12 * kg : (77 * kg) >> 3;
-  const int kbit = L == 6 ? 0 : (77 * kg) & 7;
-
   float frame = -INFINITY;   // this lane's head (kg): kFrameMargin above its running maximum
-  auto tile = [&](int t0, auto Bc) {
-    constexpr int B = decltype(Bc)::value;
-    const int nt = min(kTile, ir1 - t0);
-    wait_vm0();   // this tile's rows and meta have landed
-    const uint4 km4 = km_next;
-    if (t0 + kTile < ir1) issue(1 - B, t0 + kTile);
-    const uint32_t kmw[4] = {km4.x, km4.y, km4.z, km4.w};
+  auto step = [&](auto Sc, int v) {
+    constexpr int S = decltype(Sc)::value;
+    const int nt = min(kTile, ir1 - ir0 - kTile * v);
+    const uint32_t kmw[4] = {km[S].x, km[S].y, km[S].z, km[S].w};
     float zz[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int t = 4 * n + s;
-      const int off = t * R + kbyte;
-      const uint32_t* k32 = reinterpret_cast<const uint32_t*>(st.k(B) + (off & ~3));
-      const uint32_t x0 = k32[0], x1 = k32[1], x2 = k32[2], x3 = k32[3];
+      const uint32_t x0 = kx[S][s].x, x1 = kx[S][s].y, x2 = kx[S][s].z, x3 = kx[S][s].w;
       uint32_t w[4 * NM];
       if constexpr (L == 6) {
-        const int sh = off & 3;
+        const int sh = koff[s] & 3;
         const uint32_t d[3] = {__builtin_amdgcn_alignbyte(x1, x0, sh),
                                __builtin_amdgcn_alignbyte(x2, x1, sh),
                                __builtin_amdgcn_alignbyte(x3, x2, sh)};
@@ -489,7 +538,7 @@ __device__ __forceinline__ void qk_wave_i8(const DecodeArgs& a, int seg, int64_t
         }
         w[15] = 0;
       } else {
-        const int bs = 8 * (off & 3) + kbit;                     // < 32
+        const int bs = 8 * (koff[s] & 3) + kbit;                 // < 32
         const uint32_t w0 = __builtin_amdgcn_alignbit(x1, x0, bs);
         const uint32_t w1 = __builtin_amdgcn_alignbit(x2, x1, bs);
         const uint32_t w2 = __builtin_amdgcn_alignbit(x3, x2, bs);
@@ -522,7 +571,8 @@ __device__ __forceinline__ void qk_wave_i8(const DecodeArgs& a, int seg, int64_t
       zz[s] = t < nt ? fmaf(sK * cA, zf, mK * cB) : -INFINITY;   // rows past the chunk: no weight
       __builtin_amdgcn_sched_barrier(0);   // one set's temporaries live at a time
     }
-    *reinterpret_cast<float4*>(st.z(B) + kg * kTile + 4 * n) = make_float4(zz[0], zz[1], zz[2], zz[3]);
+    float* zb = zbuf_of<S>(st);
+    *reinterpret_cast<float4*>(zb + kg * kTile + 4 * n) = make_float4(zz[0], zz[1], zz[2], zz[3]);
     // softmax frame of head kg, kFrameMargin above the running maximum; it is
     // raised only when a logit exceeds it (in practice on the first tile)
     const float zmax = fmaxf(fmaxf(zz[0], zz[1]), fmaxf(zz[2], zz[3]));
@@ -532,19 +582,17 @@ __device__ __forceinline__ void qk_wave_i8(const DecodeArgs& a, int seg, int64_t
       for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       frame = fmaxf(frame, m + kFrameMargin * kLog2e);
     }
-    if (n == 0) st.z(B)[4 * kTile + kg] = frame;
+    if (n == 0) zb[4 * kTile + kg] = frame;
     wait_lgkm0();  // logits written
     tile_barrier();
+    issue(Slot<(S + 2) % 3>{}, v + 2);   // wave 1 is done with that V buffer
   };
-  for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 1
-    tile(t0, std::integral_constant<int, 0>{});
-    if (t0 + kTile < ir1) tile(t0 + kTile, std::integral_constant<int, 1>{});
-  }
+  for_tiles(ntiles, step);
 }
 
 template <int L>
 __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0, int64_t r1, int b, int li,
-                        int g, int64_t u, Stage2& st) {
+                        int g, int64_t u, const Stage3& st) {
   constexpr int R = (L == 6) ? 43 : 38;
   const int lane = threadIdx.x & 63;
   _Float16* wbuf = st.w;
@@ -552,8 +600,8 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
   const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
   const int cap = (int)a.cap[seg];            // cap * R < 2^31 (checked by the launcher)
   const int ir0 = (int)r0, ir1 = (int)r1;
-  const uint8_t* vcodes = a.codes[seg] + (plane_k + 1) * cap * R;
   const uint32_t* vmg = a.meta[seg] + (plane_k + 1) * cap;
+  const int ntiles = (ir1 - ir0 + kTile - 1) / kTile;
 
   // Chunk exponent E: w = p * scale_V * 2^E (p <= 1) stays below 2^15, so
   // that the fp16 hi/lo split of w neither overflows nor goes subnormal
@@ -577,33 +625,29 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
     for (int k = 0; k < 3; ++k) acc[s][k] = (f4){0.f, 0.f, 0.f, 0.f};
 
-  // The 3 KB of V bytes (16-row byte-planar tiles) from row t0 on -> buffer
-  // `buf`, and the lane's V meta word -> register, through buffer resources
-  // as in the K wave
-  uint32_t vm_next = 0;
-  const uint32_t lane16 = 16u * (uint32_t)lane;
-  auto issue = [&](int buf, int t0) {
-    const __amdgpu_buffer_rsrc_t rv = plane_rsrc(vcodes + t0 * R, (cap - t0) * R);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_at(st.v(buf), 0), 16, (int)lane16, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_at(st.v(buf), 0), 16, (int)lane16, 0, 1024, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_at(st.v(buf), 0), 16, (int)lane16, 0, 2048, 0);
-    vm_next = __builtin_amdgcn_raw_buffer_load_b32(plane_rsrc(vmg + t0, (cap - t0) * 4), 4 * lane, 0, 0);
+  // the lane's V meta word of tile v -> register slot S (wave 0 loads the
+  // V bytes); past the chunk the range is empty
+  uint32_t vmr[3];
+  auto fetch = [&](auto Sc, int v) {
+    constexpr int S = decltype(Sc)::value;
+    const bool live = v < ntiles;
+    const int t0 = ir0 + kTile * v;
+    vmr[S] = __builtin_amdgcn_raw_buffer_load_b32(
+        plane_rsrc(vmg + (live ? t0 : 0), live ? (cap - t0) * 4 : 0), 4 * lane, 0, 0);
   };
+  fetch(Slot<0>{}, 0);
+  fetch(Slot<1>{}, 1);
 
   const int col = lane & 15;
   const int quad = lane >> 4;
   // the 0x66 bias bytes of 5-level fields, held in a register so that the
   // mask and the bias go into one AND-OR
   const uint32_t bias5 = L == 5 ? bias_register() : 0u;
-  // One tile in staging buffer B (a compile-time constant, so that reads of
-  // buffer B are known not to overlap the loads in flight into 1 - B: the
-  // next tile's loads go out first and the V bytes are read where used).
-  auto tile = [&](int t0, auto Bc) {
-    constexpr int B = decltype(Bc)::value;
-    const int nt = min(kTile, ir1 - t0);
-    wait_vm0();   // this tile's V has landed
-    const uint32_t vm = vm_next;
-    if (t0 + kTile < ir1) issue(1 - B, t0 + kTile);
+  auto step = [&](auto Sc, int v) {
+    constexpr int S = decltype(Sc)::value;
+    const int nt = min(kTile, ir1 - ir0 - kTile * v);
+    fetch(Slot<(S + 2) % 3>{}, v + 2);
+    const uint32_t vm = vmr[S];
     // E from the first tile; lowered when a tile holds a scale it cannot
     // take (then the accumulators are rescaled with the frame below)
     const uint32_t sbits = vm & 0xFFFFu;                 // non-negative fp16: ordered as integers
@@ -617,11 +661,12 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
       const int e = 15 - E;                              // scales must stay below 2^e
       slim = e >= 16 ? 0x7C00u : e >= -14 ? (uint32_t)(e + 15) << 10 : e >= -24 ? 1u << (e + 24) : 1u;
     }
-    tile_barrier();                                      // logits of this tile are in LDS
+    tile_barrier();                                      // logits and V bytes of this tile are in LDS
+    const float* zb = zbuf_of<S>(st);
     float z[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) z[h] = st.z(B)[h * kTile + lane];
-    const float4 fr = *reinterpret_cast<const float4*>(st.z(B) + 4 * kTile);   // all lanes alike
+    for (int h = 0; h < 4; ++h) z[h] = zb[h * kTile + lane];
+    const float4 fr = *reinterpret_cast<const float4*>(zb + 4 * kTile);   // all lanes alike
 
     // the weights are taken against the frame of wave 0; when it was raised
     // (in practice only on the first tile) what was accumulated is rescaled
@@ -658,13 +703,13 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
     wait_lgkm0();  // weights visible to the wave
 
     // PV: 32 tokens per MFMA
-    const uint8_t* vbuf = st.v(B);
+    const uint8_t* vbuf = vbuf_of<S>(st);
 #pragma unroll
     for (int G = 0; G < 2; ++G) {
       if (32 * G >= nt) break;
       // A rows 0-3: w_hi of the 4 heads, rows 4-7: w_lo; rows 8-15 repeat
       // them and only feed C rows 8-15, which are never read.
-      const h8 aw = lds_read_h8_wait(wbuf + (col & 7) * kTile + 32 * G + 8 * quad);
+      const h8 aw = *reinterpret_cast<const h8*>(wbuf + (col & 7) * kTile + 32 * G + 8 * quad);
       const int tok0 = 32 * G + 8 * quad;
       const int vo = (tok0 >> 4) * (16 * R) + (tok0 & 15);
 #pragma unroll
@@ -704,27 +749,23 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int seg, int64_t r0
       }
     }
   };
-  if (ir0 < ir1) issue(0, ir0);
-  for (int t0 = ir0; t0 < ir1; t0 += 2 * kTile) {   // same tile sequence as wave 0
-    tile(t0, std::integral_constant<int, 0>{});
-    if (t0 + kTile < ir1) tile(t0 + kTile, std::integral_constant<int, 1>{});
-  }
+  for_tiles(ntiles, step);   // the tile sequence of wave 0
   write_partial<L>(a, u, lane, E, acc, mref, lsum, msum, kLn2);
 }
 
 template <bool kRot>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_mfma2_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t k0[kBuf], k1[kBuf], v0[kBuf], v1[kBuf];
-  __shared__ __attribute__((aligned(16))) float z0[4 * kTile + 4], z1[4 * kTile + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t v0[kBuf], v1[kBuf], v2[kBuf];
+  __shared__ __attribute__((aligned(16))) float z0[4 * kTile + 4], z1[4 * kTile + 4], z2[4 * kTile + 4];
   __shared__ __attribute__((aligned(16))) _Float16 w[2 * 4 * kTile];
   __shared__ __attribute__((aligned(16))) QPrep qp;
-  Stage2 st;
-  st.k0 = k0;
-  st.k1 = k1;
+  Stage3 st;
   st.v0 = v0;
   st.v1 = v1;
+  st.v2 = v2;
   st.z0 = z0;
   st.z1 = z1;
+  st.z2 = z2;
   st.w = w;
 
   const int x = blockIdx.x;
