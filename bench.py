@@ -80,6 +80,10 @@ def main():
                     help="layers of the bounded oracle sample")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the generation, per-layer graph and copy legs")
+    ap.add_argument("--no-cliff", action="store_true",
+                    help="skip the cliff-grid sweep (20 level settings, batch 4 x 32,768)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the mistral7b_128k (131,072-token) leg")
     ap.add_argument("--gen-steps", type=int, default=None,
                     help="generated tokens per sequence in the generation leg "
                          "(default: the gen_16x8k workload's)")
@@ -276,6 +280,17 @@ def main():
         log(f"generation: decode {g['decode_us_per_step']} us/step, "
             f"{g['decode_tokens/s']} tok/s; block quantize {g['block_quantize_us']} us")
         K = V = None
+        torch.cuda.empty_cache()
+        if not args.no_long:
+            m = strip_private(workload_leg(sk, W, torch, dev, stream, "mistral7b_128k"))
+            result["mistral7b_128k"] = m
+            log(f"mistral7b_128k: quantize {m['quantize_ms']} ms ({m['quantize_pct_hbm_peak']}%), "
+                f"decode partials {m['partials_us']} us ({m['partials_pct_hbm_peak']}%)")
+            torch.cuda.empty_cache()
+            torch.cuda.empty_cache()
+        if not args.no_cliff:
+            result["cliff_4x32k"] = cliff_leg(sk, W, torch, dev, stream)
+            torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline and not args.rotate and not args.keynorm_score:
         import cpu_baseline
@@ -297,10 +312,12 @@ def main():
         result["cpu_baseline"] = {
             "value": round(step_bytes / cpu_step_s / 1e9, 4),
             "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "cores_available": cpu_baseline.available_cores(),
             "cpu_model": cpu_baseline.cpu_model(),
             "sample": (f"oracle rank of 1 sequence, quantize+pack of {ls} of {layers} layers "
-                       f"(sequence 0) and one decode step over those layers, in {workers} worker "
-                       f"processes; measured rank {t_rank:.2f}s, quantize {tq:.2f}s, decode "
+                       f"(sequence 0) and one decode step over those layers, in {workers} "
+                       f"single-threaded worker processes ({cpu_baseline.available_cores()} cores "
+                       f"available); measured rank {t_rank:.2f}s, quantize {tq:.2f}s, decode "
                        f"{td:.2f}s, scaled to {B} sequence(s) x {layers} layers x {D} decode "
                        f"steps = {cpu_step_s:.1f}s per step"),
         }
@@ -411,6 +428,167 @@ def copy_leg(torch, stream, mib=2048):
     return {"kind": "torch device copy, best of 5", "bytes_moved": 2 * n * 4,
             "ms": round(best, 4), "GB/s": round(gbs, 1),
             "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
+
+
+def workload_leg(sk, W, torch, dev, stream, name, levels=None, r=None, inputs=None,
+                 quant_reps=5, every=8):
+    """One prompt workload outside the headline step: rank + quantize-pack
+    (median of `quant_reps` timed repetitions on the same cache), then the
+    workload's decode steps (partials + merge over all layers, fresh queries
+    each step), timed like the headline: every `every`-th partials launch and
+    the whole loop.  `levels`/`r` override the workload's; `inputs` reuses
+    (K, V, scores) already on the device."""
+    import numpy as np
+    w = W.WORKLOADS[name]
+    Lh, Ll = levels if levels is not None else (w.L_high, w.L_low)
+    r = w.r if r is None else r
+    B, n, layers, kv, Hq, D = w.batch, w.n, w.layers, w.kv_heads, w.q_heads, w.decode_steps
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        if inputs is None:
+            K, V, _ = W.make_kv_torch(w, dev)
+            scores = W.attention_mass_torch(K, w, dev)
+        else:
+            K, V, scores = inputs
+        q = W.make_q_torch(w, D, dev)
+        k = sk.semkv_topr_count(n, r)
+        cache = sk.SemKVCache(B, layers, kv, Hq, Lh, Ll, cap16(k), cap16(n - k), block=w.block,
+                              max_tokens=n)
+        perm = torch.empty((B, n), dtype=torch.int32, device=dev)
+        out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device=dev)
+    stream.synchronize()
+    Rh, Rl = sk.semkv_row_bytes(Lh), sk.semkv_row_bytes(Ll)
+    planes = B * layers * kv * 2
+    quant_bytes = planes * (k * (256 + Rh + 4) + (n - k) * (Rl + 4 + 256)) + B * n * 8
+    kv_packed = planes * (k * (Rh + 4) + (n - k) * (Rl + 4))
+    partial_bytes = kv_packed + B * layers * Hq * 128 * 2
+    decode_bytes = partial_bytes + B * layers * Hq * 128 * 4
+    sk.semkv_rank_topr(scores, k, perm, stream=stream)
+    qt = []
+    for rep in range(quant_reps + 1):
+        cache.reset()
+        a, b = Ev(), Ev()
+        a.record(stream)
+        sk.semkv_quantize_pack(cache, K, V, perm, k, stream=stream)
+        b.record(stream)
+        qt.append((a, b))
+    ev_p = [(Ev(), Ev()) for _ in range(0, D, every)]
+    m_ev = Ev()
+    start, end = Ev(), Ev()
+    for j in range(min(D, 8)):                       # warm-up launches
+        sk.semkv_decode_partials(cache, q[j], stream=stream)
+    start.record(stream)
+    for j in range(D):
+        if j % every == 0:
+            ev_p[j // every][0].record(stream)
+        sk.semkv_decode_partials(cache, q[j], stream=stream)
+        if j % every == 0:
+            ev_p[j // every][1].record(stream)
+        sk.semkv_decode_merge(cache, out, stream=stream)
+        if (j + 1) % every == 0:
+            m_ev.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    sk.semkv_sync_check(stream)
+    ms_q = float(np.median([a.elapsed_time(b) for a, b in qt[1:]]))
+    us_p = 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev_p]))
+    us_step = 1e3 * start.elapsed_time(end) / D
+    qg = quant_bytes / (ms_q * 1e-3) / 1e9
+    pg = partial_bytes / (us_p * 1e-6) / 1e9
+    dg = decode_bytes / (us_step * 1e-6) / 1e9
+    res = {"workload": name, "batch": B, "tokens": n, "layers": layers, "r": r, "levels": [Lh, Ll],
+           "v_dist": w.v_dist, "decode_steps": D,
+           "quantize_ms": round(ms_q, 4), "quantize_GB/s": round(qg, 1),
+           "quantize_pct_hbm_peak": round(100 * qg / HBM_PEAK_GBS, 2),
+           "quantize_algorithmic_bytes": quant_bytes,
+           "partials_us": round(us_p, 2), "partials_GB/s": round(pg, 1),
+           "partials_pct_hbm_peak": round(100 * pg / HBM_PEAK_GBS, 2),
+           "partials_algorithmic_bytes": partial_bytes,
+           "decode_us_per_step": round(us_step, 2), "decode_tokens/s": round(B / (us_step * 1e-6), 1),
+           "decode_GB/s": round(dg, 1), "decode_pct_hbm_peak": round(100 * dg / HBM_PEAK_GBS, 2)}
+    res["_cache"] = cache
+    res["_q"] = q
+    res["_out"] = out
+    res["_perm"] = perm
+    return res
+
+
+def cliff_leg(sk, W, torch, dev, stream):
+    """Cliff-grid sweep (batch 4 x 32,768 tokens, 8B shape): uniform levels
+    L in {4, 5, 6, 8, 16} (one pool) and the adjacent pairs (5,4), (6,5),
+    (8,6) at r in {.1, .25, .5, .75, .9}.  Each setting: quantize-pack and 64
+    decode steps (rates as in the headline), and the quality proxies:
+    nominal and stored bits per value, reconstruction MSE of K and of V over
+    layers 0 and 31 (rows reconstructed by semkv_dequantize_rows), and the
+    largest |out - ref| / max(1, |ref|) of the last decode step against fp32
+    attention over the fp16 cache (sequence 0, layers 0 and 31)."""
+    import math
+    w = W.WORKLOADS["cliff_4x32k"]
+    B, n, layers, kv, Hq = w.batch, w.n, w.layers, w.kv_heads, w.q_heads
+    with torch.cuda.stream(stream):
+        K, V, _ = W.make_kv_torch(w, dev)
+        scores = W.attention_mass_torch(K, w, dev)
+    stream.synchronize()
+    settings = [(L, L, 0.0) for L in W.CLIFF_UNIFORM]
+    settings += [(Lh, Ll, r) for Lh, Ll in W.CLIFF_PAIRS for r in W.CLIFF_RS]
+    sample_layers = (0, layers - 1)
+    rows = []
+    for Lh, Ll, r in settings:
+        leg = workload_leg(sk, W, torch, dev, stream, "cliff_4x32k", levels=(Lh, Ll), r=r,
+                           inputs=(K, V, scores), quant_reps=3)
+        cache, q, out = leg["_cache"], leg["_q"], leg["_out"]
+        k = sk.semkv_topr_count(n, r)
+        Rh, Rl = sk.semkv_row_bytes(Lh), sk.semkv_row_bytes(Ll)
+        nominal = (k * math.log2(Lh) + (n - k) * math.log2(Ll)) / n
+        stored = (k * (Rh + 4) + (n - k) * (Rl + 4)) * 8.0 / (128 * n)
+        se = {0: 0.0, 1: 0.0}
+        cnt = 0
+        with torch.cuda.stream(stream):
+            for layer in sample_layers:
+                for high, nrows in ((True, cache.n_high), (False, cache.n_low)):
+                    if nrows == 0:
+                        continue
+                    xh = torch.empty((B, kv, 2, nrows, 128), dtype=torch.float32, device=dev)
+                    sk.semkv_dequantize_rows(cache, high, layer, 0, nrows, xh, stream=stream)
+                    tok = cache.tok_view(high)[:, :nrows].long()              # [B][nrows]
+                    idx = tok[:, None, :, None].expand(B, kv, nrows, 128)
+                    for sel, X in ((0, K), (1, V)):
+                        x = torch.gather(X[:, layer].float(), 2, idx)
+                        se[sel] += float(((xh[:, :, sel] - x) ** 2).sum())
+                    cnt += B * kv * nrows * 128
+            # fp32 attention over the fp16 cache for the last decode step
+            worst = 0.0
+            qd = q[w.decode_steps - 1]
+            for layer in sample_layers:
+                kk = K[0, layer].float()                                       # [kv][n][128]
+                vv = V[0, layer].float()
+                qq = qd[0, layer].float().view(kv, Hq // kv, 128)
+                z = torch.bmm(qq, kk.transpose(1, 2).contiguous()) * w.sm_scale
+                ref = torch.bmm(torch.softmax(z, dim=-1), vv).reshape(Hq, 128)
+                err = (out[0, layer] - ref).abs() / ref.abs().clamp(min=1.0)
+                worst = max(worst, float(err.max()))
+        stream.synchronize()
+        row = strip_private(leg)
+        row.update({"nominal_bits": round(nominal, 4), "stored_bits": round(stored, 4),
+                    "compression_vs_fp16": round(16.0 / stored, 3),
+                    "mse_K": se[0] / cnt, "mse_V": se[1] / cnt,
+                    "attn_err_vs_fp16_cache": worst})
+        for key in ("workload", "batch", "tokens", "layers", "v_dist", "decode_steps",
+                    "quantize_algorithmic_bytes", "partials_algorithmic_bytes"):
+            row.pop(key, None)
+        rows.append(row)
+        log(f"cliff ({Lh},{Ll}) r={r}: quantize {row['quantize_pct_hbm_peak']}%, partials "
+            f"{row['partials_pct_hbm_peak']}%, {row['stored_bits']} bits, attn err "
+            f"{worst:.2e}")
+        del cache, q, out, leg
+        torch.cuda.empty_cache()
+    return {"workload": "cliff_4x32k", "batch": B, "tokens": n, "layers": layers,
+            "decode_steps": w.decode_steps, "quality_sample": "sequence 0 (attention), "
+            "all sequences (MSE), layers 0 and 31", "settings": rows}
+
+
+def strip_private(d):
+    return {k: v for k, v in d.items() if not k.startswith("_")}
 
 
 def gen_leg(sk, W, torch, dev, stream, gen_steps=None):

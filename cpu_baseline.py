@@ -51,13 +51,36 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
+def available_cores():
+    """CPU cores this process may run on (its affinity set)."""
+    return len(os.sched_getaffinity(0))
+
+
 def time_oracle(K, V, perm, k, Lh, Ll, q, sm, workers=None):
     """K, V fp16 [layers_s][kv][n][128] (the sample); perm int32 [n]; q fp16
-    [layers_s][Hq][128].  Returns (quantize seconds, decode seconds, workers)."""
-    workers = workers or min(16, len(os.sched_getaffinity(0)))
+    [layers_s][Hq][128].  Returns (quantize seconds, decode seconds, workers).
+
+    One single-threaded worker process per core, at most 16 (one GPU's share
+    of the host), so that `workers` is the number of threads that run."""
+    workers = workers or min(16, available_cores())
     ls, kv = K.shape[0], K.shape[1]
     group = q.shape[1] // kv
+    threads_env = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {v: os.environ.get(v) for v in threads_env}
+    for v in threads_env:
+        os.environ[v] = "1"                        # inherited by the spawned workers
     ctx = mp.get_context("spawn")
+    try:
+        return _time_in_pool(ctx, workers, K, V, perm, k, Lh, Ll, q, sm, ls, kv, group)
+    finally:
+        for v, old in saved.items():
+            if old is None:
+                os.environ.pop(v, None)
+            else:
+                os.environ[v] = old
+
+
+def _time_in_pool(ctx, workers, K, V, perm, k, Lh, Ll, q, sm, ls, kv, group):
     with ctx.Pool(workers) as pool:
         pool.map(math.sqrt, range(workers))          # start the workers before timing
         tasks = [(np.ascontiguousarray(X[l, g]), perm, k, Lh, Ll)

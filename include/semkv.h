@@ -217,6 +217,20 @@ semkv_status semkv_decode_partials(const semkv_cache* c, const uint16_t* q, int3
 semkv_status semkv_decode_merge(const semkv_cache* c, int32_t nlayers, float* out,
                                 void* workspace, int64_t ws_bytes, void* stream);
 
+/* Reconstructed pool rows, for inspection and quality measurement (the
+ * quantizer of SemKV Table 6 undone: x = min + code * scale per value in
+ * fp32; for a rotated cache, SemKV Table 2's rotation, the row is rotated
+ * back by H in fp32).  Decoding never needs this.
+ *  pool   0 = high pool (L_high), 1 = low pool (L_low)
+ *  layer  0 <= layer < layers
+ *  rows   [row0, row0 + nrows) of every (sequence, KV head, K|V) plane of that
+ *         pool and layer; they must be valid (row0 + nrows <= n_high or n_low).
+ *         Slot j of the pool holds token tok_*[b][j] (see semkv_cache).
+ *  out    fp32 [batch][kv_heads][2][nrows][128] device memory, 16-byte aligned
+ * Errors: EINVAL (pool, layer or row range, null or misaligned out). */
+semkv_status semkv_dequantize_rows(const semkv_cache* c, int32_t pool, int32_t layer,
+                                   int64_t row0, int64_t nrows, float* out, void* stream);
+
 /* semkv_decode_attn without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  The split-K partials live in a static device array

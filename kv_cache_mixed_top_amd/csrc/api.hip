@@ -439,6 +439,32 @@ semkv_status semkv_decode_attn_noalloc(const semkv_cache* c, const uint16_t* q, 
 
 int64_t semkv_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
+semkv_status semkv_dequantize_rows(const semkv_cache* c, int32_t pool, int32_t layer,
+                                   int64_t row0, int64_t nrows, float* out, void* stream) {
+  semkv_status st = check_cache(c);
+  if (st != SEMKV_OK) return st;
+  const semkv_geom& g = c->g;
+  if (pool != 0 && pool != 1) return SEMKV_EINVAL;
+  if (layer < 0 || layer >= g.layers) return SEMKV_EINVAL;
+  const int64_t valid = pool == 0 ? c->n_high : c->n_low;
+  if (row0 < 0 || nrows < 0 || row0 + nrows > valid) return SEMKV_EINVAL;
+  if (!out || !aligned(out, 16)) return SEMKV_EINVAL;
+  DequantArgs a;
+  a.codes = pool == 0 ? c->codes_high : c->codes_low;
+  a.meta = reinterpret_cast<const uint32_t*>(pool == 0 ? c->meta_high : c->meta_low);
+  a.cap = pool == 0 ? g.cap_high : g.cap_low;
+  a.fmt = row_fmt(pool == 0 ? g.L_high : g.L_low);
+  a.batch = g.batch;
+  a.layers = g.layers;
+  a.kv_heads = g.kv_heads;
+  a.layer = layer;
+  a.row0 = row0;
+  a.nrows = nrows;
+  a.rotate = g.rotate;
+  a.out = out;
+  return from_hip(launch_dequant(a, (hipStream_t)stream));
+}
+
 semkv_status semkv_sync_check(void* stream) {
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   if (e != hipSuccess) return SEMKV_EHIP;

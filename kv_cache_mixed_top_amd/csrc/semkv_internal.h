@@ -54,6 +54,21 @@ struct AppendArgs {
 };
 hipError_t launch_append_tail(const AppendArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- dequantize
+// Rows [row0, row0 + nrows) of every (sequence, KV head, K|V) plane of one
+// layer of one pool -> fp32 out[b][head][K|V][row - row0][128].
+struct DequantArgs {
+  const uint8_t* codes;
+  const uint32_t* meta;
+  int64_t cap;
+  RowFmt fmt;
+  int32_t batch, layers, kv_heads, layer;
+  int64_t row0, nrows;
+  int32_t rotate;
+  float* out;
+};
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
+
 // ---------------------------------------------------------------- decode
 struct DecodeArgs {
   const uint8_t* codes[2];

@@ -62,6 +62,8 @@ _SIGS = {
     "semkv_decode_attn_noalloc": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_i32, c_i32, c_f32,
                                           c_p, c_p]),
     "semkv_decode_noalloc_scratch_bytes": (c_i64, []),
+    "semkv_dequantize_rows": (c_i32, [ctypes.POINTER(semkv_cache), c_i32, c_i32, c_i64, c_i64,
+                                      c_p, c_p]),
     "semkv_sync_check": (c_i32, [c_p]),
     "semkv_status_str": (ctypes.c_char_p, [c_i32]),
 }
@@ -276,6 +278,20 @@ def semkv_decode_merge(cache: "SemKVCache", out, workspace=None, stream=None):
     _check("semkv_decode_merge",
            _lib.semkv_decode_merge(ctypes.byref(cache.c), out.shape[1], _ptr(out), _ptr(ws),
                                    _nbytes(ws), _stream(stream)))
+
+
+def semkv_dequantize_rows(cache: "SemKVCache", high: bool, layer, row0, nrows, out,
+                          stream=None):
+    """out fp32 [batch][kv_heads][2][nrows][128]: rows row0 .. row0+nrows-1 of one
+    layer of the high (or low) pool, reconstructed."""
+    g = cache.geom
+    if (out.dtype != torch.float32 or tuple(out.shape) != (g.batch, g.kv_heads, 2, nrows, 128)
+            or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous fp32 [batch][kv_heads][2][nrows][128] tensor")
+    _on_device(out)
+    _check("semkv_dequantize_rows",
+           _lib.semkv_dequantize_rows(ctypes.byref(cache.c), 0 if high else 1, layer, row0, nrows,
+                                      _ptr(out), _stream(stream)))
 
 
 def semkv_sync_check(stream=None):
