@@ -419,9 +419,10 @@ def test_checkpoint_roundtrip():
 
 
 # ------------------------------------------------------------------ matrix-core decode path
-# (6,5) and uniform 6- or 5-level pools with 4 query heads per KV head take
-# the MFMA kernel; these cases cover several 64-row tiles per chunk, ragged
-# last tiles, empty pools, constant / tiny / wide rows and heavy-tailed V.
+# Pools of 4, 5, 6 and 16 levels (any pair with L_high >= L_low) with 4 query
+# heads per KV head take the MFMA kernel; these cases cover several 64-row
+# tiles per chunk, ragged last tiles, empty pools, constant / tiny / wide rows
+# and heavy-tailed V.
 
 @pytest.mark.parametrize("n,r,kind", [
     (1, 0.5, "normal"), (63, 0.5, "normal"), (64, 0.25, "normal"), (65, 0.75, "normal"),
@@ -451,7 +452,7 @@ def test_decode_mfma_shapes(n, r, kind):
                                f"mfma n={n} r={r} {kind} sm={sm}")
 
 
-@pytest.mark.parametrize("L", [5, 6])
+@pytest.mark.parametrize("L", [4, 5, 6, 16])
 def test_decode_mfma_uniform_levels(L):
     _print("decode mfma uniform", L)
     rng = np.random.default_rng(L)
@@ -482,3 +483,29 @@ def test_decode_mfma_large_logits():
     sk.semkv_decode_attn(cache, to_dev(q), out, sm_scale=0.5)
     sk.semkv_sync_check()
     assert_attention_close(out.cpu().numpy(), O.decode_attention(q, op, 0.5), "peaked")
+
+
+@pytest.mark.parametrize("Lh,Ll", [(5, 4), (6, 4), (6, 6), (5, 5), (16, 16), (16, 6), (16, 5), (16, 4)])
+@pytest.mark.parametrize("kind", ["normal", "mixed", "studentt"])
+def test_decode_mfma_level_pairs(Lh, Ll, kind):
+    """Every level pair of the matrix-core kernel, on several tiles with a
+    ragged last one, peaked and heavy-tailed values."""
+    _print("decode mfma pair", Lh, Ll, kind)
+    rng = np.random.default_rng(Lh * 31 + Ll)
+    B, layers, kv, Hq, n = 1, 2, 2, 8, 1333
+    if kind == "studentt":
+        K, _ = _kv(rng, B, layers, kv, n)
+        z = rng.standard_normal((B, layers, kv, n, 128))
+        chi = (rng.standard_normal((B, layers, kv, n, 128, 4)) ** 2).sum(-1)
+        V = (z / np.sqrt(chi / 4)).astype(np.float16)
+    else:
+        K, V = _kv(rng, B, layers, kv, n, kind)
+    s = rng.random((B, n)).astype(np.float32)
+    cache, op = _quantize_case(K, V, s, 0.4, Lh, Ll, f"pair ({Lh},{Ll}) {kind}")
+    for sm in (1.0, 1 / math.sqrt(128)):
+        q = (rng.standard_normal((B, layers, Hq, 128)) / math.sqrt(128)).astype(np.float16)
+        out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
+        sk.semkv_decode_attn(cache, to_dev(q), out, sm_scale=sm)
+        sk.semkv_sync_check()
+        assert_attention_close(out.cpu().numpy(), O.decode_attention(q, op, sm),
+                               f"pair ({Lh},{Ll}) {kind} sm={sm}")
