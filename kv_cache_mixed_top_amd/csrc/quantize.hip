@@ -8,13 +8,14 @@
 // q of a row loads the 16-byte pieces at byte offsets 16q + 64i (i = 0..3),
 // so each load instruction of a quad covers 64 contiguous bytes.
 //
-// Codes: c = round-half-even((x - m) / s).  The fast path (6- and 5-level
-// pools) evaluates y = (x - m)/s + 10 as one fp32 FMA with fl(1/s) and
-// converts it to a byte; a group of 8 values with one near a half-integer
-// (within the bound of that evaluation's error) is re-read and settled
-// exactly in double with the residuals x - m - (c0 +/- 1/2) s.  The generic
-// path (any level count) evaluates y = (x - m) * fl(1/s) and settles each
-// value near a half-integer the same way.
+// Codes: c = round-half-even((x - m) / s).  The fast path (pools of 3, 4, 5,
+// 6, 8 and 16 levels) evaluates y = (x - m)/s + D (D a small even integer)
+// as one fp32 FMA with fl(1/s) and converts it to a byte; a group of 8 values
+// with one near a half-integer (within the bound of that evaluation's error)
+// is re-read and settled exactly in double with the residuals
+// x - m - (c0 +/- 1/2) s.  The generic path (any level count) evaluates
+// y = (x - m) * fl(1/s) and settles each value near a half-integer the same
+// way.
 //
 // Packing: codes go to LDS; each output byte is assembled from the fields
 // that overlap it.  K planes hold rows back to back; V planes are byte-planar
@@ -273,13 +274,22 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, int pool, int 
   }
 }
 
-// ---- fast path for the 6- and 5-level pools when the tile's first slot is
-// a multiple of 16 (every tile of a prompt): the tile's packed bytes form one
-// contiguous, 16-byte aligned range of the plane in both layouts, which is
-// assembled in LDS and stored with 16-byte writes.
+// ---- fast path for pools of 3, 4, 5, 6, 8 and 16 levels when the tile's
+// first slot is a multiple of 16 (every tile of a prompt): the tile's packed
+// bytes form one contiguous, 16-byte aligned range of the plane in both
+// layouts, which is assembled in LDS and stored with 16-byte writes.
 constexpr int kCode8Stride = 136;                 // u8 codes per LDS row: 128 + 8 zero pad
 constexpr int kCode8Bytes = kRows * kCode8Stride + 16;
-constexpr int kImgBytes = kRows * 43;             // largest packed tile (6 levels)
+constexpr int kImgBytes = kRows * 64;             // largest packed tile (16 levels)
+
+// packed row bytes of the level counts with a fast path (the row format of
+// semkv_common.h: ceil(128 / g) fields of b bits)
+template <int L> constexpr int fast_row_bytes() {
+  return L == 3 ? 26 : L == 4 ? 32 : L == 5 ? 38 : L == 6 ? 43 : L == 8 ? 48 : 64;
+}
+__host__ __device__ constexpr bool fast_quant_level(int L) {
+  return L == 3 || L == 4 || L == 5 || L == 6 || L == 8 || L == 16;
+}
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -309,7 +319,7 @@ __device__ __forceinline__ uint16_t scale_ceil_fast(float lo, float hi) {
 template <int L, bool kRot>
 __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_pool,
                                    uint8_t* codes8, uint8_t* img) {
-  constexpr int R = L == 6 ? 43 : 38;
+  constexpr int R = fast_row_bytes<L>();
   const int count = pool == 0 ? a.k_high : a.n - a.k_high;
   const int perm_off = pool == 0 ? 0 : a.k_high;
   const int y = blockIdx.y;
@@ -405,35 +415,41 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
   // from round((x - m) r) with x - m rounded once in fp32 (code error
   // <= 2^-22 (L-1)), which is within 1 of the exact code whatever |m|/s.
   //
-  // The fast pass computes y + 10 instead, which lies in [8, 16) where the
-  // fraction is the low 20 mantissa bits: the distance of the fraction from
-  // 1/2 is then one shift-and-add of the bits and an unsigned minimum, and
-  // the packed bytes are code + 10 (10 is even, so ties round alike).  Its
-  // error bound grows by the two roundings at that magnitude; the window
-  // below is twice the one above plus 2^-20.  The LDS code array keeps
-  // code + 10 (pads and constant rows too); the field sums take the offset
-  // back out in the dot product's accumulator.
+  // The fast pass computes y + D instead (D = 10 up to 6 levels, 18 for 8,
+  // 34 for 16: an even integer that keeps every y + D inside one binade,
+  // [8, 16), [16, 32) or [32, 64)), where the fraction is the low FB = 20,
+  // 19 or 18 mantissa bits: the distance of the fraction from 1/2 is then one
+  // shift-and-add of the bits and an unsigned minimum, and the packed bytes
+  // are code + D (D is even, so ties round alike).  Its error bound grows by
+  // the two roundings at that magnitude; the window below is twice the one
+  // above plus 2^-FB.  The LDS code array keeps code + D (pads and constant
+  // rows too); the field sums take the offset back out in the dot product's
+  // accumulator.
   // A constant row (s = 0; also the rows past the tile's end, read as
-  // zeros) is coded with scale 1: every value equals m, so y = 10 exactly
+  // zeros) is coded with scale 1: every value equals m, so y = D exactly
   // and every code is 0, with no branch.
-  constexpr uint32_t kTen = 0x0A0A0A0Au;
+  constexpr int kD = L <= 6 ? 10 : L == 8 ? 18 : 34;
+  constexpr int kFB = L <= 6 ? 20 : L == 8 ? 19 : 18;
+  constexpr int kSh = 32 - kFB;
+  constexpr uint32_t kZeroCode = 0x01010101u * (uint32_t)kD;   // code 0 in four code bytes
   const float sq = s > 0.0f ? s : 1.0f;
   uint32_t cw[8];
   const float rs = __builtin_amdgcn_rcpf(sq);
   const float eps = kRot ? 0x1p-22f * (1.5f * (float)(L - 1) + 1.25f * fabsf(lo) * rs) + 0x1p-30f
                          : 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
   const float rsk = kRot ? rs * kRotScale : rs;
-  const float nb10 = fmaf(-lo, rs, 10.0f);
-  const float win = (2.0f * eps + 0x1p-20f) * 1048576.0f;      // in units of 2^-20
-  const bool wide = !(win < 131072.0f);                         // then every code is settled
-  const uint32_t E = wide ? 131072u : (uint32_t)win + 1u;
-  const uint32_t bias = (E - 0x80000u) << 12;   // (frac - 1/2 + E) mod 2^20, in the top bits
-  const uint32_t thr = (2u * E) << 12;
+  const float nb10 = fmaf(-lo, rs, (float)kD);
+  constexpr float kUnit = (float)(1u << kFB);
+  const float win = (2.0f * eps + 1.0f / kUnit) * kUnit;        // in units of 2^-FB
+  const bool wide = !(win < kUnit / 8.0f);                      // then every code is settled
+  const uint32_t E = wide ? (1u << (kFB - 3)) : (uint32_t)win + 1u;
+  const uint32_t bias = (E - (1u << (kFB - 1))) << kSh;   // (frac - 1/2 + E) mod 2^FB, in the top bits
+  const uint32_t thr = (2u * E) << kSh;
   uint32_t umin[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};   // per 8 values
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const float y = fmaf(kRot ? yr[k & (kRot ? 31 : 0)] : (float)v[k >> 1][k & 1], rsk, nb10);
-    umin[k >> 3] = min(umin[k >> 3], (__builtin_bit_cast(uint32_t, y) << 12) + bias);
+    umin[k >> 3] = min(umin[k >> 3], (__builtin_bit_cast(uint32_t, y) << kSh) + bias);
     cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(y, k & 3, (k & 3) ? cw[k >> 2] : 0u);
   }
   // dims 8q + 32i .. +8 -> row r of the LDS code array; lane 0 of the quad
@@ -454,10 +470,10 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
       for (int e = 0; e < 8; ++e) {
         const float u = yr[(8 * i + e) & (kRot ? 31 : 0)];
         const float y = fmaf(u, rsk, nb10);
-        if (wide || (__builtin_bit_cast(uint32_t, y) << 12) + bias <= thr) {
+        if (wide || (__builtin_bit_cast(uint32_t, y) << kSh) + bias <= thr) {
           const float x = u * kRotScale;
           const float c = exact_code(x, lo, sq, rintf((x - lo) * rs));
-          crow[8 * q + 32 * i + e] = (uint8_t)((int)c + 10);
+          crow[8 * q + 32 * i + e] = (uint8_t)((int)c + kD);
         }
       }
     }
@@ -475,15 +491,15 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
       for (int e = 0; e < 8; ++e) {
         const float x = h2f((uint16_t)(ws[e >> 1] >> (16 * (e & 1))));
         const float y = fmaf(x, rs, nb10);
-        if (wide || (__builtin_bit_cast(uint32_t, y) << 12) + bias <= thr) {
+        if (wide || (__builtin_bit_cast(uint32_t, y) << kSh) + bias <= thr) {
           const float c = exact_code(x, lo, sq, rintf((x - lo) * rs));
-          crow[8 * q + 32 * i + e] = (uint8_t)((int)c + 10);
+          crow[8 * q + 32 * i + e] = (uint8_t)((int)c + kD);
         }
       }
     }
   }
-  if (q == 0) *reinterpret_cast<uint2*>(crow + 128) = make_uint2(kTen, kTen);
-  if (tid < 4) reinterpret_cast<uint32_t*>(codes8 + kRows * kCode8Stride)[tid] = kTen;
+  if (q == 0) *reinterpret_cast<uint2*>(crow + 128) = make_uint2(kZeroCode, kZeroCode);
+  if (tid < 4) reinterpret_cast<uint32_t*>(codes8 + kRows * kCode8Stride)[tid] = kZeroCode;
 
   if (valid && q == 0) {
     const int64_t slot = slot0 + r;
@@ -493,10 +509,10 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
   }
   __syncthreads();
 
-  // ---- fields (sum_i code[3j+i] L^i, one udot4 each) -> the tile's byte
-  // image: K rows back to back, V byte-planar in 16-row tiles.  The layout
-  // is uniform per workgroup, so each is its own code path: byte j of this
-  // thread's row lands at rowimg + j * kStep.
+  // ---- fields (sum_i code[g j + i] L^i, udot4 over the code bytes) -> the
+  // tile's byte image: K rows back to back, V byte-planar in 16-row tiles.
+  // The layout is uniform per workgroup, so each is its own code path: byte
+  // j of this thread's row lands at rowimg + j * kStep.
   auto pack = [&](auto planar_c) {
     constexpr bool kPlanar = decltype(planar_c)::value;
     constexpr int kStep = kPlanar ? 16 : 1;
@@ -504,7 +520,7 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
     const uint8_t* crow8 = codes8 + r * kCode8Stride;
     if (L == 6) {
       constexpr uint32_t W = 0x00240601u;              // bytes {1, 6, 36, 0}
-      constexpr uint32_t Z = 0u - 10u * 43u;           // removes the +10 of three codes
+      constexpr uint32_t Z = 0u - (uint32_t)kD * 43u;  // removes the +D of three codes
 #pragma unroll
       for (int u = q; u < 11; u += 4) {                // fields 4u .. 4u+3 of this thread's row
         const uint32_t* c = reinterpret_cast<const uint32_t*>(crow8 + 12 * u);
@@ -515,9 +531,49 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
         o[2 * kStep] = (uint8_t)__builtin_amdgcn_udot4(__builtin_amdgcn_alignbyte(c2, c1, 2), W, Z, false);
         if (u < 10) o[3 * kStep] = (uint8_t)__builtin_amdgcn_udot4(c2 >> 8, W, Z, false);
       }
+    } else if (L == 4) {
+      constexpr uint32_t W = 0x40100401u;              // bytes {1, 4, 16, 64}
+      constexpr uint32_t Z = 0u - (uint32_t)kD * 85u;
+      const uint32_t* c = reinterpret_cast<const uint32_t*>(crow8);
+#pragma unroll
+      for (int u = q; u < 32; u += 4)                  // byte u = codes 4u .. 4u+3
+        rowimg[u * kStep] = (uint8_t)__builtin_amdgcn_udot4(c[u], W, Z, false);
+    } else if (L == 16) {
+      constexpr uint32_t W = 0x00001001u;              // bytes {1, 16, 0, 0}
+      constexpr uint32_t Z = 0u - (uint32_t)kD * 17u;
+      const uint32_t* c = reinterpret_cast<const uint32_t*>(crow8);
+#pragma unroll
+      for (int u = q; u < 32; u += 4) {                // bytes 2u, 2u+1 = codes 4u .. 4u+3
+        rowimg[2 * u * kStep] = (uint8_t)__builtin_amdgcn_udot4(c[u], W, Z, false);
+        rowimg[(2 * u + 1) * kStep] = (uint8_t)__builtin_amdgcn_udot4(c[u] >> 16, W, Z, false);
+      }
+    } else if (L == 3) {
+      constexpr uint32_t W = 0x1B090301u;              // bytes {1, 3, 9, 27}
+      constexpr uint32_t Z = 0u - (uint32_t)kD * 121u; // the +D of five codes (81 D below)
+      const uint32_t* c = reinterpret_cast<const uint32_t*>(crow8);
+#pragma unroll
+      for (int u = q; u < 26; u += 4) {                // field u = codes 5u .. 5u+4
+        const int o = 5 * u;
+        const uint32_t d0 = c[o >> 2], d1 = c[(o >> 2) + 1], d2 = c[(o >> 2) + 2];
+        const uint32_t x = __builtin_amdgcn_alignbyte(d1, d0, o & 3);
+        const uint32_t y = __builtin_amdgcn_alignbyte(d2, d1, o & 3) & 0xFFu;
+        rowimg[u * kStep] = (uint8_t)__builtin_amdgcn_udot4(x, W, Z + 81u * y, false);
+      }
+    } else if (L == 8) {
+      constexpr uint32_t W = 0x00400801u;              // bytes {1, 8, 64, 0}
+      const uint32_t* c = reinterpret_cast<const uint32_t*>(crow8);
+#pragma unroll
+      for (int u = q; u < 16; u += 4) {                // codes 8u .. 8u+7 -> bytes 3u .. 3u+2
+        const uint32_t x0 = c[2 * u] - kZeroCode, x1 = c[2 * u + 1] - kZeroCode;   // bytes >= D: no borrow
+        const uint32_t v = __builtin_amdgcn_udot4(x0, W, 0u, false) | ((x0 >> 24) << 9) |
+                           (__builtin_amdgcn_udot4(x1, W, 0u, false) << 12) | ((x1 >> 24) << 21);
+        rowimg[3 * u * kStep] = (uint8_t)v;
+        rowimg[(3 * u + 1) * kStep] = (uint8_t)(v >> 8);
+        rowimg[(3 * u + 2) * kStep] = (uint8_t)(v >> 16);
+      }
     } else {
       constexpr uint32_t W = 0x00190501u;              // bytes {1, 5, 25, 0}
-      constexpr uint32_t Z = 0u - 10u * 31u;           // removes the +10 of three codes
+      constexpr uint32_t Z = 0u - (uint32_t)kD * 31u;  // removes the +D of three codes
 #pragma unroll
       for (int u = q; u < 6; u += 4) {                 // fields 8u .. 8u+7 = bytes 7u .. 7u+6
         const uint32_t* c = reinterpret_cast<const uint32_t*>(crow8 + 24 * u);
@@ -555,26 +611,34 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
     store_stream(dst + i, reinterpret_cast<const uint4*>(img)[i]);
 }
 
+// One pool's tile: the fast path of its level count (a compile-time count
+// when the kernel is specialised for it, else a runtime switch), or the
+// generic tile.
+template <int LF, bool kRot>
+__device__ __forceinline__ void pool_tile(const QuantArgs& a, int pool, int t, uint8_t* smem) {
+  const bool aligned16 = (a.start[pool] & 15) == 0;
+  const int L = LF ? LF : a.fmt[pool].L;
+  uint8_t* img = smem + kCode8Bytes;
+  if (aligned16 && fast_quant_level(L)) {
+    if (LF == 6 || (LF == 0 && L == 6)) quantize_tile_fast<6, kRot>(a, pool, t, smem, img);
+    else if (LF == 5 || (LF == 0 && L == 5)) quantize_tile_fast<5, kRot>(a, pool, t, smem, img);
+    else if (LF == 0 && L == 4) quantize_tile_fast<4, kRot>(a, pool, t, smem, img);
+    else if (LF == 0 && L == 16) quantize_tile_fast<16, kRot>(a, pool, t, smem, img);
+    else if (LF == 0 && L == 8) quantize_tile_fast<8, kRot>(a, pool, t, smem, img);
+    else if (LF == 0 && L == 3) quantize_tile_fast<3, kRot>(a, pool, t, smem, img);
+  } else {
+    quantize_tile<LF, kRot>(a, pool, t, reinterpret_cast<uint16_t*>(smem));
+  }
+}
+
 template <int LH, int LL, bool kRot = false>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, int tiles_high) {
   constexpr int kGeneric = kRows * kCodeStride * 2;
   constexpr int kFast = kCode8Bytes + kImgBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGeneric > kFast ? kGeneric : kFast];
   const int tile = blockIdx.x;
-  const int pool = tile < tiles_high ? 0 : 1;
-  const int t = pool == 0 ? tile : tile - tiles_high;
-  const bool aligned16 = (a.start[pool] & 15) == 0;
-  if (pool == 0) {
-    if (LH != 0 && aligned16)
-      quantize_tile_fast<LH == 0 ? 6 : LH, kRot>(a, 0, t, smem, smem + kCode8Bytes);
-    else
-      quantize_tile<LH, kRot>(a, 0, t, reinterpret_cast<uint16_t*>(smem));
-  } else {
-    if (LL != 0 && aligned16)
-      quantize_tile_fast<LL == 0 ? 5 : LL, kRot>(a, 1, t, smem, smem + kCode8Bytes);
-    else
-      quantize_tile<LL, kRot>(a, 1, t, reinterpret_cast<uint16_t*>(smem));
-  }
+  if (tile < tiles_high) pool_tile<LH, kRot>(a, 0, tile, smem);
+  else pool_tile<LL, kRot>(a, 1, tile - tiles_high, smem);
 }
 
 }  // namespace
