@@ -579,6 +579,60 @@ class GenerationCache:
 
 
 # --------------------------------------------------------------------------
+# Ragged batches (SemKV Fig. 6: each prompt is ranked and quantized on its
+# own and each sequence's generation blocks fill at their own pace; SemKV
+# Table 2: multi-turn use, with the residual block quantized at every turn's
+# end).  Reading: the sequences of a batch share nothing but the buffers, so
+# a ragged batch is its sequences taken one at a time -- one batch-of-one
+# GenerationCache per sequence, driven by that sequence's own events.
+# --------------------------------------------------------------------------
+
+
+class RaggedGeneration:
+    """Streaming oracle of a batch whose sequences advance independently."""
+
+    def __init__(self, batch, layers, kv_heads, L_high, L_low, r, block=128, rotate=False):
+        self.seqs = [GenerationCache(layers=layers, kv_heads=kv_heads, L_high=L_high,
+                                     L_low=L_low, r=r, block=block, batch=1, rotate=rotate)
+                     for _ in range(batch)]
+
+    def prompt(self, b, K, V, scores):
+        """Prompt of sequence b: K, V [layers][kv][n][128] fp16, scores [n].
+        A prompt starts a turn, so the sequence's tail must be empty."""
+        g = self.seqs[b]
+        if g.n_tail != 0:
+            raise ValueError("a prompt needs an empty tail (flush the previous turn first)")
+        g.prompt(np.asarray(K)[None], np.asarray(V)[None], np.asarray(scores, np.float32)[None])
+
+    def append(self, b, k_new, v_new, score):
+        """One generated token of sequence b: k_new, v_new [layers][kv][128]."""
+        self.seqs[b].append(np.asarray(k_new)[None], np.asarray(v_new)[None],
+                            np.asarray([score], np.float32))
+
+    def flush(self, b):
+        self.seqs[b].flush()
+
+    def counters(self, b):
+        """(n_high, n_low, n_tail, n_tokens) of sequence b."""
+        g = self.seqs[b]
+        p = g.pools
+        nh = 0 if p is None else p.codes_high.shape[4]
+        nl = 0 if p is None else p.codes_low.shape[4]
+        return nh, nl, g.n_tail, g.n_tokens
+
+    def pools(self, b) -> Pools:
+        g = self.seqs[b]
+        return g.pools if g.pools is not None else g._empty_pools()
+
+    def tail_array(self, b):
+        return self.seqs[b].tail_array()[0]
+
+    def decode(self, b, q, sm_scale, layer0=0):
+        """q [nl][Hq][128] of sequence b -> [nl][Hq][128]."""
+        return self.seqs[b].decode(np.asarray(q)[None], sm_scale, layer0=layer0)[0]
+
+
+# --------------------------------------------------------------------------
 # Storage accounting (SemKV Tables 3-6, Fig. 11).
 # --------------------------------------------------------------------------
 
