@@ -48,7 +48,7 @@ typedef int32_t semkv_status;
 enum {
   SEMKV_OK = 0,
   SEMKV_EINVAL = -1,       /* null/misaligned pointer, size or range error */
-  SEMKV_EUNSUPPORTED = -2, /* valid but not supported (head_dim, L, ragged) */
+  SEMKV_EUNSUPPORTED = -2, /* valid but not supported (head_dim, L)          */
   SEMKV_ECAPACITY = -3,    /* a pool has no room for the rows to be written */
   SEMKV_EWORKSPACE = -4,   /* workspace missing or smaller than required    */
   SEMKV_EHIP = -5          /* the HIP runtime reported an error             */
@@ -67,9 +67,10 @@ typedef struct {
                             * normalized Sylvester H_128, applied in fp32 by
                             * index-bit butterflies; the row minimum is rounded
                             * down to fp16).  Decode rotates the queries in fp32
-                            * (carried as an fp16 hi + lo pair on the matrix
-                            * cores) for the pool rows and rotates their share
-                            * of the output back; the fp16 tail of generation
+                            * (the matrix-core kernel then puts them on a
+                            * fixed-point grid of 2^-27 of their largest
+                            * component) for the pool rows and rotates their
+                            * share of the output back; the fp16 tail of generation
                             * is not quantized, hence not rotated, and is read
                             * with the query as given.  Any level pair and
                             * query group; rotated rows must stay within the
@@ -90,7 +91,9 @@ typedef struct {
  *  index 2 of the [..][2] axes: 0 = K, 1 = V.
  *  The counters are HOST-side and shared by every sequence of the batch:
  *  rows [0, n_high) / [0, n_low) of each pool are valid, tail rows
- *  [0, n_tail) are valid, and n_high + n_low + n_tail == n_tokens. */
+ *  [0, n_tail) are valid, and n_high + n_low + n_tail == n_tokens.  A cache
+ *  driven by the semkv_ragged_* calls keeps them at 0 and holds each
+ *  sequence's counters in a device array instead (see below). */
 typedef struct {
   semkv_geom g;
   uint8_t* codes_high;
@@ -246,6 +249,85 @@ semkv_status semkv_dequantize_rows(const semkv_cache* c, int32_t pool, int32_t l
 semkv_status semkv_decode_attn_noalloc(const semkv_cache* c, const uint16_t* q, int32_t layer0,
                                        int32_t nlayers, float sm_scale, float* out, void* stream);
 int64_t semkv_decode_noalloc_scratch_bytes(void);
+
+/* ---- Ragged batches: sequences of one cache advance independently (SemKV
+ * Fig. 6: each prompt is ranked and quantized on its own and each sequence's
+ * generation blocks fill at their own pace; Table 2: multi-turn use with a
+ * flush at every turn's end).  Each sequence b owns SEMKV_SEQ_WORDS int64
+ * counters in a caller-owned DEVICE array seq[batch][SEMKV_SEQ_WORDS]:
+ *   [SEMKV_SEQ_HIGH] n_high  [SEMKV_SEQ_LOW] n_low  [SEMKV_SEQ_TAIL] n_tail
+ *   [SEMKV_SEQ_TOKENS] n_tokens  [SEMKV_SEQ_STATUS] status bits (sticky)
+ * with n_high + n_low + n_tail == n_tokens; rows [0, n_high) / [0, n_low) of
+ * sequence b's pool planes and [0, n_tail) of its tail are valid, tok_* of
+ * its slots hold its own token indices.  The kernels read them as offsets and
+ * advance them in stream order, so ragged calls need no host
+ * synchronisation and may be captured in a HIP graph.  A cache used this way
+ * keeps its host counters at 0 (EINVAL otherwise).  Capacity is checked on
+ * the device: a sequence whose rows would not fit writes nothing and gets
+ * SEMKV_SEQ_CAPACITY in its status (its counters stay as they were); read
+ * the array after semkv_sync_check to see it. */
+#define SEMKV_SEQ_WORDS 8
+enum { SEMKV_SEQ_HIGH = 0, SEMKV_SEQ_LOW = 1, SEMKV_SEQ_TAIL = 2, SEMKV_SEQ_TOKENS = 3,
+       SEMKV_SEQ_STATUS = 4 };
+enum {
+  SEMKV_SEQ_CAPACITY = 1,  /* rows skipped: a pool had no room                */
+  SEMKV_SEQ_TAIL_BUSY = 2, /* prompt skipped: the sequence's tail is not empty */
+  SEMKV_SEQ_TAIL_FULL = 4  /* token dropped: the tail was full (after a
+                            * capacity failure)                               */
+};
+
+/* Zero the counters of `batch` sequences (a fill kernel on `stream`). */
+semkv_status semkv_seq_reset(int64_t* seq, int32_t batch, void* stream);
+
+/* semkv_rank_topr for prompts of different lengths: sequence b ranks the
+ * first n_seq[b] <= n_max scores of its row with k = floor(r n_seq[b] + 1/2).
+ *  n_seq  int32 [batch] device memory
+ *  perm   int32 [batch][n_max]: entries [0, n_seq[b]) of row b are written
+ *  mask   nullable uint32 [batch][ceil(n_max/32)]: words [0, ceil(n_seq[b]/32))
+ * Errors: EINVAL (pointers, sizes, r outside [0, 1]). */
+semkv_status semkv_ragged_rank_topr(const float* scores, int32_t batch, int64_t n_max,
+                                    int64_t ld_scores, const int32_t* n_seq, double r,
+                                    int32_t* perm, uint32_t* mask, void* stream);
+
+/* semkv_quantize_pack of one prompt per sequence: sequence b quantizes its
+ * tokens 0 .. n_seq[b]-1 (K, V laid out as for semkv_quantize_pack, with room
+ * for n_max tokens) with k = floor(r n_seq[b] + 1/2) high rows listed first in
+ * row b of perm (stride n_max, as semkv_ragged_rank_topr writes it), appends
+ * them after its own pool rows with token indices n_tokens + t, and advances
+ * its counters.  A sequence with n_seq[b] = 0 is left as is; one whose tail is
+ * not empty is skipped (SEMKV_SEQ_TAIL_BUSY).
+ * Errors: EINVAL (pointers, strides, n_max < 1, r, host counters not 0). */
+semkv_status semkv_ragged_quantize_pack(semkv_cache* c, int64_t* seq, const uint16_t* k,
+                                        const uint16_t* v, const int64_t strides[4], int64_t n_max,
+                                        const int32_t* n_seq, double r, const int32_t* perm,
+                                        void* stream);
+
+/* One generation step of a ragged batch (SemKV Fig. 6).  Every sequence with
+ * active[b] != 0 appends one token (k_new, v_new: [batch][layers][kv][128]
+ * fp16 with the given strides, token index 0; score_new: fp32 [batch]) to its
+ * tail.  Then every sequence whose tail holds `block` rows, or that has
+ * flush[b] != 0 and a non-empty tail (the end of its turn), ranks its tail
+ * with k = floor(r n_tail + 1/2), quantizes and appends it to its pools and
+ * empties its tail.  active may be NULL (no token appended: k_new, v_new,
+ * score_new are then unused), flush may be NULL (no flush).  workspace as for
+ * semkv_append_block (semkv_workspace_bytes).
+ * Errors: EINVAL, EWORKSPACE. */
+semkv_status semkv_ragged_append(semkv_cache* c, int64_t* seq, const uint16_t* k_new,
+                                 const uint16_t* v_new, const int64_t strides[4],
+                                 const float* score_new, const int32_t* active,
+                                 const int32_t* flush, double r, void* workspace, int64_t ws_bytes,
+                                 void* stream);
+
+/* semkv_decode_attn over a ragged batch: sequence b attends over its own
+ * n_high + n_low pool rows and n_tail tail rows.  max_high and max_low bound
+ * n_high and n_low over the batch (they size the launch; cap_high and cap_low
+ * always do); workspace: semkv_workspace_bytes(g, nlayers, max_high + max_low
+ * + block).  Every sequence must hold at least one token.
+ * Errors: as semkv_decode_attn; EINVAL if a bound exceeds its capacity. */
+semkv_status semkv_ragged_decode_attn(const semkv_cache* c, const int64_t* seq, const uint16_t* q,
+                                      int32_t layer0, int32_t nlayers, float sm_scale,
+                                      int64_t max_high, int64_t max_low, float* out,
+                                      void* workspace, int64_t ws_bytes, void* stream);
 
 /* Synchronise `stream` and map a sticky HIP error to SEMKV_EHIP. */
 semkv_status semkv_sync_check(void* stream);

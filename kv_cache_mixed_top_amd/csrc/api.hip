@@ -59,10 +59,25 @@ bool strides_ok(const int64_t* s) {
 
 semkv_status from_hip(hipError_t e) { return e == hipSuccess ? SEMKV_OK : SEMKV_EHIP; }
 
-int64_t topr(int64_t n, double r) { return (int64_t)std::floor(r * (double)n + 0.5); }
+// A cache used by ragged calls keeps its host counters at 0: each sequence's
+// counters are in the device array seq.
+semkv_status check_ragged(const semkv_cache* c, const int64_t* seq) {
+  const semkv_status st = check_cache(c);
+  if (st != SEMKV_OK) return st;
+  if (!seq || !aligned(seq, 8)) return SEMKV_EINVAL;
+  if (c->n_high != 0 || c->n_low != 0 || c->n_tail != 0 || c->n_tokens != 0) return SEMKV_EINVAL;
+  return SEMKV_OK;
+}
 
-int64_t append_ws_bytes(const semkv_geom& g) {
+int64_t topr(int64_t n, double r) { return semkv::topr_count(n, r); }
+
+// generation workspace: the block ranking's perm [batch][block], then (for a
+// ragged batch) the row count of each sequence's tail quantized by a call
+int64_t append_perm_bytes(const semkv_geom& g) {
   return ((int64_t)g.batch * g.block * 4 + 255) / 256 * 256;
+}
+int64_t append_ws_bytes(const semkv_geom& g) {
+  return append_perm_bytes(g) + ((int64_t)g.batch * 4 + 255) / 256 * 256;
 }
 
 int64_t decode_chunks_bound(int64_t max_tokens, int64_t units) {
@@ -101,16 +116,25 @@ QuantArgs quant_args(const semkv_cache* c, const uint16_t* k, const uint16_t* v,
   a.fmt[1] = row_fmt(c->g.L_low);
   a.token_base = token_base;
   a.rotate = c->g.rotate;
+  a.seq = nullptr;
+  a.n_seq = nullptr;
+  a.r = 0.0;
+  a.ld_perm = n;
+  a.tail_mode = 0;
   return a;
 }
 
+// seq != null: a ragged batch; c's counters are then bounds over the batch
+// and the tail bound is tail_rows.
 semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0, int32_t nl,
-                         float sm_scale, float* out, void* ws, int64_t ws_bytes, DecodeArgs* a) {
+                         float sm_scale, float* out, void* ws, int64_t ws_bytes, DecodeArgs* a,
+                         const int64_t* seq = nullptr, int64_t tail_rows = -1) {
   semkv_status st = check_cache(c);
   if (st != SEMKV_OK) return st;
   const semkv_geom& g = c->g;
   if (layer0 < 0 || nl < 1 || (int64_t)layer0 + nl > g.layers) return SEMKV_EINVAL;
-  const int64_t T = c->n_high + c->n_low + c->n_tail;
+  const int64_t n_tail = seq ? tail_rows : c->n_tail;
+  const int64_t T = c->n_high + c->n_low + n_tail;
   if (T <= 0) return SEMKV_EINVAL;
   const int64_t units = (int64_t)g.batch * nl * g.kv_heads;
   const int chunk = decode_chunk_tokens(T, units);
@@ -125,7 +149,8 @@ semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0
   a->fmt[0] = row_fmt(g.L_high);
   a->fmt[1] = row_fmt(g.L_low);
   a->tail_kv = c->tail_kv;
-  a->n_tail = c->n_tail;
+  a->n_tail = n_tail;
+  a->seq = seq;
   a->block = g.block;
   a->q = q;
   a->out = out;
@@ -140,7 +165,7 @@ semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0
   a->chunk = chunk;
   a->nch[0] = (int32_t)((c->n_high + chunk - 1) / chunk);
   a->nch[1] = (int32_t)((c->n_low + chunk - 1) / chunk);
-  a->nch[2] = (int32_t)((c->n_tail + chunk - 1) / chunk);
+  a->nch[2] = (int32_t)((n_tail + chunk - 1) / chunk);
   a->nchunks = a->nch[0] + a->nch[1] + a->nch[2];
   a->x0 = 0;
   const int64_t per_chunk_bytes = decode_partial_floats_per_chunk(a->group) * 4;
@@ -148,7 +173,7 @@ semkv_status decode_args(const semkv_cache* c, const uint16_t* q, int32_t layer0
     a->chunk = cm;
     a->nch[0] = (int32_t)((c->n_high + cm - 1) / cm);
     a->nch[1] = (int32_t)((c->n_low + cm - 1) / cm);
-    a->nch[2] = (int32_t)((c->n_tail + cm - 1) / cm);
+    a->nch[2] = (int32_t)((n_tail + cm - 1) / cm);
     a->nchunks = a->nch[0] + a->nch[1] + a->nch[2];
   };
   if (decode_use_mfma(*a)) {
@@ -371,6 +396,8 @@ semkv_status semkv_append_block(semkv_cache* c, const uint16_t* k_new, const uin
     aa.pos = (int32_t)c->n_tail;
     aa.tail_kv = c->tail_kv;
     aa.tail_score = c->tail_score;
+    aa.seq = nullptr;
+    aa.active = nullptr;
     st = from_hip(launch_append_tail(aa, s));
     if (st != SEMKV_OK) return st;
     c->n_tail += m;
@@ -463,6 +490,137 @@ semkv_status semkv_dequantize_rows(const semkv_cache* c, int32_t pool, int32_t l
   a.rotate = g.rotate;
   a.out = out;
   return from_hip(launch_dequant(a, (hipStream_t)stream));
+}
+
+// ---- ragged batches: per-sequence counters in device memory
+
+semkv_status semkv_seq_reset(int64_t* seq, int32_t batch, void* stream) {
+  if (!seq || !aligned(seq, 8) || batch < 1 || batch > 65535) return SEMKV_EINVAL;
+  return from_hip(launch_seq_reset(seq, batch, (hipStream_t)stream));
+}
+
+semkv_status semkv_ragged_rank_topr(const float* scores, int32_t batch, int64_t n_max,
+                                    int64_t ld_scores, const int32_t* n_seq, double r,
+                                    int32_t* perm, uint32_t* mask, void* stream) {
+  if (!scores || !perm || !aligned(scores, 4) || !aligned(perm, 4)) return SEMKV_EINVAL;
+  if (!n_seq || !aligned(n_seq, 4) || (mask && !aligned(mask, 4))) return SEMKV_EINVAL;
+  if (batch < 1 || batch > 65535 || n_max < 1 || n_max > (int64_t)INT32_MAX || ld_scores < n_max)
+    return SEMKV_EINVAL;
+  if (!(r >= 0.0 && r <= 1.0)) return SEMKV_EINVAL;
+  return from_hip(launch_rank(scores, batch, (int)n_max, ld_scores, 0, perm, mask,
+                              (hipStream_t)stream, n_seq, r, n_max));
+}
+
+semkv_status semkv_ragged_quantize_pack(semkv_cache* c, int64_t* seq, const uint16_t* k,
+                                        const uint16_t* v, const int64_t strides[4], int64_t n_max,
+                                        const int32_t* n_seq, double r, const int32_t* perm,
+                                        void* stream) {
+  semkv_status st = check_ragged(c, seq);
+  if (st != SEMKV_OK) return st;
+  if (!k || !v || !aligned(k, 16) || !aligned(v, 16) || !strides_ok(strides)) return SEMKV_EINVAL;
+  if (!perm || !aligned(perm, 4) || !n_seq || !aligned(n_seq, 4)) return SEMKV_EINVAL;
+  if (n_max < 1 || n_max > (int64_t)INT32_MAX || !(r >= 0.0 && r <= 1.0)) return SEMKV_EINVAL;
+  // launch bounds: both pool counts are non-decreasing in n, so n_max bounds them
+  QuantArgs a = quant_args(c, k, v, strides, n_max, perm, topr(n_max, r), 0);
+  a.seq = seq;
+  a.n_seq = n_seq;
+  a.r = r;
+  a.ld_perm = n_max;
+  a.tail_mode = 0;
+  hipStream_t s = (hipStream_t)stream;
+  st = from_hip(launch_quantize_pack(a, s));
+  if (st != SEMKV_OK) return st;
+  return from_hip(launch_seq_prefill_advance(seq, n_seq, r, c->g.batch, c->g.cap_high,
+                                             c->g.cap_low, s));
+}
+
+semkv_status semkv_ragged_append(semkv_cache* c, int64_t* seq, const uint16_t* k_new,
+                                 const uint16_t* v_new, const int64_t strides[4],
+                                 const float* score_new, const int32_t* active,
+                                 const int32_t* flush, double r, void* workspace, int64_t ws_bytes,
+                                 void* stream) {
+  semkv_status st = check_ragged(c, seq);
+  if (st != SEMKV_OK) return st;
+  if (!(r >= 0.0 && r <= 1.0)) return SEMKV_EINVAL;
+  if (active) {
+    if (!aligned(active, 4) || !k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+        !strides_ok(strides) || !score_new || !aligned(score_new, 4))
+      return SEMKV_EINVAL;
+  }
+  if (flush && !aligned(flush, 4)) return SEMKV_EINVAL;
+  const semkv_geom& g = c->g;
+  if (!workspace || !aligned(workspace, 256) || ws_bytes < append_ws_bytes(g))
+    return SEMKV_EWORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* wperm = reinterpret_cast<int32_t*>(workspace);
+  int32_t* nq = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) + append_perm_bytes(g));
+  if (active) {
+    AppendArgs aa;
+    aa.src[0] = k_new;
+    aa.src[1] = v_new;
+    aa.sb = strides[0];
+    aa.sl = strides[1];
+    aa.sh = strides[2];
+    aa.st = strides[3];
+    aa.score_new = score_new;
+    aa.t_total = 1;
+    aa.t_off = 0;
+    aa.t_cnt = 1;
+    aa.batch = g.batch;
+    aa.layers = g.layers;
+    aa.kv_heads = g.kv_heads;
+    aa.block = g.block;
+    aa.pos = 0;
+    aa.tail_kv = c->tail_kv;
+    aa.tail_score = c->tail_score;
+    aa.seq = seq;
+    aa.active = active;
+    st = from_hip(launch_append_tail(aa, s));
+    if (st != SEMKV_OK) return st;
+  }
+  st = from_hip(launch_seq_tail_plan(seq, active, flush, r, g.block, g.batch, g.cap_high,
+                                     g.cap_low, nq, s));
+  if (st != SEMKV_OK) return st;
+  // rank and quantize every tail with nq[b] > 0 rows (the others write nothing)
+  st = from_hip(launch_rank(c->tail_score, g.batch, g.block, g.block, 0, wperm, nullptr, s, nq, r,
+                            g.block));
+  if (st != SEMKV_OK) return st;
+  const int64_t tb = (int64_t)g.layers * g.kv_heads * 2 * g.block * kHeadDim;
+  const int64_t tstr[4] = {tb, (int64_t)g.kv_heads * 2 * g.block * kHeadDim,
+                           (int64_t)2 * g.block * kHeadDim, kHeadDim};
+  QuantArgs qa = quant_args(c, c->tail_kv, c->tail_kv + (int64_t)g.block * kHeadDim, tstr,
+                            g.block, wperm, topr(g.block, r), 0);
+  qa.seq = seq;
+  qa.n_seq = nq;
+  qa.r = r;
+  qa.ld_perm = g.block;
+  qa.tail_mode = 1;
+  st = from_hip(launch_quantize_pack(qa, s));
+  if (st != SEMKV_OK) return st;
+  return from_hip(launch_seq_tail_advance(seq, nq, r, g.batch, s));
+}
+
+semkv_status semkv_ragged_decode_attn(const semkv_cache* c, const int64_t* seq, const uint16_t* q,
+                                      int32_t layer0, int32_t nlayers, float sm_scale,
+                                      int64_t max_high, int64_t max_low, float* out,
+                                      void* workspace, int64_t ws_bytes, void* stream) {
+  semkv_status st = check_ragged(c, seq);
+  if (st != SEMKV_OK) return st;
+  if (!q || !aligned(q, 16) || !out || !aligned(out, 16)) return SEMKV_EINVAL;
+  if (max_high < 0 || max_high > c->g.cap_high || max_low < 0 || max_low > c->g.cap_low)
+    return SEMKV_EINVAL;
+  // launch over the bounds; every kernel reads its sequence's own rows
+  semkv_cache view = *c;
+  view.n_high = max_high;
+  view.n_low = max_low;
+  view.n_tokens = max_high + max_low;
+  DecodeArgs a;
+  st = decode_args(&view, q, layer0, nlayers, sm_scale, out, workspace, ws_bytes, &a, seq,
+                   c->g.block);
+  if (st != SEMKV_OK) return st;
+  st = from_hip(launch_decode_partials(a, (hipStream_t)stream));
+  if (st != SEMKV_OK) return st;
+  return from_hip(launch_decode_merge(a, (hipStream_t)stream));
 }
 
 semkv_status semkv_sync_check(void* stream) {

@@ -22,18 +22,32 @@ __global__ __launch_bounds__(256) void append_tail_kernel(AppendArgs a) {
     rest /= a.kv_heads;
     const int layer = (int)(rest % a.layers);
     const int b = (int)(rest / a.layers);
-    const uint16_t* src = a.src[kvsel] + (int64_t)b * a.sb + (int64_t)layer * a.sl +
-                          (int64_t)head * a.sh + (int64_t)(a.t_off + i) * a.st;
-    uint16_t* dst = a.tail_kv +
-                    (((((int64_t)b * a.layers + layer) * a.kv_heads + head) * 2 + kvsel) * a.block +
-                     a.pos + i) * kHeadDim;
-    reinterpret_cast<uint4*>(dst)[lane] = reinterpret_cast<const uint4*>(src)[lane];
+    // ragged batch: only active sequences append, at their own tail length
+    // (a full tail, left by a capacity failure, takes nothing more)
+    int pos = a.pos;
+    bool on = true;
+    if (a.seq) {
+      pos = (int)a.seq[(int64_t)b * kSeqWords + kSeqTail];
+      on = a.active[b] != 0 && pos < a.block;
+    }
+    if (on) {
+      const uint16_t* src = a.src[kvsel] + (int64_t)b * a.sb + (int64_t)layer * a.sl +
+                            (int64_t)head * a.sh + (int64_t)(a.t_off + i) * a.st;
+      uint16_t* dst = a.tail_kv +
+                      (((((int64_t)b * a.layers + layer) * a.kv_heads + head) * 2 + kvsel) * a.block +
+                       pos + i) * kHeadDim;
+      reinterpret_cast<uint4*>(dst)[lane] = reinterpret_cast<const uint4*>(src)[lane];
+    }
   }
   if (blockIdx.x == 0) {
     for (int j = threadIdx.x; j < a.batch * a.t_cnt; j += blockDim.x) {
       const int b = j / a.t_cnt, i = j - b * a.t_cnt;
-      a.tail_score[(int64_t)b * a.block + a.pos + i] =
-          a.score_new[(int64_t)b * a.t_total + a.t_off + i];
+      int pos = a.pos;
+      if (a.seq) {
+        pos = (int)a.seq[(int64_t)b * kSeqWords + kSeqTail];
+        if (a.active[b] == 0 || pos >= a.block) continue;
+      }
+      a.tail_score[(int64_t)b * a.block + pos + i] = a.score_new[(int64_t)b * a.t_total + a.t_off + i];
     }
   }
 }

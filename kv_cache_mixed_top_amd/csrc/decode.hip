@@ -59,7 +59,7 @@ struct Seg {
   int64_t t0, t1;
 };
 
-__device__ __forceinline__ Seg find_seg(const DecodeArgs& a, int x) {
+__device__ __forceinline__ Seg find_seg(const DecodeArgs& a, int x, int b) {
   Seg s;
   int ch;
   if (x < a.nch[0]) {
@@ -69,9 +69,9 @@ __device__ __forceinline__ Seg find_seg(const DecodeArgs& a, int x) {
   } else {
     s.seg = 2; ch = x - a.nch[0] - a.nch[1];
   }
-  const int64_t n = s.seg == 0 ? a.rows[0] : (s.seg == 1 ? a.rows[1] : a.n_tail);
+  const int64_t n = seg_rows(a, s.seg, b);        // a ragged batch's own rows
   s.t0 = (int64_t)ch * a.chunk;
-  s.t1 = min(s.t0 + (int64_t)a.chunk, n);
+  s.t1 = max(s.t0, min(s.t0 + (int64_t)a.chunk, n));
   return s;
 }
 
@@ -126,10 +126,10 @@ __global__ __launch_bounds__(kThreads) void decode_partials_kernel(DecodeArgs a)
 
   const int tid = threadIdx.x;
   const int x = a.x0 + blockIdx.x;
-  const Seg sg = find_seg(a, x);
+  const int b = blockIdx.z;
+  const Seg sg = find_seg(a, x, b);
   const int li = blockIdx.y / a.kv_heads;
   const int g = blockIdx.y % a.kv_heads;
-  const int b = blockIdx.z;
   const int layer = a.layer0 + li;
   const int G = a.group;
   const int nt_chunk = (int)(sg.t1 - sg.t0);
@@ -323,10 +323,10 @@ __global__ __launch_bounds__(kThreads) void decode_tail_kernel(DecodeArgs a) {
   const int x = a.x0 + blockIdx.x;
   const int ch = x - a.nch[0] - a.nch[1];
   const int64_t t0 = (int64_t)ch * a.chunk;
-  const int n = (int)(min(t0 + (int64_t)a.chunk, a.n_tail) - t0);
+  const int b = blockIdx.z;
+  const int n = (int)max((int64_t)0, min(t0 + (int64_t)a.chunk, seg_rows(a, 2, b)) - t0);
   const int li = blockIdx.y / a.kv_heads;
   const int g = blockIdx.y % a.kv_heads;
-  const int b = blockIdx.z;
   const int layer = a.layer0 + li;
   const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
   const uint16_t* kt = a.tail_kv + (plane_k * a.block + t0) * kHeadDim;
@@ -481,10 +481,10 @@ __global__ __launch_bounds__(kThreads) void decode_tail128_kernel(DecodeArgs a) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int x = a.x0 + blockIdx.x;
-  const int n = (int)a.n_tail;                 // one chunk: the whole tail
+  const int b = blockIdx.z;
+  const int n = (int)seg_rows(a, 2, b);        // one chunk: the whole tail
   const int li = blockIdx.y / a.kv_heads;
   const int g = blockIdx.y % a.kv_heads;
-  const int b = blockIdx.z;
   const int layer = a.layer0 + li;
   const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
   const uint16_t* kt = a.tail_kv + plane_k * a.block * kHeadDim;

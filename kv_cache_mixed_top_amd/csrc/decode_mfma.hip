@@ -796,11 +796,11 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const int x = blockIdx.x;
   const int seg = x < a.nch[0] ? 0 : 1;
   const int ch = seg == 0 ? x : x - a.nch[0];
+  const int b = blockIdx.z;
   const int64_t r0 = (int64_t)ch * a.chunk;
-  const int64_t r1 = min(r0 + (int64_t)a.chunk, a.rows[seg]);
+  const int64_t r1 = max(r0, min(r0 + (int64_t)a.chunk, seg_rows(a, seg, b)));   // a ragged batch's own rows
   const int li = blockIdx.y / a.kv_heads;
   const int g = blockIdx.y % a.kv_heads;
-  const int b = blockIdx.z;
   const int64_t u = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   QInt& qi = *reinterpret_cast<QInt*>(wx);

@@ -108,14 +108,46 @@ __device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
   }
 }
 
+// What one workgroup's pool writes: its row count, where its rows start in
+// perm, its first destination slot and the token index base.  A ragged batch
+// takes them from the sequence's device counters; a sequence whose rows would
+// not fit (or, for a prompt, whose tail is not empty) writes nothing, and the
+// counter update that follows records that in its status word.
+struct PoolPart {
+  int count, perm_off;
+  int64_t start, token_base, perm_ld;
+};
+__device__ __forceinline__ PoolPart pool_part(const QuantArgs& a, int pool, int b) {
+  PoolPart pp;
+  if (!a.seq) {
+    pp.count = pool == 0 ? a.k_high : a.n - a.k_high;
+    pp.perm_off = pool == 0 ? 0 : a.k_high;
+    pp.start = a.start[pool];
+    pp.token_base = a.token_base;
+    pp.perm_ld = a.n;
+    return pp;
+  }
+  const int64_t* sq = a.seq + (int64_t)b * kSeqWords;
+  const int n = a.n_seq[b];
+  const int k = (int)topr_count(n, a.r);
+  const bool skip = (a.tail_mode == 0 && sq[kSeqTail] != 0) || sq[kSeqHigh] + k > a.cap[0] ||
+                    sq[kSeqLow] + (n - k) > a.cap[1];
+  pp.count = skip ? 0 : (pool == 0 ? k : n - k);
+  pp.perm_off = pool == 0 ? 0 : k;
+  pp.start = sq[pool == 0 ? kSeqHigh : kSeqLow];
+  pp.token_base = sq[kSeqTokens] - sq[kSeqTail];
+  pp.perm_ld = a.ld_perm;
+  return pp;
+}
+
 // One 64-slot tile of one pool plane.  LF = level count known at compile
 // time (6 or 5), or 0 for the runtime format of the pool.
 template <int LF, bool kRot>
-__device__ __forceinline__ void quantize_tile(const QuantArgs& a, int pool, int tile_in_pool,
-                              uint16_t* codes) {
+__device__ __forceinline__ void quantize_tile(const QuantArgs& a, const PoolPart& pp, int pool,
+                                              int tile_in_pool, uint16_t* codes) {
   const RowFmt f = LF ? row_fmt(LF) : a.fmt[pool];
-  const int count = pool == 0 ? a.k_high : a.n - a.k_high;
-  const int perm_off = pool == 0 ? 0 : a.k_high;
+  const int count = pp.count;
+  const int perm_off = pp.perm_off;
   const int y = blockIdx.y;
   const int kvsel = y & 1;
   const int head = (y >> 1) % a.kv_heads;
@@ -128,13 +160,13 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, int pool, int 
   const int r = tid >> 2, q = tid & 3;
   const bool valid = r < nrows;
   const int64_t plane = (((int64_t)b * a.layers + layer) * a.kv_heads + head) * 2 + kvsel;
-  const int64_t slot0 = a.start[pool] + row0;
+  const int64_t slot0 = pp.start + row0;
 
   // ---- load 32 values of this row (d = 8q + 32i + e)
   int token = 0;
   float v[32];
   if (valid) {
-    token = a.perm[(int64_t)b * a.n + perm_off + row0 + r];
+    token = a.perm[(int64_t)b * pp.perm_ld + perm_off + row0 + r];
     const uint16_t* src = a.src[kvsel] + (int64_t)b * a.sb + (int64_t)layer * a.sl +
                           (int64_t)head * a.sh + (int64_t)token * a.st;
 #pragma unroll
@@ -201,7 +233,7 @@ __device__ __forceinline__ void quantize_tile(const QuantArgs& a, int pool, int 
     const int64_t slot = slot0 + r;
     a.meta[pool][plane * a.cap[pool] + slot] = (uint32_t)sbits | ((uint32_t)f2h(lo) << 16);
     if (layer == 0 && head == 0 && kvsel == 0)
-      a.tok[pool][(int64_t)b * a.cap[pool] + slot] = (int32_t)(a.token_base + token);
+      a.tok[pool][(int64_t)b * a.cap[pool] + slot] = (int32_t)(pp.token_base + token);
   }
   __syncthreads();
 
@@ -317,11 +349,11 @@ __device__ __forceinline__ uint16_t scale_ceil_fast(float lo, float hi) {
 
 // kRot: the rows are Hadamard-rotated (fp32 values kept in registers).
 template <int L, bool kRot>
-__device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool, int tile_in_pool,
-                                   uint8_t* codes8, uint8_t* img) {
+__device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, const PoolPart& pp, int pool,
+                                                   int tile_in_pool, uint8_t* codes8, uint8_t* img) {
   constexpr int R = fast_row_bytes<L>();
-  const int count = pool == 0 ? a.k_high : a.n - a.k_high;
-  const int perm_off = pool == 0 ? 0 : a.k_high;
+  const int count = pp.count;
+  const int perm_off = pp.perm_off;
   const int y = blockIdx.y;
   const int kvsel = y & 1;
   const int head = (y >> 1) % a.kv_heads;
@@ -333,14 +365,14 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
   const int r = tid >> 2, q = tid & 3;
   const bool valid = r < nrows;
   const int64_t plane = (((int64_t)b * a.layers + layer) * a.kv_heads + head) * 2 + kvsel;
-  const int64_t slot0 = a.start[pool] + row0;
+  const int64_t slot0 = pp.start + row0;
 
   // ---- 32 values of this row as 16 fp16 pairs (dims 8q + 32i + 2e + {0,1})
   int token = 0;
   half2_t v[16];
   const uint16_t* src = nullptr;
   if (valid) {
-    token = a.perm[(int64_t)b * a.n + perm_off + row0 + r];
+    token = a.perm[(int64_t)b * pp.perm_ld + perm_off + row0 + r];
     src = a.src[kvsel] + (int64_t)b * a.sb + (int64_t)layer * a.sl + (int64_t)head * a.sh +
           (int64_t)token * a.st;
 #pragma unroll
@@ -505,7 +537,7 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
     const int64_t slot = slot0 + r;
     a.meta[pool][plane * a.cap[pool] + slot] = (uint32_t)sbits | ((uint32_t)f2h(lo) << 16);
     if (layer == 0 && head == 0 && kvsel == 0)
-      a.tok[pool][(int64_t)b * a.cap[pool] + slot] = (int32_t)(a.token_base + token);
+      a.tok[pool][(int64_t)b * a.cap[pool] + slot] = (int32_t)(pp.token_base + token);
   }
   __syncthreads();
 
@@ -616,18 +648,20 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, int pool,
 // generic tile.
 template <int LF, bool kRot>
 __device__ __forceinline__ void pool_tile(const QuantArgs& a, int pool, int t, uint8_t* smem) {
-  const bool aligned16 = (a.start[pool] & 15) == 0;
+  const PoolPart pp = pool_part(a, pool, blockIdx.z);
+  if (t * kRows >= pp.count) return;            // past this sequence's rows (ragged bounds)
+  const bool aligned16 = (pp.start & 15) == 0;
   const int L = LF ? LF : a.fmt[pool].L;
   uint8_t* img = smem + kCode8Bytes;
   if (aligned16 && fast_quant_level(L)) {
-    if (LF == 6 || (LF == 0 && L == 6)) quantize_tile_fast<6, kRot>(a, pool, t, smem, img);
-    else if (LF == 5 || (LF == 0 && L == 5)) quantize_tile_fast<5, kRot>(a, pool, t, smem, img);
-    else if (LF == 0 && L == 4) quantize_tile_fast<4, kRot>(a, pool, t, smem, img);
-    else if (LF == 0 && L == 16) quantize_tile_fast<16, kRot>(a, pool, t, smem, img);
-    else if (LF == 0 && L == 8) quantize_tile_fast<8, kRot>(a, pool, t, smem, img);
-    else if (LF == 0 && L == 3) quantize_tile_fast<3, kRot>(a, pool, t, smem, img);
+    if (LF == 6 || (LF == 0 && L == 6)) quantize_tile_fast<6, kRot>(a, pp, pool, t, smem, img);
+    else if (LF == 5 || (LF == 0 && L == 5)) quantize_tile_fast<5, kRot>(a, pp, pool, t, smem, img);
+    else if (LF == 0 && L == 4) quantize_tile_fast<4, kRot>(a, pp, pool, t, smem, img);
+    else if (LF == 0 && L == 16) quantize_tile_fast<16, kRot>(a, pp, pool, t, smem, img);
+    else if (LF == 0 && L == 8) quantize_tile_fast<8, kRot>(a, pp, pool, t, smem, img);
+    else if (LF == 0 && L == 3) quantize_tile_fast<3, kRot>(a, pp, pool, t, smem, img);
   } else {
-    quantize_tile<LF, kRot>(a, pool, t, reinterpret_cast<uint16_t*>(smem));
+    quantize_tile<LF, kRot>(a, pp, pool, t, reinterpret_cast<uint16_t*>(smem));
   }
 }
 

@@ -24,6 +24,19 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 
+// Ragged batches: sequence b ranks its first n_seq[b] (at most n) scores
+// with its own k = floor(r n_seq[b] + 1/2); perm rows have stride ld_perm
+// and mask rows (n + 31) / 32 words, n being the bound of the launch.
+struct RaggedRank {
+  const int32_t* n_seq;
+  double r;
+  int64_t ld_perm;
+  __device__ void apply(int b, int& n, int& k) const {
+    n = min(n_seq[b], n);
+    k = (int)topr_count(n, r);
+  }
+};
+
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (f != f) return 0u;                 // NaN: below every number
@@ -62,7 +75,7 @@ __device__ int block_exclusive_scan(int v, int* buf, int* total) {
 
 __global__ __launch_bounds__(kThreads) void rank_select_kernel(
     const float* __restrict__ scores, int64_t ld, int n, int k, int items,
-    int32_t* __restrict__ perm, uint32_t* __restrict__ mask) {
+    int32_t* __restrict__ perm, uint32_t* __restrict__ mask, RaggedRank rg) {
   __shared__ uint32_t hist[kWaves][256];
   __shared__ int scan_buf[kWaves + 1];
   __shared__ uint32_t sh_prefix;
@@ -70,9 +83,11 @@ __global__ __launch_bounds__(kThreads) void rank_select_kernel(
 
   const int b = blockIdx.x;
   const float* s = scores + (int64_t)b * ld;
-  int32_t* p = perm + (int64_t)b * n;
+  int32_t* p = perm + (int64_t)b * (rg.ld_perm > 0 ? rg.ld_perm : n);
+  uint32_t* mk = mask ? mask + (int64_t)b * ((n + 31) >> 5) : nullptr;
+  if (rg.n_seq) rg.apply(b, n, k);
+  if (n <= 0) return;
   const int nwords = (n + 31) >> 5;
-  uint32_t* mk = mask ? mask + (int64_t)b * nwords : nullptr;
   const int tid = threadIdx.x, wave = tid >> 6;
 
   // -- radix select of the k-th largest key (k >= 1)
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(kThreads) void rank_select_kernel(
 // latency) and the radix digit found by a parallel scan of the 256 bins.
 __global__ __launch_bounds__(kThreads) void rank_select32_kernel(
     const float* __restrict__ scores, int64_t ld, int n, int k, int32_t* __restrict__ perm,
-    uint32_t* __restrict__ mask) {
+    uint32_t* __restrict__ mask, RaggedRank rg) {
   constexpr int kItems = 32;
   __shared__ uint32_t hist[kWaves][256];
   __shared__ int scan_buf[kWaves + 1];
@@ -177,9 +192,11 @@ __global__ __launch_bounds__(kThreads) void rank_select32_kernel(
 
   const int b = blockIdx.x;
   const float* s = scores + (int64_t)b * ld;
-  int32_t* p = perm + (int64_t)b * n;
+  int32_t* p = perm + (int64_t)b * (rg.ld_perm > 0 ? rg.ld_perm : n);
+  uint32_t* mk = mask ? mask + (int64_t)b * ((n + 31) >> 5) : nullptr;
+  if (rg.n_seq) rg.apply(b, n, k);
+  if (n <= 0) return;
   const int nwords = (n + 31) >> 5;
-  uint32_t* mk = mask ? mask + (int64_t)b * nwords : nullptr;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int begin = tid * kItems;
   const int cnt = max(0, min(kItems, n - begin));
@@ -295,11 +312,14 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
 // One wave per sequence, n <= 128.  Element e = j*64 + lane (j = 0, 1).
 __global__ __launch_bounds__(64) void rank_block_kernel(
     const float* __restrict__ scores, int64_t ld, int n, int k,
-    int32_t* __restrict__ perm, uint32_t* __restrict__ mask) {
+    int32_t* __restrict__ perm, uint32_t* __restrict__ mask, RaggedRank rg) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
   const float* s = scores + (int64_t)b * ld;
-  int32_t* p = perm + (int64_t)b * n;
+  int32_t* p = perm + (int64_t)b * (rg.ld_perm > 0 ? rg.ld_perm : n);
+  const int mask_ld = (n + 31) >> 5;
+  if (rg.n_seq) rg.apply(b, n, k);
+  if (n <= 0) return;
   const int nwords = (n + 31) >> 5;
 
   // composite: higher is better; ties resolved by the lower index
@@ -339,7 +359,7 @@ __global__ __launch_bounds__(64) void rank_block_kernel(
   const uint64_t b0 = __ballot(in0);
   const uint64_t b1 = __ballot(in1);
   if (mask) {
-    uint32_t* mk = mask + (int64_t)b * nwords;
+    uint32_t* mk = mask + (int64_t)b * mask_ld;
     const uint32_t w[4] = {(uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32)};
     if (lane < nwords) mk[lane] = w[lane];
   }
@@ -365,18 +385,20 @@ __global__ __launch_bounds__(64) void rank_block_kernel(
 }  // namespace
 
 hipError_t launch_rank(const float* scores, int batch, int n, int64_t ld, int k,
-                       int32_t* perm, uint32_t* mask, hipStream_t stream) {
+                       int32_t* perm, uint32_t* mask, hipStream_t stream, const int32_t* n_seq,
+                       double r, int64_t ld_perm) {
+  const RaggedRank rg{n_seq, r, ld_perm};
   if (n <= 128) {
     hipLaunchKernelGGL(rank_block_kernel, dim3(batch), dim3(64), 0, stream, scores, ld, n, k,
-                       perm, mask);
+                       perm, mask, rg);
   } else if (n <= 32 * kThreads) {
     hipLaunchKernelGGL(rank_select32_kernel, dim3(batch), dim3(kThreads), 0, stream, scores, ld,
-                       n, k, perm, mask);
+                       n, k, perm, mask, rg);
   } else {
     int items = (n + kThreads - 1) / kThreads;
     items = (items + 31) & ~31;   // each thread owns whole mask words
     hipLaunchKernelGGL(rank_select_kernel, dim3(batch), dim3(kThreads), 0, stream, scores, ld,
-                       n, k, items, perm, mask);
+                       n, k, items, perm, mask, rg);
   }
   return hipGetLastError();
 }

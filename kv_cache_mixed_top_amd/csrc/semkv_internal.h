@@ -18,10 +18,23 @@ struct ScoreArgs {
 };
 hipError_t launch_score_keynorm(const ScoreArgs& a, int batch, hipStream_t stream);
 
+// ---------------------------------------------------------------- ragged batches
+// Per-sequence counters in device memory, kSeqWords int64 per sequence.
+constexpr int kSeqWords = 8;
+enum SeqWord { kSeqHigh = 0, kSeqLow = 1, kSeqTail = 2, kSeqTokens = 3, kSeqStatus = 4 };
+enum SeqStatus { kSeqCapacity = 1, kSeqTailBusy = 2, kSeqTailFull = 4 };
+// floor(r n + 1/2) in double, as semkv_topr_count
+__host__ __device__ inline int64_t topr_count(int64_t n, double r) {
+  return (int64_t)floor(r * (double)n + 0.5);
+}
+
 // ---------------------------------------------------------------- rank
-// perm/mask of `batch` sequences of n scores each (row stride ld).
+// perm/mask of `batch` sequences of n scores each (row stride ld).  With
+// n_seq, sequence b ranks its first n_seq[b] <= n scores with k = floor(r
+// n_seq[b] + 1/2) and perm rows have stride ld_perm.
 hipError_t launch_rank(const float* scores, int batch, int n, int64_t ld, int k,
-                       int32_t* perm, uint32_t* mask, hipStream_t stream);
+                       int32_t* perm, uint32_t* mask, hipStream_t stream,
+                       const int32_t* n_seq = nullptr, double r = 0.0, int64_t ld_perm = -1);
 
 // ---------------------------------------------------------------- quantize
 struct QuantArgs {
@@ -38,6 +51,15 @@ struct QuantArgs {
   RowFmt fmt[2];
   int64_t token_base;       // tok_* = token_base + token
   int32_t rotate;           // Hadamard-rotate every row before quantizing
+  // ragged batches (seq != null): sequence b quantizes n_seq[b] tokens with
+  // k = floor(r n_seq[b] + 1/2), at its own pool counters, token base
+  // n_tokens - n_tail; perm rows have stride ld_perm.  tail_mode = 0: a
+  // prompt (skipped while the sequence's tail is not empty); 1: a tail block.
+  const int64_t* seq;
+  const int32_t* n_seq;
+  double r;
+  int64_t ld_perm;
+  int32_t tail_mode;
 };
 hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream);
 
@@ -51,6 +73,10 @@ struct AppendArgs {
   int32_t pos;              // first tail row written
   uint16_t* tail_kv;
   float* tail_score;
+  // ragged batches (seq != null): one token per sequence with active[b] != 0,
+  // written at that sequence's n_tail (pos and t_cnt are then unused)
+  const int64_t* seq;
+  const int32_t* active;
 };
 hipError_t launch_append_tail(const AppendArgs& a, hipStream_t stream);
 
@@ -89,7 +115,15 @@ struct DecodeArgs {
   int32_t x0;               // first chunk index handled by a launch
   float* ws;                // partials
   int32_t rotate;           // rows are Hadamard-rotated: rotate q, rotate the output back
+  // ragged batches (seq != null): sequence b has its own n_high, n_low and
+  // n_tail there; rows[] and n_tail are bounds over the batch
+  const int64_t* seq;
 };
+// rows of pool seg (0, 1) or of the tail (2) of sequence b
+__device__ __forceinline__ int64_t seg_rows(const DecodeArgs& a, int seg, int b) {
+  if (a.seq) return a.seq[(int64_t)b * kSeqWords + seg];
+  return seg == 0 ? a.rows[0] : seg == 1 ? a.rows[1] : a.n_tail;
+}
 // Chunking rule shared by the launchers and the workspace query.
 int decode_chunk_tokens(int64_t tokens_per_unit, int64_t units);
 int64_t decode_partial_floats_per_chunk(int group);
@@ -107,5 +141,21 @@ int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units);
 int64_t decode_mfma_resident_waves();
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- ragged counters
+hipError_t launch_seq_reset(int64_t* seq, int batch, hipStream_t stream);
+// After a ragged prompt: advance each sequence's counters by what the
+// quantize kernel wrote for it (the same capacity and tail decisions).
+hipError_t launch_seq_prefill_advance(int64_t* seq, const int32_t* n_seq, double r, int batch,
+                                      int64_t cap_high, int64_t cap_low, hipStream_t stream);
+// After a ragged append: count the appended tokens, decide per sequence
+// whether its tail is quantized now (full, or flushed), write that row count
+// (0 if not) to nq.
+hipError_t launch_seq_tail_plan(int64_t* seq, const int32_t* active, const int32_t* flush,
+                                double r, int block, int batch, int64_t cap_high, int64_t cap_low,
+                                int32_t* nq, hipStream_t stream);
+// After the tail blocks were quantized: move their rows to the pool counters.
+hipError_t launch_seq_tail_advance(int64_t* seq, const int32_t* nq, double r, int batch,
+                                   hipStream_t stream);
 
 }  // namespace semkv

@@ -64,6 +64,14 @@ _SIGS = {
     "semkv_decode_noalloc_scratch_bytes": (c_i64, []),
     "semkv_dequantize_rows": (c_i32, [ctypes.POINTER(semkv_cache), c_i32, c_i32, c_i64, c_i64,
                                       c_p, c_p]),
+    "semkv_seq_reset": (c_i32, [c_p, c_i32, c_p]),
+    "semkv_ragged_rank_topr": (c_i32, [c_p, c_i32, c_i64, c_i64, c_p, c_f64, c_p, c_p, c_p]),
+    "semkv_ragged_quantize_pack": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_p, c_p,
+                                           ctypes.POINTER(c_i64), c_i64, c_p, c_f64, c_p, c_p]),
+    "semkv_ragged_append": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_p, c_p,
+                                    ctypes.POINTER(c_i64), c_p, c_p, c_p, c_f64, c_p, c_i64, c_p]),
+    "semkv_ragged_decode_attn": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_p, c_i32, c_i32, c_f32,
+                                         c_i64, c_i64, c_p, c_p, c_i64, c_p]),
     "semkv_sync_check": (c_i32, [c_p]),
     "semkv_status_str": (ctypes.c_char_p, [c_i32]),
 }
@@ -292,6 +300,110 @@ def semkv_dequantize_rows(cache: "SemKVCache", high: bool, layer, row0, nrows, o
     _check("semkv_dequantize_rows",
            _lib.semkv_dequantize_rows(ctypes.byref(cache.c), 0 if high else 1, layer, row0, nrows,
                                       _ptr(out), _stream(stream)))
+
+
+# ------------------------------------------------------------------ ragged batches
+
+SEQ_WORDS = 8          # int64 counters per sequence: n_high, n_low, n_tail, n_tokens, status
+SEQ_HIGH, SEQ_LOW, SEQ_TAIL, SEQ_TOKENS, SEQ_STATUS = range(5)
+
+
+def _seq(cache, seq):
+    if (seq.dtype != torch.int64 or tuple(seq.shape) != (cache.geom.batch, SEQ_WORDS)
+            or not seq.is_contiguous()):
+        raise ValueError(f"seq must be a contiguous int64 [batch][{SEQ_WORDS}] tensor")
+    _on_device(seq)
+
+
+def _per_seq_i32(cache, t, name):
+    if t is None:
+        return
+    if t.dtype != torch.int32 or tuple(t.shape) != (cache.geom.batch,) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 [batch] tensor")
+    _on_device(t)
+
+
+def semkv_seq_reset(seq, stream=None):
+    if seq.dtype != torch.int64 or seq.dim() != 2 or seq.shape[1] != SEQ_WORDS or not seq.is_contiguous():
+        raise ValueError(f"seq must be a contiguous int64 [batch][{SEQ_WORDS}] tensor")
+    _on_device(seq)
+    _check("semkv_seq_reset", _lib.semkv_seq_reset(_ptr(seq), seq.shape[0], _stream(stream)))
+
+
+def semkv_ragged_rank_topr(scores, n_seq, r, perm, mask=None, stream=None):
+    """scores fp32 [B][>= n_max]; n_seq int32 [B]; perm int32 [B][n_max] out."""
+    batch, n_max = perm.shape
+    if scores.dtype != torch.float32 or scores.dim() != 2 or scores.stride(1) != 1 or scores.shape[1] < n_max:
+        raise ValueError("scores must be fp32 [B][>= n_max] with unit stride")
+    if perm.dtype != torch.int32 or not perm.is_contiguous() or scores.shape[0] != batch:
+        raise ValueError("perm must be a contiguous int32 [B][n_max] tensor")
+    if n_seq.dtype != torch.int32 or tuple(n_seq.shape) != (batch,) or not n_seq.is_contiguous():
+        raise ValueError("n_seq must be a contiguous int32 [B] tensor")
+    if mask is not None and (mask.dtype != torch.int32 or tuple(mask.shape) != (batch, (n_max + 31) // 32)
+                             or not mask.is_contiguous()):
+        raise ValueError("mask must be a contiguous int32 [B][ceil(n_max/32)] tensor")
+    _on_device(scores, n_seq, perm, mask)
+    _check("semkv_ragged_rank_topr",
+           _lib.semkv_ragged_rank_topr(_ptr(scores), batch, n_max, scores.stride(0), _ptr(n_seq), r,
+                                       _ptr(perm), _ptr(mask), _stream(stream)))
+
+
+def semkv_ragged_quantize_pack(cache: "SemKVCache", seq, K, V, n_seq, r, perm, stream=None):
+    """K, V fp16 [batch][layers][kv][n_max][128]; n_seq int32 [batch]; perm int32 [batch][n_max]."""
+    strides = _kv_rows(cache, K, V, "K/V")
+    n_max = K.shape[3]
+    _seq(cache, seq)
+    _per_seq_i32(cache, n_seq, "n_seq")
+    if perm.dtype != torch.int32 or tuple(perm.shape) != (cache.geom.batch, n_max) or not perm.is_contiguous():
+        raise ValueError("perm must be a contiguous int32 [batch][n_max] tensor")
+    _on_device(K, V, perm)
+    _check("semkv_ragged_quantize_pack",
+           _lib.semkv_ragged_quantize_pack(ctypes.byref(cache.c), _ptr(seq), _ptr(K), _ptr(V), strides,
+                                           n_max, _ptr(n_seq), r, _ptr(perm), _stream(stream)))
+
+
+def semkv_ragged_append(cache: "SemKVCache", seq, K_new, V_new, score_new, active, r, flush=None,
+                        workspace=None, stream=None):
+    """One token per active sequence: K_new/V_new fp16 [batch][layers][kv][1][128], score_new fp32
+    [batch], active / flush int32 [batch] (either may be None)."""
+    _seq(cache, seq)
+    _per_seq_i32(cache, active, "active")
+    _per_seq_i32(cache, flush, "flush")
+    ws = cache.workspace if workspace is None else workspace
+    _on_device(ws)
+    if active is None:
+        _check("semkv_ragged_append",
+               _lib.semkv_ragged_append(ctypes.byref(cache.c), _ptr(seq), None, None, None, None, None,
+                                        _ptr(flush), r, _ptr(ws), _nbytes(ws), _stream(stream)))
+        return
+    strides = _kv_rows(cache, K_new, V_new, "K_new/V_new")
+    if K_new.shape[3] != 1:
+        raise ValueError("K_new/V_new hold one token per sequence")
+    if (score_new.dtype != torch.float32 or tuple(score_new.shape) != (cache.geom.batch,)
+            or not score_new.is_contiguous()):
+        raise ValueError("score_new must be a contiguous fp32 [batch] tensor")
+    _on_device(K_new, V_new, score_new)
+    _check("semkv_ragged_append",
+           _lib.semkv_ragged_append(ctypes.byref(cache.c), _ptr(seq), _ptr(K_new), _ptr(V_new), strides,
+                                    _ptr(score_new), _ptr(active), _ptr(flush), r, _ptr(ws), _nbytes(ws),
+                                    _stream(stream)))
+
+
+def semkv_ragged_decode_attn(cache: "SemKVCache", seq, q, out, max_high, max_low, layer0=0, sm_scale=1.0,
+                             workspace=None, stream=None):
+    """q fp16 [B][nl][Hq][128]; out fp32 [B][nl][Hq][128]; max_high / max_low bound the
+    sequences' pool rows."""
+    _seq(cache, seq)
+    _dense(q, "q", torch.float16, cache)
+    _dense(out, "out", torch.float32, cache)
+    if out.shape[1] != q.shape[1]:
+        raise ValueError("q and out must cover the same layers")
+    ws = cache.workspace if workspace is None else workspace
+    _on_device(ws)
+    _check("semkv_ragged_decode_attn",
+           _lib.semkv_ragged_decode_attn(ctypes.byref(cache.c), _ptr(seq), _ptr(q), layer0, q.shape[1],
+                                         sm_scale, max_high, max_low, _ptr(out), _ptr(ws), _nbytes(ws),
+                                         _stream(stream)))
 
 
 def semkv_sync_check(stream=None):

@@ -88,7 +88,10 @@ def test_geometry_validation(bad, status):
 def test_workspace_query():
     g = geom()
     assert sk.semkv_workspace_bytes(g, 32, 32768) > 0
-    assert sk.semkv_workspace_bytes(g, 0, 0) == 128 * 4 + (256 - (128 * 4) % 256) % 256
+    # generation only: the block ranking's perm [batch][block] int32, then one
+    # int32 per sequence for the ragged tail plan, each rounded to 256 bytes
+    rnd = lambda x: (x + 255) // 256 * 256
+    assert sk.semkv_workspace_bytes(g, 0, 0) == rnd(1 * 128 * 4) + rnd(1 * 4)
     assert sk._lib.semkv_workspace_bytes(ctypes.byref(g), 33, 10) < 0
 
 
@@ -242,3 +245,36 @@ def test_binding_rejects_bad_quantize_and_append_inputs():
     for k_, v_, s_ in bad_app:
         with pytest.raises(ValueError):
             sk.semkv_append_block(cache, k_, v_, s_, 0.25)
+
+
+def test_ragged_validation_before_launch():
+    """Ragged calls check their arguments on the host and launch nothing on
+    a bad one (the pointers below are never dereferenced)."""
+    c = fake_cache()
+    p = ctypes.c_void_p(0x200000)
+    seq = ctypes.c_void_p(0x300000)
+    st = (ctypes.c_int64 * 4)(32 * 8 * 32768 * 128, 8 * 32768 * 128, 32768 * 128, 128)
+    E = sk.SEMKV_EINVAL
+    q = sk._lib.semkv_ragged_quantize_pack
+    assert q(ctypes.byref(c), None, p, p, st, 100, p, 0.5, p, None) == E        # null seq
+    assert q(ctypes.byref(c), ctypes.c_void_p(0x300004), p, p, st, 100, p, 0.5, p, None) == E
+    assert q(ctypes.byref(c), seq, p, p, st, 0, p, 0.5, p, None) == E          # n_max < 1
+    assert q(ctypes.byref(c), seq, p, p, st, 100, p, 1.5, p, None) == E        # r
+    assert q(ctypes.byref(c), seq, p, p, st, 100, None, 0.5, p, None) == E     # null n_seq
+    busy = fake_cache()
+    busy.n_high, busy.n_tokens = 5, 5                                          # host counters in use
+    assert q(ctypes.byref(busy), seq, p, p, st, 100, p, 0.5, p, None) == E
+    a = sk._lib.semkv_ragged_append
+    assert a(ctypes.byref(c), seq, p, p, st, p, p, None, 0.5, p, 16, None) == sk.SEMKV_EWORKSPACE
+    assert a(ctypes.byref(c), seq, None, p, st, p, p, None, 0.5, p, 1 << 20, None) == E   # active, no K
+    assert a(ctypes.byref(c), seq, p, p, st, p, ctypes.c_void_p(0x200002), None, 0.5, p, 1 << 20,
+             None) == E                                                        # misaligned active
+    d = sk._lib.semkv_ragged_decode_attn
+    assert d(ctypes.byref(c), seq, p, 0, 1, 1.0, c.g.cap_high + 16, 0, p, p, 1 << 30, None) == E
+    assert d(ctypes.byref(c), seq, p, 0, 1, 1.0, -1, 0, p, p, 1 << 30, None) == E
+    assert d(ctypes.byref(c), seq, p, 0, 1, 1.0, 100, 100, p, p, 16, None) == sk.SEMKV_EWORKSPACE
+    r = sk._lib.semkv_ragged_rank_topr
+    assert r(p, 2, 100, 99, p, 0.5, p, None, None) == E                        # ld < n_max
+    assert r(p, 2, 100, 100, None, 0.5, p, None, None) == E                    # null n_seq
+    assert sk._lib.semkv_seq_reset(None, 2, None) == E
+    assert sk._lib.semkv_seq_reset(seq, 0, None) == E
