@@ -10,4 +10,4 @@ from .semkv_oracle import (GenerationCache, Pools, attention, decode_attention, 
                            quantize_rows, rank_order, rank_topr, rank_topr_batch,
                            row_bytes, scale_fp16_ceil, topr_count, unpack_rows,
                            hadamard128, rotate_rows_f32, fp16_floor, quantize_rows_rotated,
-                           score_keynorm, RaggedGeneration)
+                           score_keynorm, RaggedGeneration, score_hidden_delta)

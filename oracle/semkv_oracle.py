@@ -74,6 +74,27 @@ def score_keynorm(K: np.ndarray, layer0: int, nlayers: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# Scoring by hidden-state delta norm (SemKV Table 2: the default indicator is
+# the hidden-state delta norm over the last 4 layers; Fig. 10: it costs O(1)
+# per token, being read from the token's own hidden states).  Reading (the
+# formula is open on the pages): with h_0 .. h_S the hidden states of token
+# t entering and leaving the last S layers (S = 4), the score is the sum over
+# those layers of the Euclidean norm of the layer's update, sum_{j=1..S}
+# ||h_j[t] - h_{j-1}[t]||_2.  Only the order matters to the ranking.
+# --------------------------------------------------------------------------
+
+
+def score_hidden_delta(H: np.ndarray) -> np.ndarray:
+    """H fp16 [B][S+1][n][d] (hidden states h_0 .. h_S per token) -> float64
+    [B][n]: score[b, t] = sum_{j=1..S} sqrt(sum_k (H[b,j,t,k] - H[b,j-1,t,k])^2)."""
+    H = np.asarray(H, dtype=np.float16).astype(np.float64)
+    if H.ndim != 4 or H.shape[1] < 2:
+        raise ValueError("need H [B][S+1][n][d] with S >= 1")
+    D = H[:, 1:] - H[:, :-1]                               # [B][S][n][d], exact in float64
+    return np.sqrt(np.sum(D * D, axis=-1)).sum(axis=1)
+
+
+# --------------------------------------------------------------------------
 # Rank (SemKV Fig. 2: ranking within each prompt, no score normalisation;
 #       SemKV Fig. 4: the top-r tokens form the high-precision set H, no
 #       threshold is estimated; SemKV Fig. 5: one assignment per token,
