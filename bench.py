@@ -275,6 +275,10 @@ def main():
             f"{result['score_keynorm']['GB/s']} GB/s")
         del K, V
         torch.cuda.empty_cache()
+        result["score_hidden_delta"] = delta_leg(sk, W, torch, w, dev, stream)
+        log(f"delta-norm score: {result['score_hidden_delta']['us']} us, "
+            f"{result['score_hidden_delta']['GB/s']} GB/s")
+        torch.cuda.empty_cache()
         result["generation"] = gen_leg(sk, W, torch, dev, stream, args.gen_steps)
         g = result["generation"]
         log(f"generation: decode {g['decode_us_per_step']} us/step, "
@@ -401,6 +405,42 @@ def score_leg(sk, torch, K, stream, window=4, reps=10):
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"layers": [layer0, layers], "algorithmic_bytes": nbytes, "us": round(ms * 1e3, 2),
             "GB/s": round(gbs, 1), "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
+
+
+def delta_leg(sk, W, torch, w, dev, stream, states=5, reps=10):
+    """Hidden-state delta-norm scores (semkv_score_hidden_delta, the pages'
+    default indicator over the last 4 layers) of synthetic hidden states at
+    the workload's token count and the backbone's hidden size, mean of `reps`
+    launches timed by HIP events; then the top-r rank of those scores.
+    Algorithmic bytes: the states read once plus the fp32 scores written."""
+    import numpy as np
+    Ev = lambda: torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        H = W.make_hidden_states_torch(w, dev, states=states)
+    stream.synchronize()
+    B, S1, n, d = H.shape
+    scores = torch.empty((B, n), dtype=torch.float32, device=dev)
+    perm = torch.empty((B, n), dtype=torch.int32, device=dev)
+    k = sk.semkv_topr_count(n, w.r)
+    sk.semkv_score_hidden_delta(H, scores, stream=stream)
+    stream.synchronize()
+    ev = [(Ev(), Ev(), Ev()) for _ in range(reps)]
+    for a, b, c in ev:
+        a.record(stream)
+        sk.semkv_score_hidden_delta(H, scores, stream=stream)
+        b.record(stream)
+        sk.semkv_rank_topr(scores, k, perm, stream=stream)
+        c.record(stream)
+    stream.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    rank_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    nbytes = B * S1 * n * d * 2 + B * n * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    del H
+    return {"states": S1, "hidden_size": d, "tokens": n, "batch": B, "algorithmic_bytes": nbytes,
+            "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+            "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "rank_us": round(rank_ms * 1e3, 2),
+            "inputs": "synthetic: h_0 ~ N(0,1), per-layer updates N(0,1) x U(0.05, 0.5) per token"}
 
 
 def copy_leg(torch, stream, mib=2048):

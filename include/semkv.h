@@ -158,6 +158,27 @@ semkv_status semkv_score_keynorm(const uint16_t* k, const int64_t strides[4], in
                                  int32_t kv_heads, int64_t n, int32_t layer0, int32_t nlayers,
                                  float* scores, int64_t ld_scores, void* stream);
 
+/* Hidden-state delta-norm token scores, the pages' default indicator (SemKV
+ * Table 2: hidden-state delta norm over the last 4 layers; Fig. 10: O(1) per
+ * token; the formula is not given there, and the reading here is the sum of
+ * the Euclidean norms of the last layers' updates to the token's hidden state):
+ *   scores[b * ld_scores + t] = sum_{j=1..nstates-1} ||h_j[t] - h_{j-1}[t]||_2
+ * where h_0 .. h_{nstates-1} are the hidden states entering and leaving those
+ * layers (nstates = 5 for the last 4 layers).  Each update is formed in fp32
+ * from the fp16 states and its squares are summed in fp32.  The result feeds
+ * semkv_rank_topr.
+ *  h        fp16 hidden states; element (b, state, token, k) is at
+ *           h + b*strides[0] + state*strides[1] + token*strides[2] + k
+ *           (strides in elements, k contiguous), k < d_model
+ *  scores   fp32 [batch][ld_scores] device memory, first n of each row written
+ * Errors: EINVAL (null or misaligned pointers: h 16-byte, scores 4-byte;
+ * strides negative or not multiples of 8; batch outside [1, 65535]; nstates
+ * outside [2, 9]; d_model not a multiple of 8 in [8, 65536]; n < 1;
+ * ld_scores < n). */
+semkv_status semkv_score_hidden_delta(const uint16_t* h, const int64_t strides[3], int32_t batch,
+                                      int32_t nstates, int64_t n, int32_t d_model, float* scores,
+                                      int64_t ld_scores, void* stream);
+
 /* Quantize and pack a prompt (SemKV Fig. 5 and Table 6).
  *  k, v     fp16 rows; element (b, layer, head, token, d) is at
  *           base + b*strides[0] + layer*strides[1] + head*strides[2]

@@ -295,6 +295,29 @@ semkv_status semkv_score_keynorm(const uint16_t* k, const int64_t strides[4], in
   return from_hip(launch_score_keynorm(a, batch, (hipStream_t)stream));
 }
 
+semkv_status semkv_score_hidden_delta(const uint16_t* h, const int64_t strides[3], int32_t batch,
+                                      int32_t nstates, int64_t n, int32_t d_model, float* scores,
+                                      int64_t ld_scores, void* stream) {
+  if (!h || !aligned(h, 16) || !strides) return SEMKV_EINVAL;
+  for (int i = 0; i < 3; ++i)
+    if (strides[i] < 0 || strides[i] % 8 != 0) return SEMKV_EINVAL;
+  if (batch < 1 || batch > 65535 || nstates < 2 || nstates > 9) return SEMKV_EINVAL;
+  if (d_model < 8 || d_model > 65536 || d_model % 8 != 0) return SEMKV_EINVAL;
+  if (n < 1 || n > (int64_t)INT32_MAX * 4 || !scores || !aligned(scores, 4) || ld_scores < n)
+    return SEMKV_EINVAL;
+  DeltaArgs a;
+  a.h = h;
+  a.sb = strides[0];
+  a.ss = strides[1];
+  a.st = strides[2];
+  a.n = n;
+  a.S = nstates - 1;
+  a.d = d_model;
+  a.scores = scores;
+  a.ld = ld_scores;
+  return from_hip(launch_score_hidden_delta(a, batch, (hipStream_t)stream));
+}
+
 semkv_status semkv_quantize_pack(semkv_cache* c, const uint16_t* k, const uint16_t* v,
                                  const int64_t strides[4], int64_t n, const int32_t* perm,
                                  int64_t k_high, void* stream) {

@@ -18,6 +18,18 @@ struct ScoreArgs {
 };
 hipError_t launch_score_keynorm(const ScoreArgs& a, int batch, hipStream_t stream);
 
+// Hidden-state delta norms: scores[b * ld + t] = sum_{j=1..S} ||h_j - h_{j-1}||
+// of token t, h_j at h + b * sb + j * ss + t * st (d contiguous fp16 values).
+struct DeltaArgs {
+  const uint16_t* h;
+  int64_t sb, ss, st;       // element strides: batch, state, token
+  int64_t n;
+  int32_t S, d;             // layers (states - 1), hidden size
+  float* scores;
+  int64_t ld;
+};
+hipError_t launch_score_hidden_delta(const DeltaArgs& a, int batch, hipStream_t stream);
+
 // ---------------------------------------------------------------- ragged batches
 // Per-sequence counters in device memory, kSeqWords int64 per sequence.
 constexpr int kSeqWords = 8;

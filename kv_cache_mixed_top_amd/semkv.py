@@ -49,6 +49,8 @@ _SIGS = {
     "semkv_workspace_bytes": (c_i64, [ctypes.POINTER(semkv_geom), c_i32, c_i64]),
     "semkv_score_keynorm": (c_i32, [c_p, ctypes.POINTER(c_i64), c_i32, c_i32, c_i64, c_i32, c_i32,
                                     c_p, c_i64, c_p]),
+    "semkv_score_hidden_delta": (c_i32, [c_p, ctypes.POINTER(c_i64), c_i32, c_i32, c_i64, c_i32,
+                                         c_p, c_i64, c_p]),
     "semkv_rank_topr": (c_i32, [c_p, c_i32, c_i64, c_i64, c_i64, c_p, c_p, c_p]),
     "semkv_quantize_pack": (c_i32, [ctypes.POINTER(semkv_cache), c_p, c_p,
                                     ctypes.POINTER(c_i64), c_i64, c_p, c_i64, c_p]),
@@ -177,6 +179,22 @@ def semkv_score_keynorm(K, scores, layer0, nlayers, stream=None):
            _lib.semkv_score_keynorm(_ptr(K), strides, K.shape[0], K.shape[2], K.shape[3],
                                     layer0, nlayers, _ptr(scores), scores.stride(0),
                                     _stream(stream)))
+
+
+def semkv_score_hidden_delta(H, scores, stream=None):
+    """H fp16 [B][states][n][d] (d contiguous, other strides multiples of 8);
+    scores fp32 [B][>= n] out: sum over consecutive states of ||h_j - h_{j-1}||."""
+    if H.dtype != torch.float16 or H.dim() != 4 or H.stride(3) != 1:
+        raise ValueError("H must be fp16 [B][states][n][d] with d contiguous")
+    B, S1, n, d = H.shape
+    if (scores.dtype != torch.float32 or scores.dim() != 2 or scores.shape[0] != B
+            or scores.shape[1] < n or scores.stride(1) != 1):
+        raise ValueError("scores must be fp32 [B][>= n] with unit stride")
+    strides = (c_i64 * 3)(H.stride(0), H.stride(1), H.stride(2))
+    _on_device(H, scores)
+    _check("semkv_score_hidden_delta",
+           _lib.semkv_score_hidden_delta(_ptr(H), strides, B, S1, n, d, _ptr(scores), scores.stride(0),
+                                         _stream(stream)))
 
 
 def semkv_rank_topr(scores, k, perm, mask=None, n=None, stream=None):

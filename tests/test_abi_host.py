@@ -278,3 +278,20 @@ def test_ragged_validation_before_launch():
     assert r(p, 2, 100, 100, None, 0.5, p, None, None) == E                    # null n_seq
     assert sk._lib.semkv_seq_reset(None, 2, None) == E
     assert sk._lib.semkv_seq_reset(seq, 0, None) == E
+
+
+def test_score_hidden_delta_validation_before_launch():
+    f = sk._lib.semkv_score_hidden_delta
+    p = ctypes.c_void_p(0x200000)
+    st = (ctypes.c_int64 * 3)(5 * 1000 * 4096, 1000 * 4096, 4096)
+    E = sk.SEMKV_EINVAL
+    assert f(None, st, 1, 5, 1000, 4096, p, 1000, None) == E               # null h
+    assert f(ctypes.c_void_p(0x200008), st, 1, 5, 1000, 4096, p, 1000, None) == E   # misaligned h
+    assert f(p, st, 1, 1, 1000, 4096, p, 1000, None) == E                  # one state: no update
+    assert f(p, st, 1, 10, 1000, 4096, p, 1000, None) == E                 # more than 8 layers
+    assert f(p, st, 1, 5, 1000, 4100, p, 1000, None) == E                  # d not a multiple of 8
+    assert f(p, st, 1, 5, 1000, 4096, p, 999, None) == E                   # ld < n
+    assert f(p, st, 0, 5, 1000, 4096, p, 1000, None) == E                  # batch
+    bad = (ctypes.c_int64 * 3)(*st)
+    bad[2] = 100
+    assert f(p, bad, 1, 5, 1000, 4096, p, 1000, None) == E                 # stride not a multiple of 8

@@ -115,3 +115,58 @@ def test_score_keynorm_full_size_sampled():
     ref = O.score_keynorm(rows, 0, 4)
     _check(scores.cpu().numpy()[:, idx], ref, 4, kv, "full size")
     del K
+
+
+# ---------------------------------------------------------------- hidden-state delta norm
+# Tolerance: each update h_j - h_{j-1} is formed in fp32 from two fp16 values
+# (relative error <= 2^-24), its square adds one more; lane l sums its
+# ceil(d / 512) * 8 squares in order and the wave adds the 64 lane sums in 6
+# rounds, so each layer's sum of squares is within (ceil(d/512)*8 + 6 + 3) *
+# 2^-24 relative (all terms are non-negative); the square root halves that
+# and adds 2^-24, and the S norms are summed with S - 1 roundings.  The test
+# allows twice that bound.
+
+def _delta_tol(d, S):
+    return 2 * ((-(-d // 512) * 8 + 9) / 2 + 1 + S) * 2.0 ** -24
+
+
+@pytest.mark.parametrize("d", [64, 1000, 4096])
+@pytest.mark.parametrize("states", [2, 5, 9])
+def test_score_hidden_delta(d, states):
+    _print("score hidden delta", d, states)
+    rng = np.random.default_rng(d + states)
+    B, n = 2, 300
+    h0 = rng.standard_normal((B, 1, n, d))
+    steps = rng.standard_normal((B, states - 1, n, d)) * rng.uniform(0.01, 0.5, size=(B, 1, n, 1))
+    H = np.concatenate([h0, h0 + np.cumsum(steps, axis=1)], axis=1).astype(np.float16)
+    scores = torch.full((B, n + 5), -1.0, dtype=torch.float32, device="cuda")
+    sk.semkv_score_hidden_delta(to_dev(H), scores)
+    sk.semkv_sync_check()
+    got = scores.cpu().numpy()
+    ref = O.score_hidden_delta(H)
+    rel = np.abs(got[:, :n].astype(np.float64) - ref) / ref
+    assert float(rel.max()) <= _delta_tol(d, states - 1), f"max rel {rel.max():.3e}"
+    assert np.all(got[:, n:] == -1.0)                         # nothing past n
+
+
+def test_score_hidden_delta_strided_and_rank():
+    """States as a strided view (token-major storage), then the rank of the
+    GPU scores equals the oracle's rank of those same scores, bit for bit."""
+    _print("score hidden delta strided + rank")
+    rng = np.random.default_rng(5)
+    B, S1, n, d = 2, 5, 777, 256
+    base = rng.standard_normal((B, n, S1, d)).astype(np.float16)     # token-major
+    Hv = to_dev(base).permute(0, 2, 1, 3)                           # [B][S1][n][d] view
+    scores = torch.empty((B, n), dtype=torch.float32, device="cuda")
+    sk.semkv_score_hidden_delta(Hv, scores)
+    sk.semkv_sync_check()
+    got = scores.cpu().numpy()
+    ref = O.score_hidden_delta(np.moveaxis(base, 1, 2))
+    rel = np.abs(got.astype(np.float64) - ref) / ref
+    assert float(rel.max()) <= _delta_tol(d, S1 - 1)
+    k = O.topr_count(n, 0.25)
+    perm = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    sk.semkv_rank_topr(scores, k, perm)
+    sk.semkv_sync_check()
+    want, _ = O.rank_topr_batch(got, k)
+    assert np.array_equal(perm.cpu().numpy(), want)

@@ -148,6 +148,28 @@ def make_gen_tokens_np(w: Workload, steps: int, seed: int = 1, chans=None):
 
 # ---------------------------------------------------------------- torch (GPU)
 
+HIDDEN_SIZE = 4096    # residual width of the pages' backbones (Llama-3.1-8B, Mistral-7B)
+
+
+def make_hidden_states_torch(w: Workload, device, states: int = 5, d_model: int = HIDDEN_SIZE,
+                             seed: int = 0):
+    """Synthetic hidden states fp16 [B][states][n][d_model] for the delta-norm
+    score: h_0 ~ N(0, 1), then each layer adds an update N(0, 1) * sigma_t with
+    a per-token scale sigma_t ~ U(0.05, 0.5) drawn once per token (so the
+    tokens' scores spread), in a seeded torch generator on `device`."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed + 11)
+    H = torch.empty((w.batch, states, w.n, d_model), dtype=torch.float16, device=device)
+    sigma = 0.05 + 0.45 * torch.rand((w.batch, w.n, 1), generator=g, device=device)
+    h = torch.randn((w.batch, w.n, d_model), generator=g, device=device)
+    H[:, 0] = h.half()
+    for j in range(1, states):
+        h = h + torch.randn((w.batch, w.n, d_model), generator=g, device=device) * sigma
+        H[:, j] = h.half()
+    return H
+
+
 def make_kv_torch(w: Workload, device, seed: int = 0):
     """K, V fp16 [B][layers][kv][n][128] drawn on `device` (large workloads).
 
