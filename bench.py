@@ -292,6 +292,12 @@ def main():
                 f"decode partials {m['partials_us']} us ({m['partials_pct_hbm_peak']}%)")
             torch.cuda.empty_cache()
             torch.cuda.empty_cache()
+        m = strip_private(workload_leg(sk, W, torch, dev, stream, "mix43_r075"))
+        m.update(mix_accounting(sk, W.WORKLOADS["mix43_r075"]))
+        result["mix43_r075"] = m
+        log(f"mix43_r075: quantize {m['quantize_ms']} ms ({m['quantize_pct_hbm_peak']}%), "
+            f"decode partials {m['partials_us']} us ({m['partials_pct_hbm_peak']}%)")
+        torch.cuda.empty_cache()
         if not args.no_cliff:
             result["cliff_4x32k"] = cliff_leg(sk, W, torch, dev, stream)
             torch.cuda.empty_cache()
@@ -551,6 +557,29 @@ def workload_leg(sk, W, torch, dev, stream, name, levels=None, r=None, inputs=No
     res["_out"] = out
     res["_perm"] = perm
     return res
+
+
+def mix_accounting(sk, w):
+    """Storage accounting of a two-level mix: the nominal bits (log2 of the
+    level counts), this format's stored bits (packed rows + 4 meta bytes per
+    128 values), and the pages' accounting (SemKV Table 6: code bits of
+    packing g codes in ceil(g log2 L) bits at the best g <= 5, plus the
+    metadata per value: two fp16 scalars per row for the affine base, one
+    for TurboQuant-MSE), each with its compression against fp16."""
+    import math
+    n, Lh, Ll = w.n, w.L_high, w.L_low
+    k = sk.semkv_topr_count(n, w.r)
+    nominal = (k * math.log2(Lh) + (n - k) * math.log2(Ll)) / n
+    stored = (k * (sk.semkv_row_bytes(Lh) + 4) + (n - k) * (sk.semkv_row_bytes(Ll) + 4)) * 8 / (128 * n)
+    page_code = lambda L: min(math.ceil(g * math.log2(L) - 1e-12) / g for g in range(1, 6))
+    code = (k * page_code(Lh) + (n - k) * page_code(Ll)) / n
+    return {"nominal_bits": round(nominal, 4), "stored_bits": round(stored, 4),
+            "compression_vs_fp16": round(16 / stored, 3),
+            "page_code_bits": round(code, 4),
+            "page_eff_bits_affine": round(code + 0.25, 4),
+            "page_compression_affine": round(16 / (code + 0.25), 3),
+            "page_eff_bits_turboquant": round(code + 0.125, 4),
+            "page_compression_turboquant": round(16 / (code + 0.125), 3)}
 
 
 def cliff_leg(sk, W, torch, dev, stream):

@@ -122,6 +122,34 @@ def test_llama8b_32k_full():
     _print(f"llama8b_32k: worst decode error {worst:.3e}")
 
 
+def test_mix43_r075_sampled():
+    """The (4,3) mix at r = 0.75 (SemKV Fig. 18's operating point, affine base)
+    at the 8B 32k shape: full rank, sampled planes bit-exact, decode of
+    sampled KV-head groups at the first and last of two steps."""
+    w = W.WORKLOADS["mix43_r075"]
+    _print("mix43_r075: inputs")
+    K, V, scores = _inputs(w)
+    n, k = w.n, sk.semkv_topr_count(w.n, w.r)
+    perm, wp = _rank_full(scores, k)
+    cache = sk.SemKVCache(w.batch, w.layers, w.kv_heads, w.q_heads, 4, 3, cap16(k), cap16(n - k),
+                          block=w.block, max_tokens=n)
+    sk.semkv_quantize_pack(cache, K, V, perm, k)
+    q = W.make_q_torch(w, 2, DEV)
+    outs = []
+    for j in range(2):
+        out = torch.empty((w.batch, w.layers, w.q_heads, 128), dtype=torch.float32, device=DEV)
+        sk.semkv_decode_attn(cache, q[j], out, sm_scale=w.sm_scale)
+        outs.append(out)
+    sk.semkv_sync_check()
+    for layer, head in ((0, 0), (31, 7), (13, 4)):
+        _print(f"mix43_r075: plane layer {layer} head {head}")
+        op = _check_plane(cache, K, V, wp, k, 4, 3, 0, layer, head)
+        for j in range(2):
+            e = _decode_group(op, q[j], 0, layer, head, w.q_heads // w.kv_heads, w.sm_scale,
+                              outs[j].cpu().numpy(), f"step {j} layer {layer} head {head}")
+            _print(f"   decode error {e:.3e}")
+
+
 def test_mistral7b_128k_sampled():
     """131,072 tokens, heavy-tailed (Student-t) V, r = 0.5."""
     w = W.WORKLOADS["mistral7b_128k"]

@@ -55,6 +55,10 @@ WORKLOADS = {
     # Mistral-7B-shaped 128k context, heavy-tailed V
     "mistral7b_128k": Workload("mistral7b_128k", 1, 32, 8, 32, 131072, 0.5, 6, 5, 128,
                                v_dist="student_t4", score="attn_mass"),
+    # the pages' lowest no-detectable-loss point (Fig. 18: 4 and 3 levels at
+    # r = 75%, code 1.9 bits) on the affine base, at the 8B 32k shape
+    "mix43_r075": Workload("mix43_r075", 1, 32, 8, 32, 32768, 0.75, 4, 3, 256,
+                           score="attn_mass"),
     # cliff-grid sweep base shape (levels and r vary per setting)
     "cliff_4x32k": Workload("cliff_4x32k", 4, 32, 8, 32, 32768, 0.25, 6, 5, 64,
                             score="attn_mass"),
