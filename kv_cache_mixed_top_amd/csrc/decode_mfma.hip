@@ -9,18 +9,18 @@ namespace {
 
 // Level pairs (high, low) with a matrix-core kernel; a pool with no rows
 // takes the other pool's level count.  Pairs with 16 levels and the rest of
-// the 3-level pairs are instantiated in decode_mfma_wide.hip.
+// the 3- and 8-level pairs are instantiated in decode_mfma_wide.hip.
 template <bool kRot>
 hipError_t launch_pair(int LA, int LB, dim3 grid, const DecodeArgs& a, hipStream_t stream) {
 #define SEMKV_PAIR(X, Y) \
   if (LA == X && LB == Y) return launch_mfma<X, Y, kRot>(grid, a, stream);
   SEMKV_PAIR(6, 5) SEMKV_PAIR(6, 6) SEMKV_PAIR(5, 5) SEMKV_PAIR(5, 4) SEMKV_PAIR(4, 4)
-  SEMKV_PAIR(6, 4) SEMKV_PAIR(4, 3) SEMKV_PAIR(3, 3)
+  SEMKV_PAIR(6, 4) SEMKV_PAIR(4, 3) SEMKV_PAIR(3, 3) SEMKV_PAIR(8, 8) SEMKV_PAIR(8, 6)
 #undef SEMKV_PAIR
   return launch_decode_mfma_wide(LA, LB, kRot, grid, a, stream);
 }
 
-bool fast_level(int L) { return L == 3 || L == 4 || L == 5 || L == 6 || L == 16; }
+bool fast_level(int L) { return L == 3 || L == 4 || L == 5 || L == 6 || L == 8 || L == 16; }
 
 void effective_pair(const DecodeArgs& a, int& LA, int& LB) {
   LA = a.fmt[0].L;

@@ -2,7 +2,7 @@
 // Device code of the matrix-core decode (see decode_mfma.hip for the
 // launchers): included by the translation units that instantiate its
 // level pairs, each of which gets its own copy (internal linkage).
-// Matrix-core decode attention over pools of 3-, 4-, 5-, 6- and 16-level rows
+// Matrix-core decode attention over pools of 3-, 4-, 5-, 6-, 8- and 16-level rows
 // (the SemKV page's mixed-precision cache, Fig. 1 and Table 2: one level
 // count per token, the operating pair b_high/b_low = log2 6 / log2 5; the
 // cliff study of Fig. 3 adds the neighbouring level counts, and Fig. 18's
@@ -57,6 +57,9 @@ constexpr float kWeightLimit = 1073741824.0f;   // 2^30: fixed-point weights sta
 // (nibbles) for 16.
 template <int L> struct Lv;
 template <> struct Lv<3> { static constexpr int R = 26, NM = 5, PS = 2, PF = 5, G = 5; };
+// 8 levels: the 3-bit codes are taken in pairs, a "super-field" F = c0 + 8 c1
+// of 6 bits (64 per row), with the features F and floor(F / 8).
+template <> struct Lv<8> { static constexpr int R = 48, NM = 4, PS = 4, PF = 2, G = 2; };
 template <> struct Lv<6> { static constexpr int R = 43, NM = 4, PS = 3, PF = 3, G = 3; };
 template <> struct Lv<5> { static constexpr int R = 38, NM = 5, PS = 3, PF = 3, G = 3; };
 template <> struct Lv<4> { static constexpr int R = 32, NM = 2, PS = 2, PF = 4, G = 4; };
@@ -76,9 +79,11 @@ __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel)
 // for the floors of floors.
 constexpr uint32_t kBias = 0x66666666u;   // perm source of the 0x66 high bytes
 template <int L> constexpr float floor_m() {
-  return L == 6 ? 0.1663818359375f : L == 5 ? 0.1995849609375f : 0.33251953125f;
+  return L == 6 ? 0.1663818359375f : L == 5 ? 0.1995849609375f : L == 8 ? 0.12469482421875f : 0.33251953125f;
 }
-template <int L> constexpr float floor_k() { return L == 6 ? 1280.0f : L == 5 ? 1229.0f : 1025.0f; }
+template <int L> constexpr float floor_k() {
+  return L == 6 ? 1280.0f : L == 5 ? 1229.0f : L == 8 ? 1344.0f : 1025.0f;
+}
 
 template <int L>
 __device__ __forceinline__ uint32_t floor_slots(uint32_t x) {   // 1536 + x -> 1536 + floor(x / L)
@@ -98,6 +103,16 @@ __device__ __forceinline__ void field_pairs(uint32_t W, uint32_t& pa, uint32_t& 
   pa = (h & 0x007F007Fu) | bias;                                       // (F0, F2)
   const u16x2 seven = {7, 7};
   pb = (u32(v2(h) >> seven) & 0x007F007Fu) | bias;                     // (F1, F3)
+}
+// ---- 8 levels: 4 six-bit super-fields in 24 bits of W, at bits 0, 6, 12,
+// 18: slots (F0, F2) from the halves (W[0:15], W[12:27]), (F1, F3) six bits
+// higher.
+__device__ __forceinline__ void field_pairs6(uint32_t W, uint32_t& pa, uint32_t& pb,
+                                             uint32_t bias) {
+  const uint32_t h = perm(W >> 12, W, 0x05040100u);
+  pa = (h & 0x003F003Fu) | bias;                                       // (F0, F2)
+  const u16x2 six = {6, 6};
+  pb = (u32(v2(h) >> six) & 0x003F003Fu) | bias;                       // (F1, F3)
 }
 // 0x66006600 in a vector register (the compiler cannot fold it back into a
 // literal, which these instructions cannot take together with a mask).
@@ -264,7 +279,7 @@ struct QCoef { uint32_t c[4][kCoefSlots]; };           // limb bytes of the coef
 
 // index of the coefficient of feature `type` of field slot `slot`
 template <int L> __device__ __forceinline__ int coef_index(int type, int slot) {
-  return L == 4 || L == 3 ? type * 32 + slot : L == 16 ? type * 64 + slot : type * 48 + slot;
+  return L == 4 || L == 3 ? type * 32 + slot : L == 16 || L == 8 ? type * 64 + slot : type * 48 + slot;
 }
 
 template <int L, bool kRot>
@@ -284,12 +299,12 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   const uint8_t* vcodes = kcodes + cap * R;
   const uint32_t* kmg = a.meta[seg] + plane_k * cap;
   const uint32_t* vmg = kmg + cap;
-  const uint32_t bias5 = L == 5 ? bias_register() : 0u;   // 5-level field bias
+  const uint32_t bias5 = L == 5 || L == 8 ? bias_register() : 0u;   // 5-level field bias
   const int ntiles = (ir1 - ir0 + kTile - 1) / kTile;
 
   // byte offset and bit shift of this lane's window within a row, and the
   // offset of set s's window within a tile
-  const int kbyte = L == 6 ? 12 * kg : L == 5 ? (77 * kg) >> 3 : L == 4 || L == 3 ? 8 * kg : 16 * kg;
+  const int kbyte = L == 6 || L == 8 ? 12 * kg : L == 5 ? (77 * kg) >> 3 : L == 4 || L == 3 ? 8 * kg : 16 * kg;
   const int kbit = L == 5 ? (77 * kg) & 7 : 0;
   int koff[4];
 #pragma unroll
@@ -389,7 +404,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   // coefficient limbs per (head, feature type, field slot).  5 and 6 levels:
   // slot kgs * 12 + j is field 12 kgs + j (6 levels) or 11 kgs + j for j < 11
   // (5 levels), fields past 42 are 0; 4 and 16 levels: the digit's dimension.
-  constexpr int kSlots = L == 4 || L == 3 ? 32 : L == 16 ? 64 : 48;
+  constexpr int kSlots = L == 4 || L == 3 ? 32 : L == 16 || L == 8 ? 64 : 48;
 #pragma unroll
   for (int p = 0; p < (4 * kSlots) / 64; ++p) {
     const int idx = lane + 64 * p;                 // (head, slot)
@@ -414,6 +429,12 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
       for (int i = 0; i < 5; ++i)
         qc.c[h][coef_index<3>(i, slot)] = slot < 26 ? limb_bytes(i == 0 ? qf[0] : qf[i] - 3 * qf[i - 1]) : 0u;
+    } else if constexpr (L == 8) {
+      // super-field m = codes 2m, 2m+1: coefficient of F is q_2m, of
+      // floor(F / 8) is q_2m+1 - 8 q_2m
+      const int qa = qi.q[h][2 * slot], qb = qi.q[h][2 * slot + 1];
+      qc.c[h][coef_index<8>(0, slot)] = limb_bytes(qa);
+      qc.c[h][coef_index<8>(1, slot)] = limb_bytes(qb - 8 * qa);
     } else {
 #pragma unroll
       for (int i = 0; i < Lv<L>::G; ++i)
@@ -467,6 +488,17 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
         w[6 * gi + 5] = perm(c2.w, c2.y, sel_pair);
       }
       w[18] = w[19] = 0;
+    } else if constexpr (L == 8) {
+      // per group of 4 super-fields (16 kg + 4 gi ..): slots of F for (0, 2),
+      // (1, 3), then of floor(F / 8) for the same
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const uint4 c0 = row(0, 16 * kg + 4 * gi), c1 = row(1, 16 * kg + 4 * gi);
+        w[4 * gi + 0] = perm(c0.z, c0.x, sel_pair);
+        w[4 * gi + 1] = perm(c0.w, c0.y, sel_pair);
+        w[4 * gi + 2] = perm(c1.z, c1.x, sel_pair);
+        w[4 * gi + 3] = perm(c1.w, c1.y, sel_pair);
+      }
     } else if constexpr (L == 3) {
       // f of fields 8kg .. 8kg+7 (XORed bytes), then F_1 .. F_4 as slots:
       // (fields 0, 2), (1, 3), (4, 6), (5, 7) of the window
@@ -559,6 +591,20 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
           w[6 * gi + 5] = floor_slots<5>(b1);
         }
         w[18] = w[19] = 0;
+      } else if constexpr (L == 8) {
+        // bytes 12 kg .. 12 kg + 11 of the row (4-byte aligned): super-fields
+        // 16 kg .. 16 kg + 15 in four 24-bit groups
+        const uint32_t Gw[4] = {x0, __builtin_amdgcn_alignbit(x1, x0, 24), __builtin_amdgcn_alignbit(x2, x1, 16),
+                                x2 >> 8};
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          uint32_t pa, pb;
+          field_pairs6(Gw[gi], pa, pb, bias5);
+          w[4 * gi + 0] = pa;
+          w[4 * gi + 1] = pb;
+          w[4 * gi + 2] = floor_slots<8>(pa);
+          w[4 * gi + 3] = floor_slots<8>(pb);
+        }
       } else if constexpr (L == 3) {
         const int sh = koff[s] & 3;
         const uint32_t d[2] = {__builtin_amdgcn_alignbyte(x1, x0, sh), __builtin_amdgcn_alignbyte(x2, x1, sh)};
@@ -698,7 +744,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;   // C: head grp; A/B: k-group grp
   const int ntiles = ((int)r1 - (int)r0 + kTile - 1) / kTile;
-  const uint32_t bias5 = L == 5 ? bias_register() : 0u;
+  const uint32_t bias5 = L == 5 || L == 8 ? bias_register() : 0u;
 
   i4 acc[NMP];
   float T[NMP];                 // digit sums so far, against the current frame
@@ -730,6 +776,9 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
         d[0] = f0 - L * vv[s * PF + 1];
         d[1] = vv[s * PF + 1] - L * vv[s * PF + 2];
         d[2] = vv[s * PF + 2];
+      } else if constexpr (L == 8) {
+        d[0] = vv[s * PF] - 8 * vv[s * PF + 1];
+        d[1] = vv[s * PF + 1];
       } else if constexpr (L == 3) {
         d[0] = vv[s * PF] + 128 * Wsum - 3 * vv[s * PF + 1];
 #pragma unroll
@@ -791,6 +840,23 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
           f[0][q] = perm(p23, p01, 0x06040200u);
           f[1][q] = perm(c1, a1, 0x06040200u);
           f[2][q] = perm(floor_slots<5>(c1), floor_slots<5>(a1), 0x06040200u);
+        }
+      } else if constexpr (L == 8) {
+        // super-field j: bits 6j .. 6j+5 of the row, in byte planes
+        // floor(6j/8) and the next (not read past the row: the bits above
+        // the field are masked off)
+        const int bit = 6 * j;
+        const int j0 = bit >> 3;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(vb + 16 * j0);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(vb + 16 * min(j0 + 1, R - 1));
+        const uint32_t b0[4] = {x0.x, x0.y, x0.z, x0.w}, b1[4] = {x1.x, x1.y, x1.z, x1.w};
+        const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t p01 = (u32(v2(perm(b1[q], b0[q], 0x05010400u)) >> shv) & 0x003F003Fu) | bias5;
+          const uint32_t p23 = (u32(v2(perm(b1[q], b0[q], 0x07030602u)) >> shv) & 0x003F003Fu) | bias5;
+          f[0][q] = perm(p23, p01, 0x06040200u);
+          f[1][q] = perm(floor_slots<8>(p23), floor_slots<8>(p01), 0x06040200u);
         }
       } else if constexpr (L == 3) {
         const uint4 x = *reinterpret_cast<const uint4*>(vb + 16 * j);

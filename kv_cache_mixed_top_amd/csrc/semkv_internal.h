@@ -143,7 +143,7 @@ hipError_t launch_decode_partials(const DecodeArgs& a, hipStream_t stream);
 // Generic kernel over chunks [a.x0, a.x0 + count).
 hipError_t launch_decode_generic(const DecodeArgs& a, int count, hipStream_t stream);
 // Matrix-core kernel for the pool chunks [0, nch[0] + nch[1]) when both pool
-// level counts are among 3, 4, 5, 6 and 16 and the query group is 4.
+// level counts are among 3, 4, 5, 6, 8 and 16 and the query group is 4.
 bool decode_mfma_supported(const DecodeArgs& a);
 // The matrix-core kernel will run for these arguments.
 bool decode_use_mfma(const DecodeArgs& a);
@@ -152,7 +152,8 @@ bool decode_use_mfma(const DecodeArgs& a);
 int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units);
 int64_t decode_mfma_resident_waves();
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
-// The matrix-core kernels of the pairs with 16 levels and of (6,3), (5,3).
+// The matrix-core kernels of the pairs with 16 levels, of (6,3), (5,3) and
+// of the 8-level pairs other than (8,8), (8,6).
 hipError_t launch_decode_mfma_wide(int LA, int LB, bool rot, dim3 grid, const DecodeArgs& a,
                                    hipStream_t stream);
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream);

@@ -38,7 +38,7 @@ def _rne_int(v: Fraction) -> int:
     return fl if fl % 2 == 0 else fl + 1
 
 
-@pytest.mark.parametrize("L,xmax", [(6, 216), (5, 125), (3, 243)])
+@pytest.mark.parametrize("L,xmax", [(6, 216), (5, 125), (3, 243), (8, 64)])
 def test_floor_by_fma(L, xmax):
     mt, kt = _constants()
     m = mt.get(L, mt[None])

@@ -419,7 +419,7 @@ def test_checkpoint_roundtrip():
 
 
 # ------------------------------------------------------------------ matrix-core decode path
-# Pools of 3, 4, 5, 6 and 16 levels (any pair with L_high >= L_low) with 4 query
+# Pools of 3, 4, 5, 6, 8 and 16 levels (any pair with L_high >= L_low) with 4 query
 # heads per KV head take the MFMA kernel; these cases cover several 64-row
 # tiles per chunk, ragged last tiles, empty pools, constant / tiny / wide rows
 # and heavy-tailed V.
@@ -452,7 +452,7 @@ def test_decode_mfma_shapes(n, r, kind):
                                f"mfma n={n} r={r} {kind} sm={sm}")
 
 
-@pytest.mark.parametrize("L", [3, 4, 5, 6, 16])
+@pytest.mark.parametrize("L", [3, 4, 5, 6, 8, 16])
 def test_decode_mfma_uniform_levels(L):
     _print("decode mfma uniform", L)
     rng = np.random.default_rng(L)
@@ -486,7 +486,8 @@ def test_decode_mfma_large_logits():
 
 
 @pytest.mark.parametrize("Lh,Ll", [(5, 4), (6, 4), (6, 6), (5, 5), (16, 16), (16, 6), (16, 5), (16, 4),
-                                   (4, 3), (3, 3), (5, 3), (6, 3), (16, 3)])
+                                   (4, 3), (3, 3), (5, 3), (6, 3), (16, 3), (8, 6), (8, 8), (16, 8),
+                                   (8, 5), (8, 4), (8, 3)])
 @pytest.mark.parametrize("kind", ["normal", "mixed", "studentt"])
 def test_decode_mfma_level_pairs(Lh, Ll, kind):
     """Every level pair of the matrix-core kernel, on several tiles with a
