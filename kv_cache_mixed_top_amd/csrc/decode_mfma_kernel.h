@@ -549,9 +549,18 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     const uint32_t kmw[4] = {km.x, km.y, km.z, km.w};
     const uint32_t vmw[4] = {vm.x, vm.y, vm.z, vm.w};
     float zz[4];
+    i4 accp;
+    // limb sums of head kg -> the integer dot product in fp32 -> the logit
+    // (log2 units) with the row's K scale and minimum
+    auto logit = [&](i4 c, uint32_t km) {
+      const int32_t tlo = (c[1] << 8) + c[0];
+      const int32_t thi = (c[3] << 8) + c[2];
+      const float zf = fmaf((float)thi, 65536.0f, (float)tlo);
+      const h2 sm = __builtin_bit_cast(h2, km);          // {scale, min}
+      return fmaf((float)sm[0], cA * zf, (float)sm[1] * cB);
+    };
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int t = 4 * n + s;
       const uint32_t x0 = kx[S][s].x, x1 = kx[S][s].y, x2 = kx[S][s].z, x3 = kx[S][s].w;
       uint32_t w[4 * NM];
       if constexpr (L == 6) {
@@ -640,14 +649,16 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
       for (int m = 0; m < NM; ++m)
         acc = mfma_i8(A[m], as_i4(w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]), acc);
-      // limb sums of head kg -> the integer dot product in fp32
-      const int32_t tlo = (acc[1] << 8) + acc[0];
-      const int32_t thi = (acc[3] << 8) + acc[2];
-      const float zf = fmaf((float)thi, 65536.0f, (float)tlo);
-      const float sK = h2f((uint16_t)(kmw[s] & 0xFFFFu));
-      const float mK = h2f((uint16_t)(kmw[s] >> 16));
-      zz[s] = t < nt ? fmaf(sK * cA, zf, mK * cB) : -INFINITY;   // rows past the chunk: no weight
+      // the logits of the previous set are formed while this set's products
+      // run on the matrix core
+      if (s > 0) zz[s - 1] = logit(accp, kmw[s - 1]);
+      accp = acc;
       __builtin_amdgcn_sched_barrier(0);   // one set's temporaries live at a time
+    }
+    zz[3] = logit(accp, kmw[3]);
+    if (nt < kTile) {                      // rows past the chunk: no weight
+#pragma unroll
+      for (int s = 0; s < 4; ++s) zz[s] = 4 * n + s < nt ? zz[s] : -INFINITY;
     }
     // softmax frame of head kg, kFrameMargin above the running maximum; it is
     // raised only when a logit exceeds it (in practice on the first tile),
@@ -664,13 +675,12 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     float wv[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const bool in = 4 * n + s < nt;
       const float p = __builtin_amdgcn_exp2f(zz[s] - frame);   // 0 past the chunk
-      const float vs = in ? h2f((uint16_t)(vmw[s] & 0xFFFFu)) : 0.0f;
-      const float vmin = in ? h2f((uint16_t)(vmw[s] >> 16)) : 0.0f;
+      // past the chunk the meta word may be anything: take {0, 0}
+      const h2 sm = __builtin_bit_cast(h2, 4 * n + s < nt ? vmw[s] : 0u);   // {scale, min}
       lsum += p;
-      msum = fmaf(p, vmin, msum);
-      wv[s] = p * vs * two_g;
+      msum = fmaf(p, (float)sm[1], msum);
+      wv[s] = (float)sm[0] * (p * two_g);
     }
     // fixed-point exponent of head kg: set from the first nonzero weights to
     // put the largest at 2^28 .. 2^29, lowered when a weight reaches 2^30
@@ -691,8 +701,10 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     }
     // limbs of the 4 tokens, transposed to one dword per limb (tokens 4n ..
     // 4n+3 in byte order) -> [head kg][limb][n]
-    const uint32_t W0 = limb_bytes((int32_t)rintf(wv[0])), W1 = limb_bytes((int32_t)rintf(wv[1]));
-    const uint32_t W2 = limb_bytes((int32_t)rintf(wv[2])), W3 = limb_bytes((int32_t)rintf(wv[3]));
+    // (truncated to integers: the error, below one unit, is < 2^-28 of the
+    // largest weight of the head)
+    const uint32_t W0 = limb_bytes((int32_t)wv[0]), W1 = limb_bytes((int32_t)wv[1]);
+    const uint32_t W2 = limb_bytes((int32_t)wv[2]), W3 = limb_bytes((int32_t)wv[3]);
     const uint32_t t01l = perm(W1, W0, 0x05010400u), t01h = perm(W1, W0, 0x07030602u);
     const uint32_t t23l = perm(W3, W2, 0x05010400u), t23h = perm(W3, W2, 0x07030602u);
     uint32_t* wb = reinterpret_cast<uint32_t*>(wbuf_of<S>(st));
@@ -808,12 +820,32 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
       Gw = Gn;
     }
     const uint8_t* vb = vbuf_of<S>(st) + grp * 16 * R;
+    // every LDS read of the tile first, one wait for all of them: plane j of
+    // column j (the field's bit window spans planes j0, j0 + 1 for 5 and 8
+    // levels)
+    constexpr int NR = (L == 5 || L == 8) ? 2 : 1;
+    uint4 xr[PS][NR];
+#pragma unroll
+    for (int s = 0; s < PS; ++s) {
+      const int j = 16 * s + col;
+      if constexpr (L == 5) {
+        const int j0 = (7 * j) >> 3;
+        xr[s][0] = *reinterpret_cast<const uint4*>(vb + 16 * j0);
+        xr[s][NR - 1] = *reinterpret_cast<const uint4*>(vb + 16 * j0 + 16);
+      } else if constexpr (L == 8) {
+        const int j0 = (6 * j) >> 3;
+        xr[s][0] = *reinterpret_cast<const uint4*>(vb + 16 * j0);
+        xr[s][NR - 1] = *reinterpret_cast<const uint4*>(vb + 16 * min(j0 + 1, R - 1));
+      } else {
+        xr[s][0] = *reinterpret_cast<const uint4*>(vb + 16 * j);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < PS; ++s) {
       const int j = 16 * s + col;
       uint32_t f[PF][4];
       if constexpr (L == 6) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vb + 16 * j);
+        const uint4 x = xr[s][0];
         const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
         const bool ones = j == 47;
 #pragma unroll
@@ -827,9 +859,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
         }
       } else if constexpr (L == 5) {
         const int bit = 7 * j;
-        const int j0 = bit >> 3;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(vb + 16 * j0);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(vb + 16 * j0 + 16);
+        const uint4 x0 = xr[s][0], x1 = xr[s][NR - 1];
         const uint32_t b0[4] = {x0.x, x0.y, x0.z, x0.w}, b1[4] = {x1.x, x1.y, x1.z, x1.w};
         const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
 #pragma unroll
@@ -846,9 +876,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
         // floor(6j/8) and the next (not read past the row: the bits above
         // the field are masked off)
         const int bit = 6 * j;
-        const int j0 = bit >> 3;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(vb + 16 * j0);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(vb + 16 * min(j0 + 1, R - 1));
+        const uint4 x0 = xr[s][0], x1 = xr[s][NR - 1];
         const uint32_t b0[4] = {x0.x, x0.y, x0.z, x0.w}, b1[4] = {x1.x, x1.y, x1.z, x1.w};
         const u16x2 shv = {(unsigned short)(bit & 7), (unsigned short)(bit & 7)};
 #pragma unroll
@@ -859,7 +887,7 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
           f[1][q] = perm(floor_slots<8>(p23), floor_slots<8>(p01), 0x06040200u);
         }
       } else if constexpr (L == 3) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vb + 16 * j);
+        const uint4 x = xr[s][0];
         const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
         const bool ones = j == 31;
 #pragma unroll
@@ -876,14 +904,14 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
           }
         }
       } else if constexpr (L == 4) {
-        const uint4 x = *reinterpret_cast<const uint4*>(vb + 16 * j);
+        const uint4 x = xr[s][0];
         const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int i = 0; i < 4; ++i) f[i][q] = (xs[q] >> (2 * i)) & 0x03030303u;
       } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(vb + 16 * j);
+        const uint4 x = xr[s][0];
         const uint32_t xs[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {

@@ -87,7 +87,6 @@ __global__ __launch_bounds__(kThreads) void rank_select_kernel(
   uint32_t* mk = mask ? mask + (int64_t)b * ((n + 31) >> 5) : nullptr;
   if (rg.n_seq) rg.apply(b, n, k);
   if (n <= 0) return;
-  const int nwords = (n + 31) >> 5;
   const int tid = threadIdx.x, wave = tid >> 6;
 
   // -- radix select of the k-th largest key (k >= 1)
@@ -196,7 +195,6 @@ __global__ __launch_bounds__(kThreads) void rank_select32_kernel(
   uint32_t* mk = mask ? mask + (int64_t)b * ((n + 31) >> 5) : nullptr;
   if (rg.n_seq) rg.apply(b, n, k);
   if (n <= 0) return;
-  const int nwords = (n + 31) >> 5;
   const int tid = threadIdx.x, wave = tid >> 6;
   const int begin = tid * kItems;
   const int cnt = max(0, min(kItems, n - begin));

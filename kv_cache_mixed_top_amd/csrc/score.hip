@@ -81,8 +81,6 @@ __global__ __launch_bounds__(kThreads) void score_keynorm_kernel(ScoreArgs a) {
 // chunks of loads in flight).  Each update is formed in fp32 from the two
 // fp16 values (one rounding) and squared into a per-layer fp32 sum; the
 // sums are reduced across the wave, square-rooted and added in layer order.
-constexpr int kDeltaMaxS = 8;
-
 template <int S>
 __global__ __launch_bounds__(kThreads) void score_hidden_delta_kernel(DeltaArgs a) {
   const int lane = threadIdx.x & 63;
