@@ -222,6 +222,7 @@ def main():
     dec_gbs = decode_bytes / (ms_dec * 1e-3) / 1e9 if D else 0.0
     part_gbs = partial_bytes / (ms_part * 1e-3) / 1e9 if D else 0.0
     kernel_src = ["kv_cache_mixed_top_amd/csrc/decode_mfma.hip",
+                  "kv_cache_mixed_top_amd/csrc/decode_mfma_kernel.h",
                   "kv_cache_mixed_top_amd/csrc/semkv_internal.h",
                   "kv_cache_mixed_top_amd/csrc/semkv_common.h"]
     traffic = traffic_for(kernel_src)
