@@ -701,10 +701,10 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     }
     // limbs of the 4 tokens, transposed to one dword per limb (tokens 4n ..
     // 4n+3 in byte order) -> [head kg][limb][n]
-    // (truncated to integers: the error, below one unit, is < 2^-28 of the
-    // largest weight of the head)
-    const uint32_t W0 = limb_bytes((int32_t)wv[0]), W1 = limb_bytes((int32_t)wv[1]);
-    const uint32_t W2 = limb_bytes((int32_t)wv[2]), W3 = limb_bytes((int32_t)wv[3]);
+    // (rounded to nearest: truncation would bias every weight down, and the
+    // many small weights of a diffuse softmax add that bias up)
+    const uint32_t W0 = limb_bytes((int32_t)rintf(wv[0])), W1 = limb_bytes((int32_t)rintf(wv[1]));
+    const uint32_t W2 = limb_bytes((int32_t)rintf(wv[2])), W3 = limb_bytes((int32_t)rintf(wv[3]));
     const uint32_t t01l = perm(W1, W0, 0x05010400u), t01h = perm(W1, W0, 0x07030602u);
     const uint32_t t23l = perm(W3, W2, 0x05010400u), t23h = perm(W3, W2, 0x07030602u);
     uint32_t* wb = reinterpret_cast<uint32_t*>(wbuf_of<S>(st));

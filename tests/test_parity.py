@@ -72,10 +72,11 @@ def test_rank_tiny_config():
 
 # ------------------------------------------------------------------ quantize + pack
 
-def _quantize_case(K, V, scores, r, Lh, Ll, what):
+def _quantize_case(K, V, scores, r, Lh, Ll, what, q_heads=None, max_decode_layers=None):
     B, layers, kv, n, _ = K.shape
     k = O.topr_count(n, r)
-    cache = sk.SemKVCache(B, layers, kv, kv * 4, Lh, Ll, cap16(k), cap16(n - k), block=128)
+    cache = sk.SemKVCache(B, layers, kv, kv * 4 if q_heads is None else q_heads, Lh, Ll, cap16(k),
+                          cap16(n - k), block=128, max_decode_layers=max_decode_layers, max_tokens=n)
     Kd, Vd = to_dev(K), to_dev(V)
     perm = torch.empty((B, n), dtype=torch.int32, device="cuda")
     sk.semkv_rank_topr(to_dev(scores), k, perm)
@@ -179,15 +180,12 @@ def _decode_case(B, layers, kv, Hq, n, r, Lh, Ll, sm, seed, nl=None, layer0=0):
     rng = np.random.default_rng(seed)
     K, V = _kv(rng, B, layers, kv, n)
     s = rng.random((B, n)).astype(np.float32)
-    cache, op = _quantize_case(K, V, s, r, Lh, Ll, f"decode setup seed={seed}")
     nl = layers if nl is None else nl
+    # the cache is built for the requested query head count and layer window
+    cache, op = _quantize_case(K, V, s, r, Lh, Ll, f"decode setup seed={seed}", q_heads=Hq,
+                               max_decode_layers=nl)
     q = (rng.standard_normal((B, nl, Hq, 128)) / math.sqrt(128)).astype(np.float16)
-    # rebuild the cache for the requested q head count
     out = torch.empty((B, nl, Hq, 128), dtype=torch.float32, device="cuda")
-    cache.geom.q_heads = Hq
-    cache.c.g.q_heads = Hq
-    cache.workspace = torch.empty(sk.semkv_workspace_bytes(cache.geom, nl, n), dtype=torch.uint8,
-                                  device="cuda")
     sk.semkv_decode_attn(cache, to_dev(q), out, layer0=layer0, sm_scale=sm)
     sk.semkv_sync_check()
     ref = O.decode_attention(q, op, sm, layer0=layer0)
