@@ -173,6 +173,14 @@ __device__ __forceinline__ i4 as_i4(uint32_t a, uint32_t b, uint32_t c, uint32_t
 __device__ __forceinline__ uint32_t limb_bytes(int32_t x) {
   return ((uint32_t)x + 0x80808080u) ^ 0x80808080u;
 }
+// floor(x + 1/2) for 0 <= x < 2^31 in one instruction (v_cvt_rpi_i32_f32;
+// rint and a conversion take two): the weights' nearest fixed-point value,
+// with halves rounded up.
+__device__ __forceinline__ int32_t round_int(float x) {
+  int32_t r;
+  asm("v_cvt_rpi_i32_f32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
 // Exact value of the four limb sums of one C row group: sum_k c[k] 256^k.
 __device__ __forceinline__ int64_t limb_value(i4 c) {
   return (int64_t)c[0] + ((int64_t)c[1] << 8) + ((int64_t)c[2] << 16) + ((int64_t)c[3] << 24);
@@ -341,7 +349,9 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     lds_void* mv = (lds_void*)((__attribute__((address_space(3))) uint32_t*)mbuf_of<S>(st) + 64);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(plane_rsrc(kmg + (live ? t0 : 0), rows * 4), mk, 4,
                                              (int)(4u * (uint32_t)lane), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(plane_rsrc(vmg + (live ? t0 : 0), rows * 4), mv, 4,
+    // (the V meta range ends with the chunk: rows past it read as {0, 0},
+    // which keeps their zero weights finite whatever the pool holds there)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(plane_rsrc(vmg + (live ? t0 : 0), live ? 4 * (ir1 - t0) : 0), mv, 4,
                                              (int)(4u * (uint32_t)lane), 0, 0, 0);
     issue_v(lds_at(vbuf_of<S>(st), 0), v);
     const int tb = live ? t0 * R : 0;
@@ -676,8 +686,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const float p = __builtin_amdgcn_exp2f(zz[s] - frame);   // 0 past the chunk
-      // past the chunk the meta word may be anything: take {0, 0}
-      const h2 sm = __builtin_bit_cast(h2, 4 * n + s < nt ? vmw[s] : 0u);   // {scale, min}
+      const h2 sm = __builtin_bit_cast(h2, vmw[s]);   // {scale, min}; {0, 0} past the chunk
       lsum += p;
       msum = fmaf(p, (float)sm[1], msum);
       wv[s] = (float)sm[0] * (p * two_g);
@@ -703,8 +712,8 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     // 4n+3 in byte order) -> [head kg][limb][n]
     // (rounded to nearest: truncation would bias every weight down, and the
     // many small weights of a diffuse softmax add that bias up)
-    const uint32_t W0 = limb_bytes((int32_t)rintf(wv[0])), W1 = limb_bytes((int32_t)rintf(wv[1]));
-    const uint32_t W2 = limb_bytes((int32_t)rintf(wv[2])), W3 = limb_bytes((int32_t)rintf(wv[3]));
+    const uint32_t W0 = limb_bytes(round_int(wv[0])), W1 = limb_bytes(round_int(wv[1]));
+    const uint32_t W2 = limb_bytes(round_int(wv[2])), W3 = limb_bytes(round_int(wv[3]));
     const uint32_t t01l = perm(W1, W0, 0x05010400u), t01h = perm(W1, W0, 0x07030602u);
     const uint32_t t23l = perm(W3, W2, 0x05010400u), t23h = perm(W3, W2, 0x07030602u);
     uint32_t* wb = reinterpret_cast<uint32_t*>(wbuf_of<S>(st));
@@ -974,6 +983,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   QInt& qi = *reinterpret_cast<QInt*>(wx);
   QCoef& qc = *reinterpret_cast<QCoef*>(vb2);
+  // The PV wave issues first when both are ready: it has less to do per tile
+  // than the QK wave, and so is never the one a tile's barrier waits for.
+  if (wave == 1) __builtin_amdgcn_s_setprio(1);
   if (seg == 0) {
     if (wave == 0) qk_wave<LA, kRot>(a, 0, r0, r1, b, li, g, u, st, qi, qc, fin);
     else pv_wave<LA>(a, r0, r1, u, st, fin);

@@ -104,6 +104,15 @@ def test_llama8b_32k_full():
         sk.semkv_decode_merge(cache, out)
         if j in steps:
             outs.append(out)
+    # the per-layer launch shape (one layer per partials + merge pair: a few
+    # hundred short chunks per head and the many-chunk merge)
+    per_layer = {}
+    for layer in (0, 31):
+        o = torch.empty((w.batch, 1, w.q_heads, 128), dtype=torch.float32, device=DEV)
+        sk.semkv_decode_partials(cache, q[0][:, layer:layer + 1].contiguous(), layer0=layer,
+                                 sm_scale=w.sm_scale)
+        sk.semkv_decode_merge(cache, o)
+        per_layer[layer] = o.cpu().numpy()
     sk.semkv_sync_check()
     group = w.q_heads // w.kv_heads
     rng = np.random.default_rng(5)
@@ -116,6 +125,9 @@ def test_llama8b_32k_full():
             for j, out in zip(steps, outs):
                 worst = max(worst, _decode_group(op, q[j], 0, layer, head, group, w.sm_scale,
                                                  out.cpu().numpy(), f"step {j} layer {layer}"))
+            worst = max(worst, _decode_group(op, q[0][:, layer:layer + 1], 0, 0, head, group,
+                                             w.sm_scale, per_layer[layer],
+                                             f"per-layer launch, step 0 layer {layer}"))
     for layer, head in extra:
         _print(f"llama8b_32k: plane layer {layer} head {head}")
         _check_plane(cache, K, V, wp, k, 6, 5, 0, layer, head)
