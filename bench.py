@@ -478,13 +478,14 @@ def copy_leg(torch, stream, mib=2048):
 
 
 def workload_leg(sk, W, torch, dev, stream, name, levels=None, r=None, inputs=None,
-                 quant_reps=5, every=8):
+                 quant_reps=5, every=8, rotate=False):
     """One prompt workload outside the headline step: rank + quantize-pack
     (median of `quant_reps` timed repetitions on the same cache), then the
     workload's decode steps (partials + merge over all layers, fresh queries
     each step), timed like the headline: every `every`-th partials launch and
     the whole loop.  `levels`/`r` override the workload's; `inputs` reuses
-    (K, V, scores) already on the device."""
+    (K, V, scores) already on the device; `rotate` builds a Hadamard-rotated
+    cache."""
     import numpy as np
     w = W.WORKLOADS[name]
     Lh, Ll = levels if levels is not None else (w.L_high, w.L_low)
@@ -500,7 +501,7 @@ def workload_leg(sk, W, torch, dev, stream, name, levels=None, r=None, inputs=No
         q = W.make_q_torch(w, D, dev)
         k = sk.semkv_topr_count(n, r)
         cache = sk.SemKVCache(B, layers, kv, Hq, Lh, Ll, cap16(k), cap16(n - k), block=w.block,
-                              max_tokens=n)
+                              max_tokens=n, rotate=rotate)
         perm = torch.empty((B, n), dtype=torch.int32, device=dev)
         out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device=dev)
     stream.synchronize()
@@ -591,7 +592,10 @@ def cliff_leg(sk, W, torch, dev, stream):
     nominal and stored bits per value, reconstruction MSE of K and of V over
     layers 0 and 31 (rows reconstructed by semkv_dequantize_rows), and the
     largest |out - ref| / max(1, |ref|) of the last decode step against fp32
-    attention over the fp16 cache (sequence 0, layers 0 and 31)."""
+    attention over the fp16 cache (sequence 0, layers 0 and 31).  Three more
+    settings repeat (4,4), (5,4) at r = .5 and (6,5) at r = .5 on a
+    Hadamard-rotated cache (SemKV Table 2's quantizer with rotation), whose
+    proxies show what the rotation does to the outlier channels of K."""
     import math
     w = W.WORKLOADS["cliff_4x32k"]
     B, n, layers, kv, Hq = w.batch, w.n, w.layers, w.kv_heads, w.q_heads
@@ -599,13 +603,14 @@ def cliff_leg(sk, W, torch, dev, stream):
         K, V, _ = W.make_kv_torch(w, dev)
         scores = W.attention_mass_torch(K, w, dev)
     stream.synchronize()
-    settings = [(L, L, 0.0) for L in W.CLIFF_UNIFORM]
-    settings += [(Lh, Ll, r) for Lh, Ll in W.CLIFF_PAIRS for r in W.CLIFF_RS]
+    settings = [(L, L, 0.0, False) for L in W.CLIFF_UNIFORM]
+    settings += [(Lh, Ll, r, False) for Lh, Ll in W.CLIFF_PAIRS for r in W.CLIFF_RS]
+    settings += [(4, 4, 0.0, True), (5, 4, 0.5, True), (6, 5, 0.5, True)]
     sample_layers = (0, layers - 1)
     rows = []
-    for Lh, Ll, r in settings:
+    for Lh, Ll, r, rot in settings:
         leg = workload_leg(sk, W, torch, dev, stream, "cliff_4x32k", levels=(Lh, Ll), r=r,
-                           inputs=(K, V, scores), quant_reps=3)
+                           inputs=(K, V, scores), quant_reps=3, rotate=rot)
         cache, q, out = leg["_cache"], leg["_q"], leg["_out"]
         k = sk.semkv_topr_count(n, r)
         Rh, Rl = sk.semkv_row_bytes(Lh), sk.semkv_row_bytes(Ll)
@@ -639,7 +644,8 @@ def cliff_leg(sk, W, torch, dev, stream):
                 worst = max(worst, float(err.max()))
         stream.synchronize()
         row = strip_private(leg)
-        row.update({"nominal_bits": round(nominal, 4), "stored_bits": round(stored, 4),
+        row.update({"rotate": rot,
+                    "nominal_bits": round(nominal, 4), "stored_bits": round(stored, 4),
                     "compression_vs_fp16": round(16.0 / stored, 3),
                     "mse_K": se[0] / cnt, "mse_V": se[1] / cnt,
                     "attn_err_vs_fp16_cache": worst})
@@ -647,7 +653,7 @@ def cliff_leg(sk, W, torch, dev, stream):
                     "quantize_algorithmic_bytes", "partials_algorithmic_bytes"):
             row.pop(key, None)
         rows.append(row)
-        log(f"cliff ({Lh},{Ll}) r={r}: quantize {row['quantize_pct_hbm_peak']}%, partials "
+        log(f"cliff ({Lh},{Ll}) r={r}{' rotated' if rot else ''}: quantize {row['quantize_pct_hbm_peak']}%, partials "
             f"{row['partials_pct_hbm_peak']}%, {row['stored_bits']} bits, attn err "
             f"{worst:.2e}")
         del cache, q, out, leg

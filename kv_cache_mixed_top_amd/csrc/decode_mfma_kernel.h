@@ -314,9 +314,15 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   // offset of set s's window within a tile
   const int kbyte = L == 6 || L == 8 ? 12 * kg : L == 5 ? (77 * kg) >> 3 : L == 4 || L == 3 ? 8 * kg : 16 * kg;
   const int kbit = L == 5 ? (77 * kg) & 7 : 0;
-  int koff[4];
+  // set s's window: its dword-aligned byte offset in the tile and its shift
+  // (bytes for 3 and 6 levels, bits for 5)
+  int kaddr[4], kshift[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) koff[s] = (4 * n + s) * R + kbyte;
+  for (int s = 0; s < 4; ++s) {
+    const int o = (4 * n + s) * R + kbyte;
+    kaddr[s] = o & ~3;
+    kshift[s] = L == 5 ? 8 * (o & 3) + kbit : o & 3;
+  }
 
   // Tile v: its V bytes (64 R bytes from its first row; 16-row byte-planar
   // tiles) -> V buffer S, then this lane's windows of its 4 K rows and the K
@@ -359,10 +365,10 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if constexpr (L == 4) {
-        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rk, koff[s], 0, 0);
+        const auto x = __builtin_amdgcn_raw_buffer_load_b64(rk, kaddr[s], 0, 0);   // (8-byte aligned)
         kx[S][s] = make_uint4(x[0], x[1], 0u, 0u);
       } else {
-        kx[S][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[s] & ~3, 0, 0));
+        kx[S][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, kaddr[s], 0, 0));
       }
     }
   };
@@ -574,7 +580,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
       const uint32_t x0 = kx[S][s].x, x1 = kx[S][s].y, x2 = kx[S][s].z, x3 = kx[S][s].w;
       uint32_t w[4 * NM];
       if constexpr (L == 6) {
-        const int sh = koff[s] & 3;
+        const int sh = kshift[s];
         const uint32_t d[3] = {__builtin_amdgcn_alignbyte(x1, x0, sh),
                                __builtin_amdgcn_alignbyte(x2, x1, sh),
                                __builtin_amdgcn_alignbyte(x3, x2, sh)};
@@ -591,7 +597,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
         }
         w[15] = 0;
       } else if constexpr (L == 5) {
-        const int bs = 8 * (koff[s] & 3) + kbit;                 // < 32
+        const int bs = kshift[s];                                // < 32
         const uint32_t w0 = __builtin_amdgcn_alignbit(x1, x0, bs);
         const uint32_t w1 = __builtin_amdgcn_alignbit(x2, x1, bs);
         const uint32_t w2 = __builtin_amdgcn_alignbit(x3, x2, bs);
@@ -625,7 +631,7 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
           w[4 * gi + 3] = floor_slots<8>(pb);
         }
       } else if constexpr (L == 3) {
-        const int sh = koff[s] & 3;
+        const int sh = kshift[s];
         const uint32_t d[2] = {__builtin_amdgcn_alignbyte(x1, x0, sh), __builtin_amdgcn_alignbyte(x2, x1, sh)};
 #pragma unroll
         for (int q = 0; q < 2; ++q) {

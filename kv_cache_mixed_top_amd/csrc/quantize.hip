@@ -112,14 +112,17 @@ __device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
 // perm, its first destination slot and the token index base.  A ragged batch
 // takes them from the sequence's device counters; a sequence whose rows would
 // not fit (or, for a prompt, whose tail is not empty) writes nothing, and the
-// counter update that follows records that in its status word.
+// counter update that follows records that in its status word.  (kRagged
+// is a compile-time choice, so that the kernels of uniform batches carry
+// none of the ragged bookkeeping.)
 struct PoolPart {
   int count, perm_off;
   int64_t start, token_base, perm_ld;
 };
+template <bool kRagged>
 __device__ __forceinline__ PoolPart pool_part(const QuantArgs& a, int pool, int b) {
   PoolPart pp;
-  if (!a.seq) {
+  if constexpr (!kRagged) {
     pp.count = pool == 0 ? a.k_high : a.n - a.k_high;
     pp.perm_off = pool == 0 ? 0 : a.k_high;
     pp.start = a.start[pool];
@@ -646,9 +649,9 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, const Poo
 // One pool's tile: the fast path of its level count (a compile-time count
 // when the kernel is specialised for it, else a runtime switch), or the
 // generic tile.
-template <int LF, bool kRot>
+template <int LF, bool kRot, bool kRagged>
 __device__ __forceinline__ void pool_tile(const QuantArgs& a, int pool, int t, uint8_t* smem) {
-  const PoolPart pp = pool_part(a, pool, blockIdx.z);
+  const PoolPart pp = pool_part<kRagged>(a, pool, blockIdx.z);
   if (t * kRows >= pp.count) return;            // past this sequence's rows (ragged bounds)
   const bool aligned16 = (pp.start & 15) == 0;
   const int L = LF ? LF : a.fmt[pool].L;
@@ -665,14 +668,33 @@ __device__ __forceinline__ void pool_tile(const QuantArgs& a, int pool, int t, u
   }
 }
 
-template <int LH, int LL, bool kRot = false>
+template <int LH, int LL, bool kRot, bool kRagged>
 __global__ __launch_bounds__(kThreads) void quantize_pack_kernel(QuantArgs a, int tiles_high) {
   constexpr int kGeneric = kRows * kCodeStride * 2;
   constexpr int kFast = kCode8Bytes + kImgBytes;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kGeneric > kFast ? kGeneric : kFast];
   const int tile = blockIdx.x;
-  if (tile < tiles_high) pool_tile<LH, kRot>(a, 0, tile, smem);
-  else pool_tile<LL, kRot>(a, 1, tile - tiles_high, smem);
+  if (tile < tiles_high) pool_tile<LH, kRot, kRagged>(a, 0, tile, smem);
+  else pool_tile<LL, kRot, kRagged>(a, 1, tile - tiles_high, smem);
+}
+
+// The (6, 5) pair has its own instance; every other pair picks its tiles at
+// run time.
+template <bool kRagged>
+void launch_kind(const QuantArgs& a, dim3 grid, int tiles_high, hipStream_t stream) {
+  const bool pair65 = a.fmt[0].L == 6 && a.fmt[1].L == 5;
+  if (pair65 && a.rotate)
+    hipLaunchKernelGGL((quantize_pack_kernel<6, 5, true, kRagged>), grid, dim3(kThreads), 0, stream, a,
+                       tiles_high);
+  else if (pair65)
+    hipLaunchKernelGGL((quantize_pack_kernel<6, 5, false, kRagged>), grid, dim3(kThreads), 0, stream,
+                       a, tiles_high);
+  else if (a.rotate)
+    hipLaunchKernelGGL((quantize_pack_kernel<0, 0, true, kRagged>), grid, dim3(kThreads), 0, stream, a,
+                       tiles_high);
+  else
+    hipLaunchKernelGGL((quantize_pack_kernel<0, 0, false, kRagged>), grid, dim3(kThreads), 0, stream,
+                       a, tiles_high);
 }
 
 }  // namespace
@@ -684,18 +706,8 @@ hipError_t launch_quantize_pack(const QuantArgs& a, hipStream_t stream) {
   const int tiles = tiles_high + tiles_low;
   if (tiles == 0) return hipSuccess;
   dim3 grid(tiles, a.layers * a.kv_heads * 2, a.batch);
-  if (a.fmt[0].L == 6 && a.fmt[1].L == 5 && a.rotate)
-    hipLaunchKernelGGL((quantize_pack_kernel<6, 5, true>), grid, dim3(kThreads), 0, stream, a,
-                       tiles_high);
-  else if (a.fmt[0].L == 6 && a.fmt[1].L == 5)
-    hipLaunchKernelGGL((quantize_pack_kernel<6, 5>), grid, dim3(kThreads), 0, stream, a,
-                       tiles_high);
-  else if (a.rotate)
-    hipLaunchKernelGGL((quantize_pack_kernel<0, 0, true>), grid, dim3(kThreads), 0, stream, a,
-                       tiles_high);
-  else
-    hipLaunchKernelGGL((quantize_pack_kernel<0, 0>), grid, dim3(kThreads), 0, stream, a,
-                       tiles_high);
+  if (a.seq) launch_kind<true>(a, grid, tiles_high, stream);
+  else launch_kind<false>(a, grid, tiles_high, stream);
   return hipGetLastError();
 }
 
