@@ -366,9 +366,11 @@ def graph_leg(sk, torch, cache, q, D, layers, B, Hq, decode_bytes, stream):
         stream.synchronize()
         rel = (out_g - out_e).abs() / out_e.abs().clamp(min=1.0)
         worst = max(worst, float(rel.max()))
-    # per-layer launches split the rows into different chunks, so the two
-    # forms agree to the rounding of the split, well inside the parity bound
-    assert worst <= 2e-3, f"graph replay differs from the one-launch decode by {worst}"
+    # per-layer launches split the rows into different chunks (each chunk has
+    # its own fixed-point weight scale), so the two forms differ by their two
+    # approximation errors, each within the 2e-3 parity bound of the exact
+    # attention: at most twice that bound apart
+    assert worst <= 4e-3, f"graph replay differs from the one-launch decode by {worst}"
     times = []
     for j in range(steps):
         with torch.cuda.stream(stream):

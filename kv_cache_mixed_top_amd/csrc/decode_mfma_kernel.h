@@ -684,6 +684,10 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     if (__ballot(zmax > frame) != 0ull) {
       const float nf = fmaxf(frame, group_max(zmax) + kFrameMargin * kLog2e);
       fac = nf == frame ? 1.0f : __builtin_amdgcn_exp2f(frame - nf);   // 2^-inf = 0 on the first tile
+      // a raised frame shrinks every weight from here on by fac: the
+      // fixed-point exponent is taken afresh from this tile (kept, the later
+      // weights would lose as many bits as the frame rose)
+      gset = gset && nf == frame;
       frame = nf;
       lsum *= fac;
       msum *= fac;
@@ -697,10 +701,10 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
       msum = fmaf(p, (float)sm[1], msum);
       wv[s] = (float)sm[0] * (p * two_g);
     }
-    // fixed-point exponent of head kg: set from the first nonzero weights to
-    // put the largest at 2^28 .. 2^29, lowered when a weight reaches 2^30
-    // (both change the scale of the sums: wave 1 moves what it has summed to
-    // its totals first)
+    // fixed-point exponent of head kg: set from the first nonzero weights
+    // (and again after each frame raise) to put the largest at 2^28 .. 2^29,
+    // lowered when a weight reaches 2^30 (each change rescales the sums:
+    // wave 1 moves what it has summed to its totals first)
     const float wmx = fmaxf(fmaxf(wv[0], wv[1]), fmaxf(wv[2], wv[3]));
     if (__ballot(wmx >= kWeightLimit || (!gset && wmx > 0.0f)) != 0ull) {
       const float gm = group_max(wmx);

@@ -128,9 +128,17 @@ def test_llama8b_32k_full():
             worst = max(worst, _decode_group(op, q[0][:, layer:layer + 1], 0, 0, head, group,
                                              w.sm_scale, per_layer[layer],
                                              f"per-layer launch, step 0 layer {layer}"))
+    # more layers, every KV head: a head's chunks of 4,096 rows each see a
+    # different sequence of softmax frames and fixed-point exponents
+    for layer in (8, 16, 24):
+        for head in range(w.kv_heads):
+            extra.append((layer, head))
     for layer, head in extra:
         _print(f"llama8b_32k: plane layer {layer} head {head}")
-        _check_plane(cache, K, V, wp, k, 6, 5, 0, layer, head)
+        op = _check_plane(cache, K, V, wp, k, 6, 5, 0, layer, head)
+        for j, out in zip(steps, outs):
+            worst = max(worst, _decode_group(op, q[j], 0, layer, head, group, w.sm_scale,
+                                             out.cpu().numpy(), f"step {j} layer {layer}"))
     _print(f"llama8b_32k: worst decode error {worst:.3e}")
 
 
