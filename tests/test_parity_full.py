@@ -289,3 +289,51 @@ def test_cliff_grid_sampled():
         _print(f"cliff ({Lh},{Ll}) r={r}: plane ({b},{layer},{head}) exact, decode error {e:.3e}")
         del cache, out
         torch.cuda.empty_cache()
+
+
+def test_decode_frame_raise_after_lowered_exponent():
+    """Logits shaped so that every 1,024-row chunk of a 32-layer launch first
+    lowers its fixed-point exponent (a few tokens just under the softmax
+    frame) and then raises its frame (a spike 11.5 nats above the typical
+    tokens, whose weights after the raise are small).  Besides the 2e-3
+    parity bound the error is held to 2e-5, ten times what the arithmetic
+    allows: the weights keep at least 28 bits against a chunk's largest
+    weight (an error below rows / 2^29 = 1.9e-6 of its normaliser) and the
+    query 27 bits, so a larger error means lost weight bits.  (An exponent
+    kept across the frame raise leaves the typical tokens' weights at a few
+    units: 1.6e-4 here.)"""
+    B, layers, kv, Hq, n, r = 1, 32, 8, 32, 8192, 0.5
+    beta = 10.0 / 3.0                                   # logit per unit of the u component
+    g = torch.Generator(device=DEV)
+    g.manual_seed(21)
+    u = torch.randn((layers, kv, 128), generator=g, device=DEV)
+    u = u / u.norm(dim=-1, keepdim=True)
+    a = 0.3 * torch.randn((n,), generator=g, device=DEV)           # typical logits ~ N(0, 1)
+    pos = torch.arange(n, device=DEV) % 2048
+    for off in (200, 260, 320, 380):
+        a = torch.where(pos == off, torch.full_like(a, 3.0), a)     # just under the frame: 10 nats
+    for off in (1100, 1160):
+        a = torch.where(pos == off, torch.full_like(a, 3.45), a)    # the spike: 11.5 nats
+    K = (0.05 * torch.randn((B, layers, kv, n, 128), generator=g, device=DEV)
+         + a[None, None, None, :, None] * u[None, :, :, None, :]).half()
+    V = torch.randn((B, layers, kv, n, 128), generator=g, device=DEV).half()
+    q = (beta * u.repeat_interleave(Hq // kv, dim=1)[None]
+         + 0.02 * torch.randn((B, layers, Hq, 128), generator=g, device=DEV)).half()
+    scores = torch.rand((B, n), generator=g, device=DEV)
+    k = sk.semkv_topr_count(n, r)
+    perm, wp = _rank_full(scores, k)
+    cache = sk.SemKVCache(B, layers, kv, Hq, 6, 5, cap16(k), cap16(n - k), max_tokens=n)
+    sk.semkv_quantize_pack(cache, K, V, perm, k)
+    out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device=DEV)
+    sk.semkv_decode_partials(cache, q)
+    sk.semkv_decode_merge(cache, out)
+    sk.semkv_sync_check()
+    got = out.cpu().numpy()
+    worst = 0.0
+    for layer in (0, 17):
+        for head in range(kv):
+            op = _check_plane(cache, K, V, wp, k, 6, 5, 0, layer, head)
+            worst = max(worst, _decode_group(op, q, 0, layer, head, Hq // kv, 1.0, got,
+                                             f"frame raise layer {layer} head {head}"))
+    _print(f"frame raise after a lowered exponent: worst decode error {worst:.3e}")
+    assert worst <= 2e-5, f"frame raise after a lowered exponent: {worst:.3e} > 2e-5"
