@@ -67,12 +67,12 @@ bool decode_mfma_supported(const DecodeArgs& a) {
   return true;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
-  const int pool_chunks = a.nch[0] + a.nch[1];
-  if (pool_chunks == 0) return hipSuccess;
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool with_tail, hipStream_t stream) {
+  const int chunks = a.nch[0] + a.nch[1] + (with_tail ? a.nch[2] : 0);
+  if (chunks == 0) return hipSuccess;
   int LA, LB;
   effective_pair(a, LA, LB);
-  dim3 grid(pool_chunks, a.nl * a.kv_heads, a.batch);
+  dim3 grid(chunks, a.nl * a.kv_heads, a.batch);
   return a.rotate ? launch_pair<true>(LA, LB, grid, a, stream) : launch_pair<false>(LA, LB, grid, a, stream);
 }
 

@@ -957,6 +957,193 @@ __device__ __forceinline__ void pv_wave(const DecodeArgs& a, int64_t r0, int64_t
     }
 }
 
+// ---- the fp16 tail of generation (at most 128 rows, one chunk), handled by
+// a workgroup of the same launch, so that it runs alongside the pool chunks
+// instead of in a launch of its own.  The rows are the unquantized K and V
+// (not rotated on a rotated cache).  QK^T on the 16x16x32 f16 matrix core (A
+// rows 0-3 = the 4 query heads, B columns = 16 K rows; fp16 products are
+// exact, sums fp32); wave w takes the 16-row blocks w, w + 2, w + 4, w + 6.
+// The logits go to LDS, one row per thread for the softmax statistics; then
+// thread (rs, dg) sums rows rs, rs + 8, ... over dimensions 8 dg .. 8 dg + 7
+// for the 4 heads.  The record is the same (m, l, o[128]) per head as the
+// pool chunks', m in natural-log units; on a rotated cache o is stored as
+// H o, which the merge's rotation returns to o (H H = I).
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+constexpr int kTailRowsMax = 128;
+
+__device__ __forceinline__ void tail_pair(const DecodeArgs& a, int b, int li, int g, int64_t u,
+                                          const Stage3& st) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = (int)min((int64_t)kTailRowsMax, seg_rows(a, 2, b));   // the whole tail
+  const int layer = a.layer0 + li;
+  const int64_t plane_k = (((int64_t)b * a.layers + layer) * a.kv_heads + g) * 2;
+  const uint16_t* kt = a.tail_kv + plane_k * a.block * kHeadDim;
+  const uint16_t* vt = kt + (int64_t)a.block * kHeadDim;
+  float* z = reinterpret_cast<float*>(st.v0);      // [4][128] logits, then weights
+  float* part = reinterpret_cast<float*>(st.v1);   // [4][128] wave 1's output sums
+  float* red = reinterpret_cast<float*>(st.w0);    // [2 waves][8]: maxima, sums
+
+  // queries as the A operand (row col < 4 = head col), K rows as B; two
+  // rounds of two 16-row blocks (so that this path holds no more registers
+  // than the pool path of the lightest level pairs)
+  const int col = lane & 15, kg = lane >> 4;
+  const uint16_t* qh = a.q + (((int64_t)b * a.nl + li) * a.q_heads + g * 4 + min(col, 3)) * kHeadDim;
+  uint4 qa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qa[ks] = col < 4 ? *reinterpret_cast<const uint4*>(qh + 32 * ks + 8 * kg) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int round = 0; round < 2; ++round) {
+    uint4 kb[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 16 * (wave + 2 * (2 * round + j)) + col;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kb[j][ks] = r < n ? *reinterpret_cast<const uint4*>(kt + (int64_t)r * kHeadDim + 32 * ks + 8 * kg)
+                          : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, qa[ks]),
+                                                     __builtin_bit_cast(h8, kb[j][ks]), acc, 0, 0, 0);
+      const int r = 16 * (wave + 2 * (2 * round + j)) + col;
+      if (kg == 0 && r < n) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) z[h * kTailRowsMax + r] = a.sm_scale * acc[h];
+      }
+    }
+  }
+  // the V rows of this thread: rows rs + 8 i, dimensions 8 dg .. 8 dg + 7, in
+  // four passes of four rows (the first two loaded now)
+  const int dg = tid & 15, rs = tid >> 4;
+  auto load_v = [&](int pass, uint4 (&vv)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rs + 8 * (4 * pass + j);
+      vv[j] = r < n ? *reinterpret_cast<const uint4*>(vt + (int64_t)r * kHeadDim + 8 * dg)
+                    : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 va[4], vb[4];
+  load_v(0, va);
+  load_v(1, vb);
+  __syncthreads();                                  // logits in LDS
+
+  // softmax statistics per head, one row per thread
+  float zr[4], mx[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    zr[h] = tid < n ? z[h * kTailRowsMax + tid] : -INFINITY;
+    mx[h] = wave_max(zr[h]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) red[wave * 8 + h] = mx[h];
+  }
+  __syncthreads();
+  float sm[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    mx[h] = fmaxf(red[h], red[8 + h]);
+    const float p = tid < n ? __expf(zr[h] - mx[h]) : 0.0f;
+    if (tid < n) z[h * kTailRowsMax + tid] = p;
+    sm[h] = wave_sum(p);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) red[wave * 8 + 4 + h] = sm[h];
+  }
+  __syncthreads();                                  // weights and sums in LDS
+
+  float acc[4][8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+  auto pv_pass = [&](int pass, const uint4 (&vv)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = rs + 8 * (4 * pass + j);
+      if (r < n) {
+        const uint32_t w4[4] = {vv[j].x, vv[j].y, vv[j].z, vv[j].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float p = z[h * kTailRowsMax + r];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc[h][e] = fmaf(p, h2f((uint16_t)(w4[e >> 1] >> (16 * (e & 1)))), acc[h][e]);
+        }
+      }
+    }
+  };
+  pv_pass(0, va);
+  load_v(2, va);
+  pv_pass(1, vb);
+  load_v(3, vb);
+  pv_pass(2, va);
+  pv_pass(3, vb);
+  // rows of the wave's 4 row groups (lanes 16 apart), then wave 1 -> wave 0
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[h][e] += __shfl_xor(acc[h][e], 16, 64);
+      acc[h][e] += __shfl_xor(acc[h][e], 32, 64);
+    }
+  if (wave == 1 && lane < 16) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float4* dst = reinterpret_cast<float4*>(part + h * kHeadDim + 8 * dg);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && lane < 16) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float4* dst = reinterpret_cast<float4*>(part + h * kHeadDim + 8 * dg);
+      const float4 o0 = dst[0], o1 = dst[1];
+      dst[0] = make_float4(o0.x + acc[h][0], o0.y + acc[h][1], o0.z + acc[h][2], o0.w + acc[h][3]);
+      dst[1] = make_float4(o1.x + acc[h][4], o1.y + acc[h][5], o1.z + acc[h][6], o1.w + acc[h][7]);
+    }
+  }
+  __syncthreads();                                  // o[4][128] in LDS
+  if (wave == 0) {
+    float* wsu = a.ws + u * 4 * kPartialStride;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float o0 = part[h * kHeadDim + lane], o1 = part[h * kHeadDim + lane + 64];   // dims lane, lane + 64
+      if (a.rotate) {
+        // o -> H o: index bit 6 within the lane, bits 0-5 across lanes
+        const float s0 = o0 + o1, s1 = o0 - o1;
+        o0 = s0;
+        o1 = s1;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+          const float p0 = __shfl_xor(o0, m, 64), p1 = __shfl_xor(o1, m, 64);
+          const bool upper = (lane & m) != 0;
+          o0 = upper ? p0 - o0 : o0 + p0;
+          o1 = upper ? p1 - o1 : o1 + p1;
+        }
+        o0 *= 0.08838834764831845f;   // fp32(1/sqrt(128))
+        o1 *= 0.08838834764831845f;
+      }
+      wsu[h * kPartialStride + 2 + lane] = o0;
+      wsu[h * kPartialStride + 2 + lane + 64] = o1;
+      if (lane == 0) {
+        wsu[h * kPartialStride + 0] = mx[h];
+        wsu[h * kPartialStride + 1] = red[4 + h] + red[8 + 4 + h];
+      }
+    }
+  }
+}
+
 template <int L> constexpr int vbuf_bytes() {
   return ((64 * Lv<L>::R + 1023) / 1024 * 1024) > 3072 ? ((64 * Lv<L>::R + 1023) / 1024 * 1024) : 3072;
 }
@@ -982,14 +1169,18 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   st.m2 = mt2;
 
   const int x = blockIdx.x;
-  const int seg = x < a.nch[0] ? 0 : 1;
-  const int ch = seg == 0 ? x : x - a.nch[0];
   const int b = blockIdx.z;
-  const int64_t r0 = (int64_t)ch * a.chunk;
-  const int64_t r1 = max(r0, min(r0 + (int64_t)a.chunk, seg_rows(a, seg, b)));   // a ragged batch's own rows
   const int li = blockIdx.y / a.kv_heads;
   const int g = blockIdx.y % a.kv_heads;
   const int64_t u = (((int64_t)b * a.nl + li) * a.kv_heads + g) * a.nchunks + x;
+  if (x >= a.nch[0] + a.nch[1]) {                  // the fp16 tail chunk (launched with the pools)
+    tail_pair(a, b, li, g, u, st);
+    return;
+  }
+  const int seg = x < a.nch[0] ? 0 : 1;
+  const int ch = seg == 0 ? x : x - a.nch[0];
+  const int64_t r0 = (int64_t)ch * a.chunk;
+  const int64_t r1 = max(r0, min(r0 + (int64_t)a.chunk, seg_rows(a, seg, b)));   // a ragged batch's own rows
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   QInt& qi = *reinterpret_cast<QInt*>(wx);
   QCoef& qc = *reinterpret_cast<QCoef*>(vb2);

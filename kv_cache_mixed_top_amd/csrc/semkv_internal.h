@@ -151,7 +151,9 @@ bool decode_use_mfma(const DecodeArgs& a);
 // layer, KV head) to fill the device's resident wave slots once.
 int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units);
 int64_t decode_mfma_resident_waves();
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+// The pool chunks, and with with_tail the fp16 tail chunk too (a tail of at
+// most 128 rows in one chunk: nch[2] <= 1, block <= 128).
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool with_tail, hipStream_t stream);
 // The matrix-core kernels of the pairs with 16 levels, of (6,3), (5,3) and
 // of the 8-level pairs other than (8,8), (8,6).
 hipError_t launch_decode_mfma_wide(int LA, int LB, bool rot, dim3 grid, const DecodeArgs& a,
