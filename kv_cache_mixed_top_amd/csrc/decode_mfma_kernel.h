@@ -554,8 +554,11 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   float frame = -INFINITY;   // kFrameMargin above the running maximum (log2 units)
   int G = 0;                 // fixed-point exponent: w = rint(p scale_V 2^G)
   bool gset = false;
-  float two_g = 1.0f;
-  float lsum = 0.0f, msum = 0.0f;
+  // The logits are formed as zz = z - bias, with bias = frame - G once the
+  // frame is finite, so that 2^zz is p 2^G itself (no subtraction and no
+  // scaling per token); thr = frame - bias is the frame in the same terms.
+  float bias = 0.0f, thr = -INFINITY;
+  float lsum = 0.0f, msum = 0.0f;   // sums of p 2^G and p 2^G min_V
 
   auto step = [&](auto Sc, int v) {
     constexpr int S = decltype(Sc)::value;
@@ -567,13 +570,13 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     float zz[4];
     i4 accp;
     // limb sums of head kg -> the integer dot product in fp32 -> the logit
-    // (log2 units) with the row's K scale and minimum
+    // (log2 units) with the row's K scale and minimum, less the bias
     auto logit = [&](i4 c, uint32_t km) {
       const int32_t tlo = (c[1] << 8) + c[0];
       const int32_t thi = (c[3] << 8) + c[2];
       const float zf = fmaf((float)thi, 65536.0f, (float)tlo);
       const h2 sm = __builtin_bit_cast(h2, km);          // {scale, min}
-      return fmaf((float)sm[0], cA * zf, (float)sm[1] * cB);
+      return fmaf((float)sm[0], cA * zf, fmaf((float)sm[1], cB, -bias));
     };
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -681,8 +684,8 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
     // and what was summed so far is then scaled by fac
     float fac = 1.0f;
     const float zmax = fmaxf(fmaxf(zz[0], zz[1]), fmaxf(zz[2], zz[3]));
-    if (__ballot(zmax > frame) != 0ull) {
-      const float nf = fmaxf(frame, group_max(zmax) + kFrameMargin * kLog2e);
+    if (__ballot(zmax > thr) != 0ull) {
+      const float nf = fmaxf(frame, (group_max(zmax) + bias) + kFrameMargin * kLog2e);
       fac = nf == frame ? 1.0f : __builtin_amdgcn_exp2f(frame - nf);   // 2^-inf = 0 on the first tile
       // a raised frame shrinks every weight from here on by fac: the
       // fixed-point exponent is taken afresh from this tile (kept, the later
@@ -691,15 +694,22 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
       frame = nf;
       lsum *= fac;
       msum *= fac;
+      // this tile's logits against the new frame, and the bias from here on
+      const float corr = (bias - frame) + (float)G;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) zz[s] += corr;
+      bias = frame - (float)G;
+      thr = (float)G;
     }
     float wv[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float p = __builtin_amdgcn_exp2f(zz[s] - frame);   // 0 past the chunk
+      const float p = __builtin_amdgcn_exp2f(zz[s]);   // p 2^G; 0 past the chunk
       const h2 sm = __builtin_bit_cast(h2, vmw[s]);   // {scale, min}; {0, 0} past the chunk
       lsum += p;
       msum = fmaf(p, (float)sm[1], msum);
-      wv[s] = (float)sm[0] * (p * two_g);
+      // (+0 addend: one mixed-precision fma; the product is never negative)
+      wv[s] = fmaf((float)sm[0], p, 0.0f);
     }
     // fixed-point exponent of head kg: set from the first nonzero weights
     // (and again after each frame raise) to put the largest at 2^28 .. 2^29,
@@ -712,10 +722,13 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
         // (at most 2^100, so that 2^G stays finite whatever the first weights)
         const int dG = min(28 - ilogbf(gm), 100 - G);
         G += dG;
-        two_g = ldexpf(1.0f, G);
         gset = true;
 #pragma unroll
         for (int s = 0; s < 4; ++s) wv[s] = ldexpf(wv[s], dG);
+        lsum = ldexpf(lsum, dG);
+        msum = ldexpf(msum, dG);
+        bias -= (float)dG;
+        thr = (float)G;
       }
     }
     // limbs of the 4 tokens, transposed to one dword per limb (tokens 4n ..
@@ -742,8 +755,8 @@ __device__ __forceinline__ void qk_wave(const DecodeArgs& a, int seg, int64_t r0
   for_tiles(ntiles, step);
 
   // per-head sums -> the partial record (m, l) and, for wave 1, sum p min_V
-  lsum = group_sum(lsum);
-  msum = group_sum(msum);
+  lsum = ldexpf(group_sum(lsum), -G);
+  msum = ldexpf(group_sum(msum), -G);
   if (n == 0) {
     float* wsu = a.ws + u * 4 * kPartialStride + kg * kPartialStride;
     wsu[0] = frame * kLn2;   // natural-log units
