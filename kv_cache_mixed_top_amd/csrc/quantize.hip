@@ -64,13 +64,39 @@ __device__ __forceinline__ float quad_xor2(float x) {
 // bits 3-4 (q) across the quad -- each pair (a, b) -> (a + b, a - b), then
 // one multiply by fp32(1/sqrt(128)).  kFrom: the first within-lane bit still
 // to do (1 when the caller has done bit 0 already); kScale = false leaves the
-// multiply to the caller.  Across the quad the lane's own value is added with
-// sign +1 (lower lane) or -1 (upper lane) in one fma, which rounds as the add
-// or subtract does.
+// multiply to the caller.
+//
+// Across the quad each value takes one v_fmac_f32 with a DPP source: own +
+// b * partner, b = +1 in the lower lane and -1 in the upper one.  The upper
+// lane so gets hi - lo, the exact negation of lo - hi (round to nearest is
+// symmetric), and keeps it: after both stages the lane holds its values times
+// sigma = (-1)^(q0 + q1), and the within-lane stages keep that sign.  The
+// function returns sigma; with kScale the multiply takes it out.
 constexpr float kRotScale = 0.08838834764831845f;          // fp32(1/sqrt(128))
 
+// x += b * (x of lane ^ 1), resp. lane ^ 2, within the quad.  The s_nop gives
+// the two wait states a DPP read needs after a VALU write of its source; the
+// caller puts a scheduling barrier before the first of a run of these, so
+// that the compiler places no write of a later source between them.
+template <int kM, bool kFirst>
+__device__ __forceinline__ void quad_fmac(float& x, float b) {
+  if constexpr (kM == 1) {
+    if constexpr (kFirst)
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+                   : "+v"(x) : "v"(b));
+    else
+      asm volatile("v_fmac_f32_dpp %0, %0, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "+v"(x) : "v"(b));
+  } else {
+    if constexpr (kFirst)
+      asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %0, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+                   : "+v"(x) : "v"(b));
+    else
+      asm volatile("v_fmac_f32_dpp %0, %0, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "+v"(x) : "v"(b));
+  }
+}
+
 template <int kFrom = 0, bool kScale = true>
-__device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
+__device__ __forceinline__ float rotate_row(float (&v)[32], int q) {
 #pragma unroll
   for (int bit = kFrom; bit < 3; ++bit)
 #pragma unroll
@@ -82,15 +108,17 @@ __device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
           v[8 * i + e] = x0 + x1;
           v[8 * i + e + (1 << bit)] = x0 - x1;
         }
+  // bits 3, 4: lane q ^ 1, then q ^ 2
+  const float b1 = (q & 1) ? -1.0f : 1.0f, b2 = (q & 2) ? -1.0f : 1.0f;
+  __builtin_amdgcn_sched_barrier(0);
+  quad_fmac<1, true>(v[0], b1);
 #pragma unroll
-  for (int m = 1; m <= 2; m <<= 1) {                       // bits 3, 4: lane q ^ m
-    const float sgn = (q & m) ? -1.0f : 1.0f;
+  for (int j = 1; j < 32; ++j) quad_fmac<1, false>(v[j], b1);
+  quad_fmac<2, true>(v[0], b2);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const float p = m == 1 ? quad_xor1(v[j]) : quad_xor2(v[j]);
-      v[j] = fmaf(v[j], sgn, p);
-    }
-  }
+  for (int j = 1; j < 32; ++j) quad_fmac<2, false>(v[j], b2);
+  __builtin_amdgcn_sched_barrier(0);
+  const float sigma = b1 * b2;
 #pragma unroll
   for (int bit = 0; bit < 2; ++bit)                        // bits 5, 6: i ^ (1 << bit)
 #pragma unroll
@@ -103,9 +131,11 @@ __device__ __forceinline__ void rotate_row(float (&v)[32], int q) {
           v[8 * (i + (1 << bit)) + e] = x0 - x1;
         }
   if constexpr (kScale) {
+    const float k = sigma * kRotScale;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) v[j] *= kRotScale;
+    for (int j = 0; j < 32; ++j) v[j] *= k;
   }
+  return kScale ? 1.0f : sigma;
 }
 
 // What one workgroup's pool writes: its row count, where its rows start in
@@ -394,6 +424,7 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, const Poo
   // ---- row min / max: packed fp16 (exact), then the quad; rotated rows:
   // fp32 values, the stored minimum rounded down to fp16
   float yr[kRot ? 32 : 1];
+  float rsig = 1.0f;   // rotated rows: yr holds rsig times the sums
   float lo, hi;
   if constexpr (kRot) {
     // bit 0 pairs are the two halves of one fp16 pair: a mixed-precision
@@ -409,13 +440,18 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, const Poo
     }
     // the sums u before the scaling: the rotated value is x = fl(u k), and
     // as rounding is monotone the extremes are fl(min u k), fl(max u k)
-    rotate_row<1, false>(yr, q);
+    rsig = rotate_row<1, false>(yr, q);   // yr holds rsig u
     lo = yr[0];
     hi = yr[0];
 #pragma unroll
     for (int k = 1; k < 32; ++k) {
       lo = fminf(lo, yr[k]);
       hi = fmaxf(hi, yr[k]);
+    }
+    if (rsig < 0.0f) {
+      const float t = lo;
+      lo = -hi;
+      hi = -t;
     }
     lo *= kRotScale;
     hi *= kRotScale;
@@ -473,6 +509,7 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, const Poo
   const float eps = kRot ? 0x1p-22f * (1.5f * (float)(L - 1) + 1.25f * fabsf(lo) * rs) + 0x1p-30f
                          : 0x1p-22f * ((float)(L - 1) + fabsf(lo) * rs) + 0x1p-30f;
   const float rsk = kRot ? rs * kRotScale : rs;
+  const float rsks = kRot ? rsig * rsk : rs;   // y from rsig u: the sign cancels exactly
   const float nb10 = fmaf(-lo, rs, (float)kD);
   constexpr float kUnit = (float)(1u << kFB);
   const float win = (2.0f * eps + 1.0f / kUnit) * kUnit;        // in units of 2^-FB
@@ -483,7 +520,7 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, const Poo
   uint32_t umin[4] = {0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};   // per 8 values
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const float y = fmaf(kRot ? yr[k & (kRot ? 31 : 0)] : (float)v[k >> 1][k & 1], rsk, nb10);
+    const float y = fmaf(kRot ? yr[k & (kRot ? 31 : 0)] : (float)v[k >> 1][k & 1], rsks, nb10);
     umin[k >> 3] = min(umin[k >> 3], (__builtin_bit_cast(uint32_t, y) << kSh) + bias);
     cw[k >> 2] = __builtin_amdgcn_cvt_pk_u8_f32(y, k & 3, (k & 3) ? cw[k >> 2] : 0u);
   }
@@ -503,7 +540,7 @@ __device__ __forceinline__ void quantize_tile_fast(const QuantArgs& a, const Poo
       if (!((flag >> i) & 1u)) continue;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float u = yr[(8 * i + e) & (kRot ? 31 : 0)];
+        const float u = rsig * yr[(8 * i + e) & (kRot ? 31 : 0)];
         const float y = fmaf(u, rsk, nb10);
         if (wide || (__builtin_bit_cast(uint32_t, y) << kSh) + bias <= thr) {
           const float x = u * kRotScale;
