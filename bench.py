@@ -674,6 +674,7 @@ def gen_leg(sk, W, torch, dev, stream, gen_steps=None):
     prompts, then per step append one token per sequence (a block of 128 is
     ranked, quantized and packed when the tail fills) and decode all layers
     over the pools plus the fp16 tail."""
+    import numpy as np
     w = W.WORKLOADS["gen_16x8k"]
     T = w.gen_tokens if gen_steps is None else gen_steps
     B, n = w.batch, w.n
@@ -694,11 +695,18 @@ def gen_leg(sk, W, torch, dev, stream, gen_steps=None):
     stream.synchronize()
     Rh, Rl = sk.semkv_row_bytes(w.L_high), sk.semkv_row_bytes(w.L_low)
     planes = B * w.layers * w.kv_heads * 2
-    qa, qb = Ev(), Ev()
-    qa.record(stream)
-    sk.semkv_rank_topr(scores, k, perm, stream=stream)
-    sk.semkv_quantize_pack(cache, K, V, perm, k, stream=stream)
-    qb.record(stream)
+    # the prompt's rank + quantize-pack: the median of 3 passes over the same
+    # cache after an untimed first one, as the other legs time their
+    # quantize (each pass writes the same pools again)
+    qev = []
+    for rep in range(4):
+        cache.reset()
+        qa, qb = Ev(), Ev()
+        qa.record(stream)
+        sk.semkv_rank_topr(scores, k, perm, stream=stream)
+        sk.semkv_quantize_pack(cache, K, V, perm, k, stream=stream)
+        qb.record(stream)
+        qev.append((qa, qb))
     del K, V
     ev_app = [(Ev(), Ev()) for _ in range(T)]
     ev_dec = [(Ev(), Ev()) for _ in range(T)]
@@ -730,7 +738,7 @@ def gen_leg(sk, W, torch, dev, stream, gen_steps=None):
     dec_gbs = sum(dec_bytes) / (sum(t_dec) * 1e-3) / 1e9
     blk_bytes = planes * (kb * (256 + Rh + 4) + (w.block - kb) * (256 + Rl + 4))
     ms_blk = sum(t_app[i] for i in blocks) / max(1, len(blocks))
-    prompt_ms = qa.elapsed_time(qb)
+    prompt_ms = float(np.median([x.elapsed_time(y) for x, y in qev[1:]]))
     prompt_bytes = planes * (k * (256 + Rh + 4) + (n - k) * (256 + Rl + 4))
     res = {"workload": "gen_16x8k", "batch": B, "prompt_tokens": n, "r": w.r,
            "generated_tokens": T,
