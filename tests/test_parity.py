@@ -308,7 +308,10 @@ def test_generation_block_exact(block, steps, r):
     vs = rng.standard_normal((steps, B, layers, kv, 128)).astype(np.float16)
     ss = rng.random((steps, B)).astype(np.float32)
     out = torch.empty((B, layers, Hq, 128), dtype=torch.float32, device="cuda")
-    check_at = {0, block - 1, block, steps - 1}
+    # tails of 1, 16, 17 and block - 1 rows (the largest a decode sees: the
+    # folded tail path's 16-row groups full, ragged and all present), none,
+    # and the last step's
+    check_at = {0, 15, 16, block - 2, block - 1, block, steps - 1}
     for i in range(steps):
         kd = to_dev(ks[i][:, :, :, None, :])
         vd = to_dev(vs[i][:, :, :, None, :])

@@ -118,7 +118,7 @@ def test_ragged_generation(Hq, rotate, levels):
                 R.append(b, kn[b, :, :, 0], vn[b, :, :, 0], sc[b])
             if flush[b]:
                 R.flush(b)
-        if step in (45, 89):
+        if step in (30, 45, 89):   # step 30: tails of 31 (block - 1), 16 and 31 rows
             sk.semkv_sync_check()
             _check_state(cache, seq, R, f"step {step}")
             nh = max(R.counters(b)[0] for b in range(B))
