@@ -709,13 +709,18 @@ hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t stream) {
 }
 
 int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units) {
-  // Chunks fill whole rounds of the resident workgroup slots; a chunk holds
-  // at most kMfmaChunkMax rows, which bounds the length of the matrix-core
-  // accumulations (longer contexts take more rounds instead), and at least
-  // kMfmaChunkMin rows: a chunk's fixed work (query fragments, the V scale
-  // pass, the partial record, its share of the merge) then spreads over four
+  // Chunks fill whole rounds of the resident workgroup slots.  A launch that
+  // fits one round with chunks of at most kMfmaChunkExact rows (the longest
+  // whose PV limb sums stay exact in int32) takes that one round: every
+  // chunk start costs its query preparation, pipeline fill and epilogue, so
+  // one round of long chunks beats several of short ones (measured on 128k
+  // contexts: 564 us against 595 us).  Otherwise a chunk holds at most
+  // kMfmaChunkMax rows and the launch takes several rounds of similar chunks,
+  // which the dispatcher balances better than a few long ones.  A chunk
+  // holds at least kMfmaChunkMin rows: its fixed work then spreads over four
   // tiles.  (A launch over few (sequence, layer, KV head) units, such as one
   // layer of one sequence, would otherwise take one- or two-tile chunks.)
+  constexpr int64_t kMfmaChunkExact = 16384;
   constexpr int64_t kMfmaChunkMax = 4096;
   constexpr int64_t kMfmaChunkMin = 4 * kTile;
   const int64_t slots = decode_mfma_resident_waves();
@@ -730,7 +735,8 @@ int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units) {
     return c;
   };
   int64_t c = fit(per_round);
-  if (c > kMfmaChunkMax) c = fit(per_round * ((c + kMfmaChunkMax - 1) / kMfmaChunkMax));
+  const bool one_round = c <= kMfmaChunkExact && units * count(c) <= slots;
+  if (c > kMfmaChunkMax && !one_round) c = fit(per_round * ((c + kMfmaChunkMax - 1) / kMfmaChunkMax));
   if (c < kMfmaChunkMin) c = kMfmaChunkMin;
   return (int)c;
 }
