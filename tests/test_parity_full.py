@@ -291,18 +291,13 @@ def test_cliff_grid_sampled():
         torch.cuda.empty_cache()
 
 
-def test_decode_frame_raise_after_lowered_exponent():
-    """Logits shaped so that every 1,024-row chunk of a 32-layer launch first
-    lowers its fixed-point exponent (a few tokens just under the softmax
-    frame) and then raises its frame (a spike 11.5 nats above the typical
-    tokens, whose weights after the raise are small).  Besides the 2e-3
-    parity bound the error is held to 2e-5, ten times what the arithmetic
-    allows: the weights keep at least 28 bits against a chunk's largest
-    weight (an error below rows / 2^29 = 1.9e-6 of its normaliser) and the
-    query 27 bits, so a larger error means lost weight bits.  (An exponent
-    kept across the frame raise leaves the typical tokens' weights at a few
-    units: 1.6e-4 here.)"""
-    B, layers, kv, Hq, n, r = 1, 32, 8, 32, 8192, 0.5
+def _frame_raise_case(n, layers_checked, heads_checked, bound, what):
+    """Logits shaped so that every chunk of a 32-layer launch first lowers
+    its fixed-point exponent (a few tokens just under the softmax frame) and
+    then raises its frame (a spike 11.5 nats above the typical tokens, whose
+    weights after the raise are small); the pattern repeats every 2,048
+    rows.  The decode error against the oracle is held to `bound`."""
+    B, layers, kv, Hq, r = 1, 32, 8, 32, 0.5
     beta = 10.0 / 3.0                                   # logit per unit of the u component
     g = torch.Generator(device=DEV)
     g.manual_seed(21)
@@ -330,10 +325,29 @@ def test_decode_frame_raise_after_lowered_exponent():
     sk.semkv_sync_check()
     got = out.cpu().numpy()
     worst = 0.0
-    for layer in (0, 17):
-        for head in range(kv):
+    for layer in layers_checked:
+        for head in heads_checked:
             op = _check_plane(cache, K, V, wp, k, 6, 5, 0, layer, head)
             worst = max(worst, _decode_group(op, q, 0, layer, head, Hq // kv, 1.0, got,
-                                             f"frame raise layer {layer} head {head}"))
-    _print(f"frame raise after a lowered exponent: worst decode error {worst:.3e}")
-    assert worst <= 2e-5, f"frame raise after a lowered exponent: {worst:.3e} > 2e-5"
+                                             f"{what} layer {layer} head {head}"))
+    _print(f"{what}: worst decode error {worst:.3e}")
+    assert worst <= bound, f"{what}: {worst:.3e} > {bound:.1e}"
+
+
+def test_decode_frame_raise_after_lowered_exponent():
+    """8,192 tokens: the launch takes 1,024-row chunks.  Besides the 2e-3
+    parity bound the error is held to 2e-5, ten times what the arithmetic
+    allows: the weights keep at least 28 bits against a chunk's largest
+    weight (an error below rows / 2^29 = 1.9e-6 of its normaliser) and the
+    query 27 bits, so a larger error means lost weight bits.  (An exponent
+    kept across the frame raise leaves the typical tokens' weights at a few
+    units: 1.6e-4 here.)"""
+    _frame_raise_case(8192, (0, 17), range(8), 2e-5, "frame raise, 1,024-row chunks")
+
+
+def test_decode_frame_raise_long_chunks():
+    """65,536 tokens: the launch fits one round of 8,192-row chunks (the
+    single-round rule; the kernel takes chunks up to 16,384 rows).  The bound
+    is ten times the weights' error for the longest such chunk,
+    10 x 16,384 / 2^29 = 3.1e-4 of a chunk's normaliser."""
+    _frame_raise_case(65536, (5,), (0, 7), 3.1e-4, "frame raise, long chunks")
