@@ -11,8 +11,12 @@
  *
  * Conventions for every entry point
  *  - Data pointers are DEVICE pointers owned by the caller; the library never
- *    allocates, frees or retains device memory and keeps no global state
- *    besides its loaded code objects.  `stream` is a hipStream_t passed as
+ *    allocates, frees or retains device memory.  Its only state besides its
+ *    loaded code objects: per device, the decode kernel's resident workgroup
+ *    count (taken from the occupancy query on first use, held in an atomic)
+ *    and the address of the static scratch array of
+ *    semkv_decode_attn_noalloc (part of the code object; looked up on first
+ *    use).  Both are the same for every caller.  `stream` is a hipStream_t passed as
  *    void* (NULL = the null stream).  Calls enqueue work on `stream` and
  *    return without synchronising, except semkv_sync_check.
  *  - fp16 data is passed as uint16_t bit patterns so this header does not
