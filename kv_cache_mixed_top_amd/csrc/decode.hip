@@ -736,7 +736,16 @@ int decode_mfma_chunk_rows(int64_t n_high, int64_t n_low, int64_t units) {
   };
   int64_t c = fit(per_round);
   const bool one_round = c <= kMfmaChunkExact && units * count(c) <= slots;
-  if (c > kMfmaChunkMax && !one_round) c = fit(per_round * ((c + kMfmaChunkMax - 1) / kMfmaChunkMax));
+  // Several rounds: chunks of at most kMfmaChunkMax rows, or twice that when
+  // one pool holds at most an eighth of the rows and the units fit the slots
+  // (then the minority pool is one short chunk per unit and the majority
+  // pool's chunks are alike, so longer chunks save starts without
+  // unbalancing the last round: measured 0.5-18% faster at a fraction of
+  // 0.1 or 0.9 over 4 x 32k, and 5-10% slower at 0.25 and 0.75).
+  const int64_t minority = n_high < n_low ? n_high : n_low;
+  const int64_t cap = units <= slots && minority > 0 && 8 * minority <= n_high + n_low
+                          ? 2 * kMfmaChunkMax : kMfmaChunkMax;
+  if (c > cap && !one_round) c = fit(per_round * ((c + cap - 1) / cap));
   if (c < kMfmaChunkMin) c = kMfmaChunkMin;
   return (int)c;
 }
